@@ -1,0 +1,226 @@
+"""Reference oracle for the fused block-dequant matmul (TEST INFRASTRUCTURE).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` import this package.  The HIP library never calls it, and it
+shares no code with that library: the arithmetic lives in ``oracle.c`` (plain
+C, binary64 accumulation), and this module only marshals numpy arrays.
+
+What it computes is the plain definition of the method on the page "Building a
+Rust Inference Engine That Matches Llama.cpp", section "Where the wins came
+from": weights stored as GGUF quantized blocks are dequantized at the moment
+they enter the dot product; the fused result equals dequantize-then-dot.
+
+Parity pins: every function here is pinned by tests marked ``not gpu``
+(hand-built blocks, closed forms, exhaustive binary16 decode against numpy,
+an independently written numpy unpacker, brute force and invariants).  The
+MoE readings (SwiGLU between the expert projections, top-k softmax weights
+used without renormalisation) are readings, not pinned by the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+Q8_0 = 0
+Q4_K = 1
+
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc into liboracle.so (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+             "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        vp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        L.orc_half_to_double.restype = ctypes.c_double
+        L.orc_half_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_double_to_half.restype = ctypes.c_uint16
+        L.orc_double_to_half.argtypes = [ctypes.c_double]
+        L.orc_half_array_to_double.argtypes = [vp, i64, vp]
+        L.orc_double_array_to_half.argtypes = [vp, i64, vp]
+        L.orc_q4k_fields.argtypes = [vp, vp, vp, vp, vp, vp]
+        L.orc_dequant.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp]
+        L.orc_gemv.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, vp]
+        L.orc_gemv_separate.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp]
+        L.orc_gemm.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
+        L.orc_moe_route.argtypes = [vp, i64, i64, i64, vp, vp]
+        L.orc_moe_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                  vp, vp, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _u8(w):
+    w = np.ascontiguousarray(w)
+    if w.dtype != np.uint8:
+        w = w.view(np.uint8)
+    return w.reshape(-1)
+
+
+def _bits16(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    assert x.dtype == np.uint16
+    return x
+
+
+def _idx(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64).reshape(-1))
+
+
+def row_bytes(fmt: int, K: int) -> int:
+    return K // 32 * 34 if fmt == Q8_0 else K // 256 * 144
+
+
+def _check(fmt, w, M, K):
+    if fmt == Q8_0:
+        assert K % 32 == 0
+    else:
+        assert K % 256 == 0
+    assert w.size >= M * row_bytes(fmt, K)
+
+
+# -- binary16 ---------------------------------------------------------------
+
+def half_to_double(bits) -> np.ndarray:
+    bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16).reshape(-1))
+    out = np.empty(bits.size, dtype=np.float64)
+    lib().orc_half_array_to_double(_p(bits), bits.size, _p(out))
+    return out
+
+
+def double_to_half(v) -> np.ndarray:
+    """Round each value to binary16 (nearest, ties to even); returns bit patterns."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64).reshape(-1))
+    out = np.empty(v.size, dtype=np.uint16)
+    lib().orc_double_array_to_half(_p(v), v.size, _p(out))
+    return out
+
+
+# -- block decode -------------------------------------------------------------
+
+def q4k_fields(block):
+    """(d, dmin, sc[8], m[8], q[256]) of one 144-byte Q4_K super-block."""
+    block = _u8(block)
+    assert block.size == 144
+    d = ctypes.c_double()
+    dmin = ctypes.c_double()
+    sc = np.empty(8, np.int32)
+    m = np.empty(8, np.int32)
+    q = np.empty(256, np.int32)
+    lib().orc_q4k_fields(_p(block), ctypes.byref(d), ctypes.byref(dmin), _p(sc), _p(m), _p(q))
+    return d.value, dmin.value, sc, m, q
+
+
+def dequant(fmt: int, w, M: int, K: int):
+    """(w32 [M][K] float32, w16 [M][K] uint16 bits)."""
+    w = _u8(w)
+    _check(fmt, w, M, K)
+    o32 = np.empty((M, K), np.float32)
+    o16 = np.empty((M, K), np.uint16)
+    lib().orc_dequant(fmt, _p(w), M, K, _p(o32), _p(o16))
+    return o32, o16
+
+
+# -- products -----------------------------------------------------------------
+
+def gemv(fmt: int, w, x, M: int, K: int, rows=None):
+    """y[b][i] = sum_k w32[rows[i]][k] x[b][k] (binary64) and its bound S."""
+    w = _u8(w)
+    _check(fmt, w, M, K)
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32).reshape(-1, K))
+    B = x.shape[0]
+    rows = _idx(rows)
+    nr = M if rows is None else rows.size
+    y = np.empty((B, nr), np.float64)
+    S = np.empty((B, nr), np.float64)
+    lib().orc_gemv(fmt, _p(w), _p(x), M, K, B, _p(rows), nr, _p(y), _p(S))
+    return y, S
+
+
+def gemv_separate(fmt: int, w, x, M: int, K: int):
+    w = _u8(w)
+    _check(fmt, w, M, K)
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32).reshape(-1, K))
+    y = np.empty((x.shape[0], M), np.float64)
+    lib().orc_gemv_separate(fmt, _p(w), _p(x), M, K, x.shape[0], _p(y))
+    return y
+
+
+def gemm(fmt: int, w, x16, M: int, K: int, rows=None, toks=None):
+    """Y[t][i] = sum_k w32[rows[i]][k] x16[toks[t]][k] (binary64) and its bound S."""
+    w = _u8(w)
+    _check(fmt, w, M, K)
+    x16 = _bits16(x16).reshape(-1, K)
+    N = x16.shape[0]
+    rows = _idx(rows)
+    toks = _idx(toks)
+    nr = M if rows is None else rows.size
+    nt = N if toks is None else toks.size
+    y = np.empty((nt, nr), np.float64)
+    S = np.empty((nt, nr), np.float64)
+    lib().orc_gemm(fmt, _p(w), _p(x16), M, K, N, _p(rows), nr, _p(toks), nt, _p(y), _p(S))
+    return y, S
+
+
+def moe_route(logits, topk: int):
+    """Top-k of the binary64 softmax of each row: (ids int32 [T][k], wts float64 [T][k])."""
+    logits = np.ascontiguousarray(np.asarray(logits, dtype=np.float32))
+    T, E = logits.shape
+    ids = np.empty((T, topk), np.int32)
+    wts = np.empty((T, topk), np.float64)
+    lib().orc_moe_route(_p(logits), T, E, topk, _p(ids), _p(wts))
+    return ids, wts
+
+
+def moe_ffn(w_gate, w_up, w_down, x16, ids, wts, H: int, I: int, E: int):
+    """Binary64 MoE feed-forward; returns dict of g, u, h, d, out, Sg, Su, Sd."""
+    x16 = _bits16(x16).reshape(-1, H)
+    T = x16.shape[0]
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    wts = np.ascontiguousarray(np.asarray(wts, dtype=np.float32))
+    topk = ids.shape[1]
+    assert ids.shape == (T, topk) and wts.shape == (T, topk)
+    assert 0 <= ids.min() and ids.max() < E
+    gu = I * (H // 256) * 144
+    dn = H * (I // 256) * 144
+    wg, wu, wd = _u8(w_gate), _u8(w_up), _u8(w_down)
+    assert wg.size >= E * gu and wu.size >= E * gu and wd.size >= E * dn
+    A = T * topk
+    r = {k: np.empty((A, I)) for k in ("g", "u", "h", "Sg", "Su")}
+    r.update({k: np.empty((A, H)) for k in ("d", "Sd")})
+    r["out"] = np.empty((T, H))
+    lib().orc_moe_ffn(_p(wg), _p(wu), _p(wd), _p(x16), _p(ids), _p(wts), T, H, I, E, topk,
+                      _p(r["g"]), _p(r["u"]), _p(r["h"]), _p(r["d"]), _p(r["out"]),
+                      _p(r["Sg"]), _p(r["Su"]), _p(r["Sd"]))
+    return r
