@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused dequant matrix products on one MI355X.
+
+A step is one decode step of a Llama-3-8B-shaped Q4_K linear stack at batch 1:
+32 layers x {q 4096x4096, k 1024x4096, v 1024x4096, o 4096x4096,
+gate 14336x4096, up 14336x4096, down 4096x14336} = 224 fused-dequant
+matrix-vector products (3,925,868,544 bytes of packed weights), launched on
+one stream and replayed as one HIP graph.  Every matrix has its own weights
+(no reuse through the caches) and its own binary32 N(0,1) activation vector.
+``value`` is packed weight bytes per second over the timed steps.
+
+The same run also measures, outside the timed steps, the other forms of the
+hot path (batch 4 and 16 stacks, single decode matrices hot and rotated, the
+prefill matrix products, the mixture-of-experts layer, the Q8_0 product) and
+times the binary64 CPU oracle on a bounded sample of the stack.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K fused-dequant GEMV weight GB/s (decode); dequant-GEMM TFLOP/s (prefill)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FP16_PEAK_TFLOPS = 2500.0    # MI355X dense binary16 matrix cores
+LAYER = (("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
+         ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336))
+N_LAYERS = 32
+STACK_WORKLOAD = 2           # generator stream ids shared with the parity tests
+PREFILL_WORKLOAD = 3
+MOE_WORKLOAD = 4
+
+
+def q4k_bytes(M, K):
+    return M * (K // 256) * 144
+
+
+def gemv_bytes(M, K, B):
+    """Algorithmic bytes of one matrix-vector product: packed weights, x, y."""
+    return q4k_bytes(M, K) + 4 * B * K + 4 * B * M
+
+
+class Stack:
+    """The 224 weight matrices of the decode stack, resident in HBM."""
+
+    def __init__(self, torch, synth):
+        self.mats = []
+        for layer in range(N_LAYERS):
+            for i, (name, M, K) in enumerate(LAYER):
+                t = layer * len(LAYER) + i
+                w = torch.from_numpy(synth.q4k_blocks(STACK_WORKLOAD, t, M, K)).cuda()
+                self.mats.append((name, M, K, t, w))
+        self.weight_bytes = sum(q4k_bytes(M, K) for _, M, K, _, _ in self.mats)
+
+
+def stack_graph(torch, gq, synth, stack, B, stream):
+    xs, ys = [], []
+    for _, M, K, t, _ in stack.mats:
+        xs.append(torch.from_numpy(synth.activations_f32(STACK_WORKLOAD, 100 * t + B, B, K)).cuda())
+        ys.append(torch.empty((B, M), dtype=torch.float32, device="cuda"))
+
+    def launch_all():
+        for (_, M, K, _, w), x, y in zip(stack.mats, xs, ys):
+            gq.gq_gemv_q4k(w, x, y, M, K, B, stream)
+
+    with torch.cuda.stream(stream):
+        launch_all()  # eager once: loads the library, checks every call
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        launch_all()
+    torch.cuda.synchronize()
+    return g, launch_all
+
+
+def time_graph(torch, g, steps, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def per_launch_times(torch, stream, launches, reps=3):
+    """Average duration (s) of each launch, bracketed by HIP events on `stream`."""
+    n = len(launches)
+    tot = [0.0] * n
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(n)]
+            for (a, b), fn in zip(ev, launches):
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(ev):
+                tot[i] += a.elapsed_time(b) * 1e-3
+    return [t / reps for t in tot]
+
+
+def event_time(torch, stream, fn, reps=20, warmup=3):
+    """Median per-call time (s) of fn() on `stream`, HIP events per rep."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def cpu_baseline(synth, budget_s=12.0):
+    """The binary64 oracle on whole matrices of the stack (layer 0 onwards, in
+    order) until about budget_s seconds of oracle time are spent; one thread.
+    Input generation is not timed."""
+    import oracle
+    oracle.lib()
+    done_bytes, mats, secs = 0, 0, 0.0
+    for t in range(N_LAYERS * len(LAYER)):
+        name, M, K = LAYER[t % len(LAYER)]
+        w = synth.q4k_blocks(STACK_WORKLOAD, t, M, K)
+        x = synth.activations_f32(STACK_WORKLOAD, 100 * t + 1, 1, K)
+        a = time.perf_counter()
+        oracle.gemv(oracle.Q4_K, w, x, M, K)
+        secs += time.perf_counter() - a
+        done_bytes += q4k_bytes(M, K)
+        mats += 1
+        if secs >= budget_s:
+            break
+    return {"value": round(done_bytes / secs / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "first %d of the 224 stack matrices (layer order q,k,v,o,gate,up,down), "
+                      "batch 1, all rows, %.1f s single-threaded binary64" % (mats, secs)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
+              "and has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from quantized_unpack_q4_amd import gq, synth
+
+    torch.cuda.set_device(0)
+    gq.lib()
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    log("generating the decode stack ...")
+    stack = Stack(torch, synth)
+    stream = torch.cuda.Stream()
+    g1, launch1 = stack_graph(torch, gq, synth, stack, 1, stream)
+
+    log("timing %d steps after %d warm-up steps" % (args.steps, args.warmup))
+    sec = time_graph(torch, g1, args.steps, args.warmup)
+    value = stack.weight_bytes / sec / 1e9
+
+    # per-launch durations of the matrix-vector kernel (the dominant kernel)
+    launches = []
+    xs = []
+    for _, M, K, t, w in stack.mats:
+        x = torch.from_numpy(synth.activations_f32(STACK_WORKLOAD, 100 * t + 1, 1, K)).cuda()
+        y = torch.empty((1, M), dtype=torch.float32, device="cuda")
+        xs.append((x, y))
+        launches.append(lambda w=w, x=x, y=y, M=M, K=K: gq.gq_gemv_q4k(w, x, y, M, K, 1, stream))
+    durs = per_launch_times(torch, stream, launches)
+    alg = [gemv_bytes(M, K, 1) for _, M, K, _, _ in stack.mats]
+    avg_dur = sum(durs) / len(durs)
+    avg_bytes = sum(alg) / len(alg)
+    achieved = avg_bytes / avg_dur / 1e9
+    by_shape = {}
+    for (name, M, K, _, _), dsec in zip(stack.mats, durs):
+        by_shape.setdefault(name, []).append(dsec)
+    shape_report = {n: {"M": M, "K": K, "us": round(1e6 * sum(v) / len(v), 2),
+                        "GB/s": round(q4k_bytes(M, K) / (sum(v) / len(v)) / 1e9, 1)}
+                    for (n, M, K), v in zip(LAYER, by_shape.values())}
+
+    extra = {"stack_b1": {"ms_per_step_graph": round(sec * 1e3, 4),
+                          "kernel_sum_ms": round(sum(durs) * 1e3, 4),
+                          "per_shape": shape_report}}
+
+    if not args.no_extra:
+        for B in (4, 16):
+            log("stack batch", B)
+            gB, _ = stack_graph(torch, gq, synth, stack, B, stream)
+            s = time_graph(torch, gB, max(3, args.steps // 2), 2)
+            flops = sum(2 * M * K * B for _, M, K, _, _ in stack.mats)
+            extra["stack_b%d" % B] = {"ms_per_step": round(s * 1e3, 4),
+                                      "weight_GB/s": round(stack.weight_bytes / s / 1e9, 1),
+                                      "TFLOP/s": round(flops / s / 1e12, 2)}
+            del gB
+        # single decode matrices: hot (one matrix again and again) and rotated
+        for name, M, K in (("q", 4096, 4096), ("gate", 14336, 4096)):
+            mats = [m for m in stack.mats if m[0] == name or (name == "q" and m[0] == "o")]
+            x = torch.from_numpy(synth.activations_f32(1, M, 1, K)).cuda()
+            y = torch.empty((1, M), dtype=torch.float32, device="cuda")
+            w0 = mats[0][4]
+            hot = event_time(torch, stream, lambda: gq.gq_gemv_q4k(w0, x, y, M, K, 1, stream))
+            it = {"i": 0}
+
+            def rot():
+                w = mats[it["i"] % len(mats)][4]
+                it["i"] += 1
+                gq.gq_gemv_q4k(w, x, y, M, K, 1, stream)
+            rotated = event_time(torch, stream, rot, reps=len(mats), warmup=len(mats))
+            extra["gemv_%dx%d_b1" % (M, K)] = {
+                "hot_us": round(hot * 1e6, 2), "hot_GB/s": round(q4k_bytes(M, K) / hot / 1e9, 1),
+                "rotated_us": round(rotated * 1e6, 2),
+                "rotated_GB/s": round(q4k_bytes(M, K) / rotated / 1e9, 1),
+                "rotated_over_MB": round(len(mats) * q4k_bytes(M, K) / 1e6, 1)}
+        del stack, g1
+        torch.cuda.empty_cache()
+        # prefill matrix products
+        pre = {}
+        for M, K in ((14336, 4096), (4096, 14336)):
+            w = torch.from_numpy(synth.q4k_blocks(PREFILL_WORKLOAD, M, M, K)).cuda()
+            for N in (512, 4096):
+                x16 = torch.from_numpy(synth.activations_f16(PREFILL_WORKLOAD, N, N, K)).cuda()
+                y16 = torch.empty((N, M), dtype=torch.float16, device="cuda")
+                s = event_time(torch, stream, lambda: gq.gq_gemm_q4k(w, x16, y16, M, K, N, stream))
+                tf = 2.0 * M * K * N / s / 1e12
+                pre["%dx%dxN%d" % (M, K, N)] = {"us": round(s * 1e6, 1), "TFLOP/s": round(tf, 1),
+                                                "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)}
+                del x16, y16
+            del w
+        extra["prefill_gemm"] = pre
+        # mixture of experts, OLMoE-1B-7B shape
+        import oracle  # routing only: the oracle's binary64 softmax/top-k on the host
+        H, I, E, k = 2048, 1024, 64, 8
+        wg = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 0, E * I, H)).cuda()
+        wu = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 1, E * I, H)).cuda()
+        wd = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 2, E * H, I)).cuda()
+        moe = {}
+        wbytes = 3 * E * q4k_bytes(I, H)
+        for T in (256, 2048):
+            x16 = torch.from_numpy(synth.activations_f16(MOE_WORKLOAD, 0, T, H)).cuda()
+            ids, wts = oracle.moe_route(synth.router_logits(MOE_WORKLOAD, 0, T, E), k)
+            ids_d = torch.from_numpy(ids).cuda()
+            wts_d = torch.from_numpy(wts.astype(np.float32)).cuda()
+            need = gq.gq_moe_workspace_bytes(T, H, I, E, k)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+            out = torch.empty((T, H), dtype=torch.float16, device="cuda")
+            s = event_time(torch, stream, lambda: gq.gq_moe_gemm_q4k(
+                wg, wu, wd, x16, ids_d, wts_d, out, T, H, I, E, k, ws, need, stream))
+            flops = 2.0 * T * k * 3 * H * I
+            moe["T%d" % T] = {"us": round(s * 1e6, 1), "TFLOP/s": round(flops / s / 1e12, 1),
+                              "weight_GB/s": round(wbytes / s / 1e9, 1)}
+        extra["moe_olmoe"] = moe
+        del wg, wu, wd
+        # Q8_0 matrix-vector product, 256 x 1024
+        wq = torch.from_numpy(synth.q8_0_blocks(0, 0, 256, 1024)).cuda()
+        xq = torch.from_numpy(synth.activations_f32(0, 0, 1, 1024)).cuda()
+        yq = torch.empty((1, 256), dtype=torch.float32, device="cuda")
+        s = event_time(torch, stream, lambda: gq.gq_gemv_q8_0(wq, xq, yq, 256, 1024, 1, stream))
+        extra["gemv_q8_0_256x1024_b1_us"] = round(s * 1e6, 2)
+
+    cpu = None if args.no_cpu else cpu_baseline(synth)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_k weights, f32 activations and accumulation",
+        "data": "synthetic (seeded Q4_K blocks and N(0,1) activations)",
+        "config": {"workload": "llama3-8b-shaped Q4_K decode stack, 32 layers x 7 GEMVs, "
+                               "batch 1, graph-replayed",
+                   "weight_bytes_per_step": stack_bytes_total(),
+                   "global_batch": 1, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "gemv_q4k_kernel (batch 1)",
+                     "avg_launch_us": round(avg_dur * 1e6, 3),
+                     "alg_bytes_per_launch": int(avg_bytes)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def stack_bytes_total():
+    return N_LAYERS * sum(q4k_bytes(M, K) for _, M, K in LAYER)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * gq.h -- fused block-dequant matrix products for AMD MI355X (gfx950).
+ *
+ * The operation (page "Building a Rust Inference Engine That Matches
+ * Llama.cpp", section "Where the wins came from"): weights are kept as GGUF
+ * quantized blocks (4-bit and 8-bit) and are never expanded into a full
+ * precision buffer; each weight is dequantized inside the dot product that
+ * consumes it.  Four forms are exported: batch-1 and small-batch
+ * matrix-vector products for decode and continuous batching, a matrix
+ * product for prefill, and the grouped per-expert form for mixture-of-experts
+ * layers (page "Frink Inference: the Rust alternative to llama.cpp", opening
+ * paragraph: quantized kernels and expert routing; section "A serving stack
+ * with the full sampling surface": continuous batching).
+ *
+ * Block formats (GGUF; page "Building a Rust Inference Engine That Matches
+ * Llama.cpp", sections "What Ferrox actually is" and "Further resources"),
+ * little-endian, rows of K weights stored back to back with no padding:
+ *
+ *   Q8_0  34 bytes per 32 weights: binary16 d, then 32 int8 q; w = d*q.
+ *   Q4_K  144 bytes per 256 weights: binary16 d, binary16 dmin, 12 bytes
+ *         holding eight 6-bit scales sc[j] and eight 6-bit mins m[j] of the
+ *         32-weight sub-blocks j, then 128 bytes of 4-bit quants q (byte 32g+i
+ *         holds weight 64g+i in its low nibble and weight 64g+32+i in its high
+ *         nibble); w = d*sc[j]*q - dmin*m[j].
+ *
+ * Each binary32 weight is the exact value rounded once (nearest even); the
+ * binary16 weight fed to half-precision matrix cores is that binary32 value
+ * rounded to binary16.  Activations of the matrix-vector products stay
+ * binary32 (page "Frink Inference: the Rust alternative to llama.cpp",
+ * section "Where llama.cpp is still ahead", K-quant item): they are never
+ * quantized.
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are device pointers on the current HIP device,
+ *     allocated and owned by the caller; the library never allocates, frees
+ *     or retains them.  Base pointers must be 16-byte aligned.
+ *   - Activations and outputs are dense row-major: x[B][K], y[B][M] for the
+ *     matrix-vector products; X[N][K], Y[N][M] for the matrix products
+ *     (Y = X * W^T).  binary16 buffers are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: the return value covers argument checks and the launch
+ *     only; faults surface at the caller's next synchronisation.
+ *   - A call with no work (zero rows, tokens or batch) returns GQ_OK and
+ *     launches nothing; its pointers are not checked.  K (H, I) must be
+ *     positive.
+ *   - On any status other than GQ_OK nothing has been launched and
+ *     gq_last_error() (per thread) names the argument and the violated
+ *     condition.  Unsupported shapes are refused, never computed on a subset.
+ *   - No entry point keeps state between calls apart from the error string;
+ *     calls on different streams may run concurrently.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gq_status {
+    GQ_OK = 0,
+    GQ_EINVAL = 1,     /* null pointer, negative size, batch out of range, topk outside [1, E] */
+    GQ_ESHAPE = 2,     /* K (or H, I) not a multiple of the block size, or a size too large */
+    GQ_EALIGN = 3,     /* a base pointer not 16-byte aligned */
+    GQ_EWORKSPACE = 4, /* workspace missing or smaller than gq_moe_workspace_bytes() */
+    GQ_EHIP = 5        /* the HIP runtime reported an error at launch */
+} gq_status;
+
+/* Largest batch accepted by the matrix-vector products. */
+#define GQ_GEMV_MAX_BATCH 16
+
+/* Q8_0 matrix-vector product, binary32 activations:
+ *   y[b][r] = sum_k w[r][k] * x[b][k]  for r < M, b < B, accumulated in binary32.
+ * w: M rows of K/32 Q8_0 blocks (M*K/32*34 bytes).  x: [B][K] float.  y: [B][M] float.
+ * Requires K % 32 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH. */
+gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
+                       void *stream);
+
+/* Q4_K matrix-vector product, binary32 activations; same contract as
+ * gq_gemv_q8_0 with w holding M rows of K/256 super-blocks (M*K/256*144
+ * bytes).  Requires K % 256 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH. */
+gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
+                      void *stream);
+
+/* Q4_K matrix product for prefill, binary16 activations and output:
+ *   Y[n][r] = binary16( sum_k X[n][k] * w16[r][k] ),  accumulated in binary32,
+ * where w16 is each weight rounded to binary16 as described above.
+ * x: [N][K] binary16 bits.  y: [N][M] binary16 bits.  Requires K % 256 == 0. */
+gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                      int64_t N, void *stream);
+
+/* Mixture-of-experts feed-forward over Q4_K experts (the grouped form):
+ *   for every token t and slot s < topk, with e = topk_ids[t][s]:
+ *     g = Wg_e x_t, u = Wu_e x_t            (binary16 matrix cores, binary32 sums)
+ *     h = binary16( silu(g) * u )           silu(z) = z / (1 + exp(-z))
+ *     d = Wd_e h                            (binary32)
+ *   out[t] = binary16( sum_{s = 0..topk-1} topk_w[t][s] * d_s ), summed in slot order.
+ * w_gate, w_up: E stacked [I rows][H cols] Q4_K matrices.  w_down: E stacked
+ * [H rows][I cols] Q4_K matrices.  x: [T][H] binary16.  topk_ids: [T][topk]
+ * int32 in [0, E).  topk_w: [T][topk] float (used as given, no renormalisation).
+ * out: [T][H] binary16.  ws: workspace of at least gq_moe_workspace_bytes()
+ * bytes (layout: gq_moe_workspace_offsets()); contents on entry are ignored.
+ * Requires H % 256 == 0, I % 256 == 0, 1 <= topk <= E <= 256, T*topk <= 2^20.
+ * An id outside [0, E) cannot be checked on the host: its slot is skipped
+ * (contributes nothing) and counted in the workspace's expert table. */
+gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_down,
+                          const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                          uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
+                          int64_t topk, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace size for gq_moe_gemm_q4k with these sizes (0 if they are invalid). */
+size_t gq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+
+/* Byte offsets of the workspace regions (each 256-byte aligned), in order:
+ *   off[0] expert table     int32 [E+3]    [0..E-1] first sorted position of each
+ *                                          expert, [E] valid assignments, [E+1] token
+ *                                          tiles, [E+2] assignments dropped because
+ *                                          their id is outside [0, E)
+ *   off[1] sorted list      int32 [A]      assignment index t*topk+s at each sorted position
+ *   off[2] position table   int32 [A]      sorted position of each assignment
+ *   off[3] tile list        int32 [2][A+E] (expert, first position) of each token tile
+ *   off[4] h                binary16 [A][I] expert activations, sorted order
+ *   off[5] d                float [A][H]   expert outputs, sorted order
+ *   off[6] total size
+ * with A = T*topk.  Returns GQ_EINVAL for invalid sizes. */
+gq_status gq_moe_workspace_offsets(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                                   size_t off[7]);
+
+/* Dequantization probes: write every weight of an M x K matrix as binary32
+ * (out32, [M][K]) and/or binary16 (out16, [M][K] bits); either may be NULL.
+ * Bit-exact with the rounding rule above. */
+gq_status gq_dequant_q8_0(const void *w, float *out32, uint16_t *out16, int64_t M, int64_t K,
+                          void *stream);
+gq_status gq_dequant_q4k(const void *w, float *out32, uint16_t *out16, int64_t M, int64_t K,
+                         void *stream);
+
+/* Diagnostics. */
+const char *gq_last_error(void);       /* message of this thread's last failed call */
+const char *gq_status_str(gq_status s); /* short name of a status */
+int gq_version(void);                   /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

@@ -1,0 +1,288 @@
+// gq_api.cpp -- the C ABI of libgq: argument checks, error reporting, launches.
+//
+// Every check runs on the host before anything is launched; a failed check
+// returns its status and leaves a sentence naming the argument and the
+// condition in a per-thread buffer.  Unsupported shapes are refused rather
+// than computed on a subset (page "Frink Inference: the Rust alternative to
+// llama.cpp", section "The goal, stated once", first point: load or refuse
+// with a sentence naming what is missing, never compute something else).
+#include "gq.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gq_status fail(gq_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+gq_status check_ptr(const char *fn, const char *name, const void *p)
+{
+    if (!p)
+        return fail(GQ_EINVAL, "%s: %s is NULL", fn, name);
+    if (!aligned16(p))
+        return fail(GQ_EALIGN, "%s: %s (%p) is not 16-byte aligned", fn, name, p);
+    return GQ_OK;
+}
+
+// Sizes the kernels index with 32-bit row/column counts.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+gq_status check_dim(const char *fn, const char *name, int64_t v, bool allow_zero)
+{
+    if (v < 0 || (!allow_zero && v == 0))
+        return fail(GQ_EINVAL, "%s: %s = %lld must be %s", fn, name, (long long)v,
+                    allow_zero ? "non-negative" : "positive");
+    if (v > kMaxDim)
+        return fail(GQ_ESHAPE, "%s: %s = %lld exceeds the supported maximum %lld", fn, name,
+                    (long long)v, (long long)kMaxDim);
+    return GQ_OK;
+}
+
+gq_status check_k(const char *fn, const char *name, int64_t K, int64_t block)
+{
+    gq_status st = check_dim(fn, name, K, false);
+    if (st != GQ_OK)
+        return st;
+    if (K % block != 0)
+        return fail(GQ_ESHAPE, "%s: %s = %lld is not a multiple of the %lld-weight block", fn,
+                    name, (long long)K, (long long)block);
+    return GQ_OK;
+}
+
+gq_status launched(const char *fn, hipError_t e)
+{
+    if (e != hipSuccess)
+        return fail(GQ_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return GQ_OK;
+}
+
+#define GQ_TRY(expr)                                                                           \
+    do {                                                                                       \
+        gq_status st_ = (expr);                                                                \
+        if (st_ != GQ_OK)                                                                      \
+            return st_;                                                                        \
+    } while (0)
+
+gq_status gemv_checks(const char *fn, const void *w, const float *x, float *y, int64_t M,
+                      int64_t K, int64_t B, int64_t block)
+{
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, block));
+    if (B < 0 || B > GQ_GEMV_MAX_BATCH)
+        return fail(GQ_EINVAL, "%s: B = %lld is outside [0, %d]", fn, (long long)B,
+                    GQ_GEMV_MAX_BATCH);
+    if (M == 0 || B == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "y", y));
+    return GQ_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+gq_status moe_layout(const char *fn, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                     size_t off[7])
+{
+    GQ_TRY(check_dim(fn, "T", T, true));
+    GQ_TRY(check_k(fn, "H", H, 256));
+    GQ_TRY(check_k(fn, "I", I, 256));
+    if (E < 1 || E > 256)
+        return fail(GQ_ESHAPE, "%s: E = %lld is outside the supported range [1, 256]", fn,
+                    (long long)E);
+    if (topk < 1 || topk > E)
+        return fail(GQ_EINVAL, "%s: topk = %lld is outside [1, E = %lld]", fn, (long long)topk,
+                    (long long)E);
+    const int64_t A = T * topk;
+    if (A > ((int64_t)1 << 20))
+        return fail(GQ_ESHAPE, "%s: T*topk = %lld exceeds the supported maximum %lld", fn,
+                    (long long)A, (long long)1 << 20);
+    size_t o = 0;
+    off[0] = o;
+    o = up(o + (size_t)(E + 3) * 4);
+    off[1] = o;
+    o = up(o + (size_t)A * 4);
+    off[2] = o;
+    o = up(o + (size_t)A * 4);
+    off[3] = o;
+    o = up(o + (size_t)2 * (A + E) * 4);
+    off[4] = o;
+    o = up(o + (size_t)A * I * 2);
+    off[5] = o;
+    o = up(o + (size_t)A * H * 4);
+    off[6] = o;
+    return GQ_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
+                       void *stream)
+{
+    static const char fn[] = "gq_gemv_q8_0";
+    GQ_TRY(gemv_checks(fn, w, x, y, M, K, B, 32));
+    if (M == 0 || B == 0)
+        return GQ_OK;
+    return launched(fn, gq::launch_gemv_q8_0(w, x, y, M, K, (int)B, (hipStream_t)stream));
+}
+
+gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
+                      void *stream)
+{
+    static const char fn[] = "gq_gemv_q4k";
+    GQ_TRY(gemv_checks(fn, w, x, y, M, K, B, 256));
+    if (M == 0 || B == 0)
+        return GQ_OK;
+    return launched(fn, gq::launch_gemv_q4k(w, x, y, M, K, (int)B, (hipStream_t)stream));
+}
+
+gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                      int64_t N, void *stream)
+{
+    static const char fn[] = "gq_gemm_q4k";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    GQ_TRY(check_dim(fn, "N", N, true));
+    if (N > ((int64_t)1 << 21))
+        return fail(GQ_ESHAPE, "%s: N = %lld exceeds the supported maximum %lld", fn,
+                    (long long)N, (long long)1 << 21);
+    if (M == 0 || N == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "y", y));
+    return launched(fn, gq::launch_gemm_q4k(w, x, y, M, K, N, (hipStream_t)stream));
+}
+
+size_t gq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk)
+{
+    size_t off[7];
+    char saved[sizeof g_err];
+    memcpy(saved, g_err, sizeof g_err);
+    const gq_status st = moe_layout("gq_moe_workspace_bytes", T, H, I, E, topk, off);
+    if (st != GQ_OK)
+        return 0;
+    memcpy(g_err, saved, sizeof g_err);
+    return off[6];
+}
+
+gq_status gq_moe_workspace_offsets(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                                   size_t off[7])
+{
+    if (!off)
+        return fail(GQ_EINVAL, "gq_moe_workspace_offsets: off is NULL");
+    return moe_layout("gq_moe_workspace_offsets", T, H, I, E, topk, off);
+}
+
+gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_down,
+                          const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                          uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
+                          int64_t topk, void *ws, size_t ws_bytes, void *stream)
+{
+    static const char fn[] = "gq_moe_gemm_q4k";
+    gq::MoeArgs a;
+    GQ_TRY(moe_layout(fn, T, H, I, E, topk, a.off));
+    if (T == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w_gate", w_gate));
+    GQ_TRY(check_ptr(fn, "w_up", w_up));
+    GQ_TRY(check_ptr(fn, "w_down", w_down));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "topk_ids", topk_ids));
+    GQ_TRY(check_ptr(fn, "topk_w", topk_w));
+    GQ_TRY(check_ptr(fn, "out", out));
+    if (!ws)
+        return fail(GQ_EWORKSPACE, "%s: ws is NULL (needs %zu bytes)", fn, a.off[6]);
+    if (!aligned16(ws))
+        return fail(GQ_EALIGN, "%s: ws (%p) is not 16-byte aligned", fn, ws);
+    if (ws_bytes < a.off[6])
+        return fail(GQ_EWORKSPACE, "%s: ws_bytes = %zu is below the required %zu", fn, ws_bytes,
+                    a.off[6]);
+    a.w_gate = (const uint8_t *)w_gate;
+    a.w_up = (const uint8_t *)w_up;
+    a.w_down = (const uint8_t *)w_down;
+    a.x = x;
+    a.ids = topk_ids;
+    a.wts = topk_w;
+    a.out = out;
+    a.T = T;
+    a.H = H;
+    a.I = I;
+    a.E = E;
+    a.topk = topk;
+    a.ws = (uint8_t *)ws;
+    return launched(fn, gq::launch_moe(a, (hipStream_t)stream));
+}
+
+gq_status gq_dequant_q8_0(const void *w, float *out32, uint16_t *out16, int64_t M, int64_t K,
+                          void *stream)
+{
+    static const char fn[] = "gq_dequant_q8_0";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 32));
+    if (M == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    if (!out32 && !out16)
+        return fail(GQ_EINVAL, "%s: out32 and out16 are both NULL", fn);
+    if (out32)
+        GQ_TRY(check_ptr(fn, "out32", out32));
+    if (out16)
+        GQ_TRY(check_ptr(fn, "out16", out16));
+    return launched(fn, gq::launch_dequant_q8_0(w, out32, out16, M, K, (hipStream_t)stream));
+}
+
+gq_status gq_dequant_q4k(const void *w, float *out32, uint16_t *out16, int64_t M, int64_t K,
+                         void *stream)
+{
+    static const char fn[] = "gq_dequant_q4k";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    if (M == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    if (!out32 && !out16)
+        return fail(GQ_EINVAL, "%s: out32 and out16 are both NULL", fn);
+    if (out32)
+        GQ_TRY(check_ptr(fn, "out32", out32));
+    if (out16)
+        GQ_TRY(check_ptr(fn, "out16", out16));
+    return launched(fn, gq::launch_dequant_q4k(w, out32, out16, M, K, (hipStream_t)stream));
+}
+
+const char *gq_last_error(void) { return g_err; }
+
+const char *gq_status_str(gq_status s)
+{
+    switch (s) {
+    case GQ_OK: return "GQ_OK";
+    case GQ_EINVAL: return "GQ_EINVAL";
+    case GQ_ESHAPE: return "GQ_ESHAPE";
+    case GQ_EALIGN: return "GQ_EALIGN";
+    case GQ_EWORKSPACE: return "GQ_EWORKSPACE";
+    case GQ_EHIP: return "GQ_EHIP";
+    }
+    return "GQ_UNKNOWN";
+}
+
+int gq_version(void) { return 100; }
+
+} // extern "C"

@@ -1,0 +1,41 @@
+// gq_internal.h -- launchers behind the C ABI.  Arguments are already
+// validated by gq_api.cpp (sizes positive, K a multiple of the block,
+// pointers non-null and 16-byte aligned) when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gq {
+
+hipError_t launch_dequant_q8_0(const void *w, float *out32, uint16_t *out16, int64_t M,
+                               int64_t K, hipStream_t s);
+hipError_t launch_dequant_q4k(const void *w, float *out32, uint16_t *out16, int64_t M,
+                              int64_t K, hipStream_t s);
+
+hipError_t launch_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K,
+                            int B, hipStream_t s);
+hipError_t launch_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int B,
+                           hipStream_t s);
+
+hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                           int64_t N, hipStream_t s);
+
+// Mixture-of-experts pieces; ws_off are the region offsets of gq_moe_workspace_offsets.
+struct MoeArgs {
+    const uint8_t *w_gate, *w_up, *w_down;
+    const uint16_t *x;
+    const int32_t *ids;
+    const float *wts;
+    uint16_t *out;
+    int64_t T, H, I, E, topk;
+    uint8_t *ws;
+    size_t off[7];
+};
+hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
+
+// Token-tile size used by the grouped products for a given mean tokens per expert.
+int moe_token_tile(int64_t assignments, int64_t experts);
+
+} // namespace gq

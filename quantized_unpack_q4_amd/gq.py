@@ -1,0 +1,215 @@
+"""ctypes binding of libgq.so: the same entry points as ``include/gq.h``.
+
+Argument marshalling only: every step runs in the HIP kernels of libgq.so.
+Tensors are torch tensors on the current HIP device (torch supplies device
+memory and the current stream); binary16 data travels as ``torch.float16``
+or ``torch.int16``/``torch.uint16`` bit patterns.  A missing library is an
+error, never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgq.so")
+
+GQ_OK = 0
+GQ_EINVAL = 1
+GQ_ESHAPE = 2
+GQ_EALIGN = 3
+GQ_EWORKSPACE = 4
+GQ_EHIP = 5
+MAX_BATCH = 16
+
+EXPORTS = (
+    "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemm_q4k", "gq_moe_gemm_q4k",
+    "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
+    "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
+)
+
+
+class GQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libgq.so is not built (%s); run `python -m quantized_unpack_q4_amd.build`"
+                % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        st = ctypes.c_int
+        for name in ("gq_gemv_q8_0", "gq_gemv_q4k"):
+            f = getattr(L, name)
+            f.restype = st
+            f.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.gq_gemm_q4k.restype = st
+        L.gq_gemm_q4k.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.gq_moe_gemm_q4k.restype = st
+        L.gq_moe_gemm_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                      vp, sz, vp]
+        L.gq_moe_workspace_bytes.restype = sz
+        L.gq_moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.gq_moe_workspace_offsets.restype = st
+        L.gq_moe_workspace_offsets.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
+        for name in ("gq_dequant_q8_0", "gq_dequant_q4k"):
+            f = getattr(L, name)
+            f.restype = st
+            f.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.gq_last_error.restype = ctypes.c_char_p
+        L.gq_last_error.argtypes = []
+        L.gq_status_str.restype = ctypes.c_char_p
+        L.gq_status_str.argtypes = [st]
+        L.gq_version.restype = ctypes.c_int
+        L.gq_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().gq_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != GQ_OK:
+        raise GQError(status, "%s: %s" % (lib().gq_status_str(status).decode(), last_error()))
+
+
+def _ptr(t):
+    """Device address of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libgq must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# -- raw entry points (same names as the C ABI) ---------------------------------
+
+def gq_gemv_q8_0(w, x, y, M, K, B, stream=None):
+    _check(lib().gq_gemv_q8_0(_ptr(w), _ptr(x), _ptr(y), M, K, B, _stream(stream)))
+
+
+def gq_gemv_q4k(w, x, y, M, K, B, stream=None):
+    _check(lib().gq_gemv_q4k(_ptr(w), _ptr(x), _ptr(y), M, K, B, _stream(stream)))
+
+
+def gq_gemm_q4k(w, x, y, M, K, N, stream=None):
+    _check(lib().gq_gemm_q4k(_ptr(w), _ptr(x), _ptr(y), M, K, N, _stream(stream)))
+
+
+def gq_moe_workspace_bytes(T, H, I, E, topk) -> int:
+    return int(lib().gq_moe_workspace_bytes(T, H, I, E, topk))
+
+
+def gq_moe_workspace_offsets(T, H, I, E, topk):
+    off = (ctypes.c_size_t * 7)()
+    _check(lib().gq_moe_workspace_offsets(T, H, I, E, topk, off))
+    return list(off)
+
+
+def gq_moe_gemm_q4k(w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I, E, topk, ws,
+                    ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gq_moe_gemm_q4k(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x),
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(out), T, H, I, E, topk,
+                                 _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq_dequant_q8_0(w, out32, out16, M, K, stream=None):
+    _check(lib().gq_dequant_q8_0(_ptr(w), _ptr(out32), _ptr(out16), M, K, _stream(stream)))
+
+
+def gq_dequant_q4k(w, out32, out16, M, K, stream=None):
+    _check(lib().gq_dequant_q4k(_ptr(w), _ptr(out32), _ptr(out16), M, K, _stream(stream)))
+
+
+def gq_version() -> int:
+    return int(lib().gq_version())
+
+
+# -- tensor-level helpers (allocate outputs with torch, then call the ABI) -------
+
+def q4k_row_bytes(K: int) -> int:
+    return K // 256 * 144
+
+
+def q8_0_row_bytes(K: int) -> int:
+    return K // 32 * 34
+
+
+def gemv_q4k(w, x, M: int, K: int, out=None, stream=None):
+    """y[B][M] = x[B][K] * W^T for packed Q4_K w (uint8 device tensor)."""
+    import torch
+    x2 = x.reshape(-1, K)
+    B = x2.shape[0]
+    y = out if out is not None else torch.empty((B, M), dtype=torch.float32, device=x.device)
+    gq_gemv_q4k(w, x2, y, M, K, B, stream)
+    return y
+
+
+def gemv_q8_0(w, x, M: int, K: int, out=None, stream=None):
+    import torch
+    x2 = x.reshape(-1, K)
+    B = x2.shape[0]
+    y = out if out is not None else torch.empty((B, M), dtype=torch.float32, device=x.device)
+    gq_gemv_q8_0(w, x2, y, M, K, B, stream)
+    return y
+
+
+def gemm_q4k(w, x16, M: int, K: int, out=None, stream=None):
+    """Y[N][M] (float16) = X[N][K] (float16) * W^T."""
+    import torch
+    x2 = x16.reshape(-1, K)
+    N = x2.shape[0]
+    y = out if out is not None else torch.empty((N, M), dtype=torch.float16, device=x16.device)
+    gq_gemm_q4k(w, x2, y, M, K, N, stream)
+    return y
+
+
+def moe_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, H: int, I: int, E: int, ws=None,
+            out=None, stream=None):
+    """Mixture-of-experts feed-forward; returns (out [T][H] float16, workspace)."""
+    import torch
+    T, topk = topk_ids.shape
+    need = gq_moe_workspace_bytes(T, H, I, E, topk)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x16.device)
+    o = out if out is not None else torch.empty((T, H), dtype=torch.float16, device=x16.device)
+    gq_moe_gemm_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, o, T, H, I, E, topk, ws,
+                    stream=stream)
+    return o, ws
+
+
+def dequant(fmt: str, w, M: int, K: int, want32=True, want16=True, stream=None):
+    import torch
+    dev = w.device
+    o32 = torch.empty((M, K), dtype=torch.float32, device=dev) if want32 else None
+    o16 = torch.empty((M, K), dtype=torch.float16, device=dev) if want16 else None
+    if fmt == "q4k":
+        gq_dequant_q4k(w, o32, o16, M, K, stream)
+    elif fmt == "q8_0":
+        gq_dequant_q8_0(w, o32, o16, M, K, stream)
+    else:
+        raise ValueError("unknown format %r" % fmt)
+    return o32, o16

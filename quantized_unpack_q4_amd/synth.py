@@ -75,12 +75,12 @@ def q4k_blocks(workload: int, tensor: int, M: int, K: int, scale: float = 1e-3,
     if out is None:
         out = np.empty(nbytes, np.uint8)
     assert out.dtype == np.uint8 and out.size == nbytes
+    # every byte uniform first (the 12 scale/min bytes and 128 quant bytes keep
+    # these), then d and dmin overwrite bytes 0..3 of each super-block
+    out[:] = g.integers(0, 256, size=nbytes, dtype=np.uint8)
     blk = out.reshape(nsb, Q4_K_BLOCK_BYTES)
-    # d and dmin: two binary16 values per super-block, little-endian
     dd = (np.abs(g.standard_normal((nsb, 2))) * scale).astype("<f2")
     blk[:, 0:4] = dd.view(np.uint8).reshape(nsb, 4)
-    # 12 scale/min bytes then 128 quant bytes: uniform random bytes
-    blk[:, 4:] = g.integers(0, 256, size=(nsb, Q4_K_BLOCK_BYTES - 4), dtype=np.uint8)
     return out
 
 

@@ -1,0 +1,115 @@
+"""The C ABI on the CPU: the library loads, exports what include/gq.h declares,
+and refuses bad arguments on the host before anything is launched.  None of
+these calls reaches a kernel launch (every one fails a host-side check)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gq.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from quantized_unpack_q4_amd import gq
+    return gq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    from quantized_unpack_q4_amd import gq
+    names = declared_functions()
+    assert set(names) == set(gq.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.gq_version() >= 100
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: checks fail first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def status_and_msg(L, st):
+    return L.gq_status_str(st).decode(), L.gq_last_error().decode()
+
+
+def test_gemv_refusals(L):
+    for f, blk in ((L.gq_gemv_q4k, 256), (L.gq_gemv_q8_0, 32)):
+        st = f(FAKE, FAKE, FAKE, 16, blk + 32 if blk == 256 else 48, 1, None)
+        s, m = status_and_msg(L, st)
+        assert s == "GQ_ESHAPE" and "K = " in m and "multiple" in m
+        st = f(FAKE, FAKE, FAKE, 16, blk, 17, None)
+        s, m = status_and_msg(L, st)
+        assert s == "GQ_EINVAL" and "B = 17" in m
+        st = f(None, FAKE, FAKE, 16, blk, 1, None)
+        s, m = status_and_msg(L, st)
+        assert s == "GQ_EINVAL" and "w is NULL" in m
+        st = f(FAKE, MISALIGNED, FAKE, 16, blk, 1, None)
+        s, m = status_and_msg(L, st)
+        assert s == "GQ_EALIGN" and "x" in m
+        st = f(FAKE, FAKE, FAKE, -1, blk, 1, None)
+        assert status_and_msg(L, st)[0] == "GQ_EINVAL"
+        st = f(FAKE, FAKE, FAKE, 16, 0, 1, None)
+        assert status_and_msg(L, st)[0] == "GQ_EINVAL"
+        st = f(FAKE, FAKE, FAKE, 1 << 31, blk, 1, None)
+        assert status_and_msg(L, st)[0] == "GQ_ESHAPE"
+        # no work: accepted, nothing launched, pointers not examined
+        assert f(None, None, None, 0, blk, 1, None) == 0
+        assert f(None, None, None, 16, blk, 0, None) == 0
+
+
+def test_gemm_refusals(L):
+    f = L.gq_gemm_q4k
+    assert status_and_msg(L, f(FAKE, FAKE, FAKE, 64, 300, 8, None))[0] == "GQ_ESHAPE"
+    assert status_and_msg(L, f(FAKE, FAKE, MISALIGNED, 64, 256, 8, None))[0] == "GQ_EALIGN"
+    assert status_and_msg(L, f(FAKE, None, FAKE, 64, 256, 8, None))[0] == "GQ_EINVAL"
+    assert status_and_msg(L, f(FAKE, FAKE, FAKE, 64, 256, 1 << 22, None))[0] == "GQ_ESHAPE"
+    assert f(None, None, None, 64, 256, 0, None) == 0
+
+
+def test_moe_workspace_and_refusals(L):
+    from quantized_unpack_q4_amd import gq
+    T, H, I, E, k = 256, 2048, 1024, 64, 8
+    A = T * k
+    need = gq.gq_moe_workspace_bytes(T, H, I, E, k)
+    off = gq.gq_moe_workspace_offsets(T, H, I, E, k)
+    assert off[6] == need and off == sorted(off) and all(o % 256 == 0 for o in off)
+    assert off[5] - off[4] >= A * I * 2 and need - off[5] >= A * H * 4
+    assert off[1] - off[0] >= (E + 3) * 4 and off[4] - off[3] >= 2 * (A + E) * 4
+    assert gq.gq_moe_workspace_bytes(T, H, 1000, E, k) == 0
+    assert gq.gq_moe_workspace_bytes(T, H, I, E, E + 1) == 0
+    assert gq.gq_moe_workspace_bytes(T, H, I, 300, 8) == 0
+    f = L.gq_moe_gemm_q4k
+    args = [FAKE] * 7
+    st = f(*args, T, H, I, E, k, FAKE, need - 1, None)
+    s, m = status_and_msg(L, st)
+    assert s == "GQ_EWORKSPACE" and str(need) in m
+    st = f(*args, T, H, I, E, k, None, need, None)
+    assert status_and_msg(L, st)[0] == "GQ_EWORKSPACE"
+    st = f(*args, T, H, I, E, 0, FAKE, need, None)
+    assert status_and_msg(L, st)[0] == "GQ_EINVAL"
+    st = f(*args, T, 2000, I, E, k, FAKE, need, None)
+    assert status_and_msg(L, st)[0] == "GQ_ESHAPE"
+    st = f(*args, 1 << 20, H, I, E, k, FAKE, 1 << 62, None)
+    assert status_and_msg(L, st)[0] == "GQ_ESHAPE"
+    assert f(*([None] * 7), 0, H, I, E, k, None, 0, None) == 0
+
+
+def test_dequant_refusals(L):
+    assert status_and_msg(L, L.gq_dequant_q4k(FAKE, None, None, 4, 256, None))[0] == "GQ_EINVAL"
+    assert status_and_msg(L, L.gq_dequant_q8_0(FAKE, FAKE, None, 4, 40, None))[0] == "GQ_ESHAPE"
+    assert status_and_msg(L, L.gq_dequant_q8_0(FAKE, MISALIGNED, None, 4, 32, None))[0] == "GQ_EALIGN"
+
+
+def test_binding_raises_on_refusal():
+    from quantized_unpack_q4_amd import gq
+    with pytest.raises(gq.GQError) as ei:
+        gq._check(gq.lib().gq_gemv_q4k(FAKE, FAKE, FAKE, 16, 100, 1, None))
+    assert ei.value.status == gq.GQ_ESHAPE

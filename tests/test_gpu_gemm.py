@@ -1,0 +1,83 @@
+"""Parity of the fused dequant matrix product (prefill) with the binary64 oracle.
+
+Bound: |Y_gpu - Y_ref| <= 2e-3 * S with S = sum_k |w_k x_k|: binary16
+weights and output, binary32 accumulation, oracle in binary64 on the binary32
+weights.  One-hot activation rows must read out the binary16 weights exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_unpack_q4_amd import gq, synth
+from tests._gpu import dev, half_bits, say, torch_cuda, within
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _gemm(w_d, x16, M, K):
+    torch = torch_cuda()
+    N = x16.shape[0]
+    y = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    gq.gq_gemm_q4k(w_d, dev(x16), y, M, K, N)
+    return half_bits(y).view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 256, 1), (130, 512, 37), (256, 1024, 128),
+                                   (200, 2048, 300), (64, 768, 8), (1, 256, 5)])
+def test_gemm_parity_small(M, K, N):
+    say("gemm", M, K, N)
+    w = synth.q4k_blocks(90, M, M, K)
+    x16 = synth.activations_f16(90, N, N, K)
+    y = _gemm(dev(w), x16, M, K)
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K)
+    r = within(y, yr, S, TOL, "gemm %dx%dx%d" % (M, K, N))
+    say("  max err/S", r)
+
+
+@pytest.mark.parametrize("M,K,N", [(14336, 4096, 512), (4096, 14336, 512),
+                                   (14336, 4096, 4096), (4096, 14336, 4096)])
+def test_gemm_parity_prefill_sampled(M, K, N):
+    """Prefill shapes at full size: sampled rows over all tokens, and all rows
+    over sampled tokens."""
+    say("gemm full", M, K, N)
+    g = np.random.default_rng(91)
+    w = synth.q4k_blocks(3, M, M, K)
+    x16 = synth.activations_f16(3, N, N, K)
+    y = _gemm(dev(w), x16, M, K)
+    rows = np.sort(g.choice(M, 24, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    toks = np.sort(g.choice(N, min(N, 256), replace=False))
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K, rows=rows, toks=toks)
+    r1 = within(y[np.ix_(toks, rows)], yr, S, TOL, "rows sample")
+    t2 = np.array([0, N - 1])
+    yr2, S2 = oracle.gemm(oracle.Q4_K, w, x16, M, K, toks=t2)
+    r2 = within(y[t2], yr2, S2, TOL, "token sample")
+    say("  max err/S", r1, r2)
+
+
+def test_gemm_one_hot_exact():
+    M, K = 256, 1024
+    w = synth.q4k_blocks(92, 0, M, K)
+    _, w16 = oracle.dequant(oracle.Q4_K, w, M, K)
+    ks = np.array([0, 1, 31, 32, 63, 64, 255, 256, 300, 511, 512, 700, 1023])
+    x16 = np.zeros((ks.size, K), np.float16)
+    x16[np.arange(ks.size), ks] = 1.0
+    torch = torch_cuda()
+    y = torch.empty((ks.size, M), dtype=torch.float16, device="cuda")
+    gq.gq_gemm_q4k(dev(w), dev(x16), y, M, K, ks.size)
+    yb = half_bits(y)
+    for i, k in enumerate(ks):
+        a = yb[i].view(np.float16)
+        b = w16[:, k].view(np.float16)
+        assert np.array_equal(a, b), k  # equal values (+0 and -0 compare equal)
+
+
+def test_gemm_deterministic():
+    M, K, N = 384, 2048, 200
+    w = dev(synth.q4k_blocks(93, 0, M, K))
+    x16 = synth.activations_f16(93, 0, N, K)
+    a = _gemm(w, x16, M, K)
+    b = _gemm(w, x16, M, K)
+    assert np.array_equal(a, b)

@@ -1,0 +1,158 @@
+"""Parity of the grouped mixture-of-experts feed-forward with the oracle.
+
+Routing (binary64 softmax, top-k, ties to the lower id) is computed once by
+the oracle on the host and passed to both sides, so they route identically.
+The check runs in stages, each against the oracle applied to the GPU's own
+inputs to that stage:
+  (i)   grouping: every assignment sits at a stable, per-expert position;
+  (ii)  h (binary16, in the workspace) against silu(g)*u of the oracle, with a
+        bound propagated from 2e-3 * S_g and 2e-3 * S_u plus binary16 rounding;
+  (iii) d (binary32, in the workspace) against Wd_e h_gpu, bound 2e-3 * S_d;
+  (iv)  out against sum_s w_s * (Wd_e h_gpu), bound 2e-3 * sum_s w_s S_d.
+The end-to-end difference from the all-binary64 oracle is reported.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_unpack_q4_amd import gq, synth
+from tests._gpu import dev, half_bits, host, say, torch_cuda, within
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _dsilu(z):
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def _setup(seed, T, H, I, E, k):
+    wg = synth.q4k_blocks(seed, 0, E * I, H)
+    wu = synth.q4k_blocks(seed, 1, E * I, H)
+    wd = synth.q4k_blocks(seed, 2, E * H, I)
+    x16 = synth.activations_f16(seed, 0, T, H)
+    ids, wts64 = oracle.moe_route(synth.router_logits(seed, 0, T, E), k)
+    return wg, wu, wd, x16, ids, wts64.astype(np.float32)
+
+
+def _run(wg, wu, wd, x16, ids, wts, H, I, E):
+    out, ws = gq.moe_q4k(dev(wg), dev(wu), dev(wd), dev(x16), dev(ids), dev(wts), H, I, E)
+    T, k = ids.shape
+    off = gq.gq_moe_workspace_offsets(T, H, I, E, k)
+    wsh = host(ws)
+    A = T * k
+    table = wsh[off[0]:off[0] + 4 * (E + 3)].view(np.int32)
+    sorted_ = wsh[off[1]:off[1] + 4 * A].view(np.int32)
+    pos_of = wsh[off[2]:off[2] + 4 * A].view(np.int32)
+    h = wsh[off[4]:off[4] + 2 * A * I].view(np.float16).reshape(A, I)
+    d = wsh[off[5]:off[5] + 4 * A * H].view(np.float32).reshape(A, H)
+    o = half_bits(out).view(np.float16).astype(np.float64)
+    return o, table, sorted_, pos_of, h, d
+
+
+def _check_grouping(ids, E, table, sorted_, pos_of):
+    T, k = ids.shape
+    A = T * k
+    flat = ids.reshape(-1)
+    counts = np.bincount(flat, minlength=E)
+    assert np.array_equal(table[:E], np.concatenate([[0], np.cumsum(counts)[:-1]]))
+    assert table[E] == A and table[E + 2] == 0
+    # stable order: sorted by (expert, assignment index)
+    ref = np.lexsort((np.arange(A), flat))
+    assert np.array_equal(sorted_, ref)
+    assert np.array_equal(pos_of[sorted_], np.arange(A))
+
+
+def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks):
+    T, k = ids.shape
+    gu = I * (H // 256) * 144
+    dn = H * (I // 256) * 144
+    worst = {"h": 0.0, "d": 0.0, "out": 0.0}
+    for t in toks:
+        acc = np.zeros(H)
+        accS = np.zeros(H)
+        for s in range(k):
+            a = t * k + s
+            e = ids[t, s]
+            p = pos_of[a]
+            assert sorted_[p] == a
+            # (ii) h against the oracle's g and u for this token and expert
+            g, Sg = oracle.gemm(oracle.Q4_K, wg[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
+            u, Su = oracle.gemm(oracle.Q4_K, wu[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
+            g, Sg, u, Su = g[0], Sg[0], u[0], Su[0]
+            href = _silu(g) * u
+            bound = TOL * (np.abs(_dsilu(g) * u) * Sg + np.abs(_silu(g)) * Su) \
+                + np.abs(href) * 2.0 ** -10 + 2.0 ** -24
+            err = np.abs(h[p].astype(np.float64) - href)
+            assert np.all(err <= bound), ("h", t, s, float((err - bound).max()))
+            worst["h"] = max(worst["h"], float((err / bound).max()))
+            # (iii) d against Wd_e applied to the GPU's own h
+            dref, Sd = oracle.gemm(oracle.Q4_K, wd[e * dn:(e + 1) * dn],
+                                   h[p:p + 1].view(np.uint16), H, I)
+            worst["d"] = max(worst["d"], within(d[p], dref[0], Sd[0], TOL, "d"))
+            acc += np.float64(wts[t, s]) * dref[0]
+            accS += np.float64(wts[t, s]) * Sd[0]
+        # (iv) combine
+        worst["out"] = max(worst["out"], within(o[t], acc, accS, TOL, "out t=%d" % t))
+    return worst
+
+
+def test_moe_small_full():
+    T, H, I, E, k = 5, 512, 256, 4, 2
+    wg, wu, wd, x16, ids, wts = _setup(60, T, H, I, E, k)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
+                    range(T))
+    r = oracle.moe_ffn(wg, wu, wd, x16, ids, wts, H, I, E)
+    say("moe small staged", worst, "end-to-end", _e2e(o, r, wts))
+
+
+def _e2e(o, r, wts):
+    """Largest |out_gpu - out_ref| / sum_s w_s S_d over the binary64 oracle (reported)."""
+    T, k = wts.shape
+    Sd = r["Sd"].reshape(T, k, -1)
+    bound = np.einsum("tk,tkh->th", np.abs(wts).astype(np.float64), Sd)
+    return float((np.abs(o - r["out"]) / np.maximum(bound, 1e-300)).max())
+
+
+def test_moe_empty_expert_and_dropped_ids():
+    """Experts that receive no token, and ids outside [0, E), which are skipped."""
+    T, H, I, E, k = 6, 256, 256, 8, 2
+    wg, wu, wd, x16, _, _ = _setup(61, T, H, I, E, k)
+    ids = np.array([[0, 3], [3, 0], [5, 3], [0, 5], [3, 9], [-1, 0]], np.int32)
+    wts = np.full((T, k), 0.5, np.float32)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E)
+    assert table[E + 2] == 2  # the two out-of-range ids
+    assert pos_of[4 * 2 + 1] == -1 and pos_of[5 * 2 + 0] == -1
+    valid = (ids >= 0) & (ids < E)
+    counts = np.bincount(ids[valid], minlength=E)
+    assert np.array_equal(table[:E], np.concatenate([[0], np.cumsum(counts)[:-1]]))
+    assert table[E] == valid.sum()
+    # every valid slot still combines exactly like the full check
+    ids_ok = np.where(valid, ids, 0)
+    wts_ok = np.where(valid, wts, 0).astype(np.float32)
+    r = oracle.moe_ffn(wg, wu, wd, x16, ids_ok, wts_ok, H, I, E)
+    ratio = _e2e(o, r, wts_ok)
+    say("moe dropped ids end-to-end", ratio)
+    assert ratio <= 2 * TOL
+
+
+@pytest.mark.parametrize("T", [256, 2048])
+def test_moe_olmoe_shape_sampled(T):
+    """OLMoE-1B-7B-shaped layer (64 experts, top-8, hidden 2048, expert 1024) at
+    full size; grouping checked whole, values on sampled tokens."""
+    H, I, E, k = 2048, 1024, 64, 8
+    say("moe olmoe T", T)
+    wg, wu, wd, x16, ids, wts = _setup(4, T, H, I, E, k)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    toks = [0, T // 2, T - 1]
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks)
+    say("  staged worst ratios", worst)
