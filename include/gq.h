@@ -84,6 +84,35 @@ gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64
 gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                       void *stream);
 
+/* Batch-1 Q4_K matrix-vector products of a whole table of independent
+ * matrices in ONE launch (a decode step of a transformer's linear layers:
+ * every weight byte streamed once, no per-matrix launch cost).  The pages cut
+ * the same per-matmul overhead by grouping work into fewer GPU submissions
+ * (page "Frink Inference: the Rust alternative to llama.cpp", section "The
+ * engine").  Use in three steps:
+ *   1. bytes = gq_gemv_q4k_multi_table_bytes(n);
+ *   2. gq_gemv_q4k_multi_plan(descs, n, table, bytes) checks every descriptor
+ *      on the host and writes the work table into host memory `table`;
+ *   3. copy those bytes once to a device buffer `table_dev` (16-byte aligned)
+ *      and call gq_gemv_q4k_multi(table, table_dev, stream) as often as needed;
+ *      each call computes y_i = W_i x_i for every descriptor i.
+ * The table holds the descriptors' pointers: it stays valid as long as those
+ * buffers do.  table_dev must hold exactly the bytes of `table` (only the host
+ * copy is checked).  Each descriptor needs K % 256 == 0, 256 <= K <= 16384,
+ * M >= 1 and 16-byte aligned w, x, y; x is [K] and y is [M] (batch 1).
+ * Products run concurrently: outputs must not overlap any input. */
+typedef struct gq_gemv_desc {
+    const void *w; /* Q4_K weights, M rows of K/256 super-blocks */
+    const float *x; /* [K] binary32 */
+    float *y;       /* [M] binary32 */
+    int64_t M, K;
+} gq_gemv_desc;
+
+size_t gq_gemv_q4k_multi_table_bytes(int64_t n); /* 0 if n is outside [1, 2^20] */
+gq_status gq_gemv_q4k_multi_plan(const gq_gemv_desc *descs, int64_t n, void *table,
+                                 size_t table_bytes);
+gq_status gq_gemv_q4k_multi(const void *table, const void *table_dev, void *stream);
+
 /* Q4_K matrix product for prefill, binary16 activations and output:
  *   Y[n][r] = binary16( sum_k X[n][k] * w16[r][k] ),  accumulated in binary32,
  * where w16 is each weight rounded to binary16 as described above.

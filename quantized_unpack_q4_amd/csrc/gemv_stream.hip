@@ -1,0 +1,390 @@
+// gemv_stream.hip -- batch-1 Q4_K matrix-vector products streamed by a
+// persistent grid, for one matrix or for a whole table of independent
+// matrices (a decode step) in a single launch.
+//
+// Decode is memory-bound: every packed weight byte is read once and the
+// dequantization is fused into the dot product (page "Building a Rust
+// Inference Engine That Matches Llama.cpp", section "Where the wins came
+// from").  A launch per matrix costs a fixed ramp-up and drain that, summed
+// over a 224-matrix step, is as large as the streaming itself; the pages fight
+// the same per-matmul overhead with fewer GPU submissions (page "Frink
+// Inference: the Rust alternative to llama.cpp", section "The engine":
+// command-buffer waits per token cut from 192 to 20, one submission per group
+// of layers).  Here the whole table is one launch: the total weight bytes are
+// split into equal contiguous byte ranges, one per workgroup, and a workgroup
+// processes every row tile that starts inside its range.
+//
+// Arithmetic per lane.  Two lanes share a 256-weight super-block: lane p
+// (0 or 1) owns quant groups p and p + 2, i.e. sub-blocks 2p, 2p+1, 2p+4 and
+// 2p+5, whose scales come from the same three scale bytes per pair (j, j+4).
+// Activations are scaled by a power of two (max|x| into [2^14, 2^15)), split
+// as x = hi + lo with hi, lo binary16 (about 22 significant bits together)
+// and staged in LDS once per matrix; the scale is undone exactly.  Quants are
+// used as binary16 subnormals (the nibble bits themselves, q * 2^-24, or
+// 16q * 2^-24 for high nibbles), so one v_dot2_f32_f16 multiplies two quants
+// by two activation halves exactly and accumulates in binary32.  Per
+// sub-block j the contribution is (d*sc_j) * sum(q*x) - (dmin*m_j) * sum(x);
+// sum(x) per sub-block is staged with x.  With a one-hot x the result is the
+// binary32 weight exactly (d*sc*q exact, one rounding with -dmin*m).
+//
+// Pipelining: each wave issues the global loads of its next step before
+// computing the current one; the loads are unconditional (out-of-range rows
+// and super-blocks read a clamped in-range address and get a zero header), so
+// the compiler can wait for exactly the older loads.
+#include "gq_device.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const f32x4 g_f32x4;
+
+__device__ __forceinline__ uint4 gload16(const void *p)
+{
+    const u32x4 v = *(g_u32x4 *)(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float4 gloadf4(const float *p)
+{
+    const f32x4 v = *(g_f32x4 *)(p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c,
+                                  false);
+}
+
+// Sum over each row of 16 lanes (xor 1, xor 2, rotate 4, rotate 8); every lane
+// of the row ends with the row's sum.
+__device__ __forceinline__ float rowsum16(float v)
+{
+#define GQ_DPP(x, ctrl)                                                                          \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, \
+                                                          0xF, 0xF, true))
+    v += GQ_DPP(v, 0xB1);  // quad_perm [1,0,3,2]
+    v += GQ_DPP(v, 0x4E);  // quad_perm [2,3,0,1]
+    v += GQ_DPP(v, 0x124); // row_ror:4
+    v += GQ_DPP(v, 0x128); // row_ror:8
+#undef GQ_DPP
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+constexpr int kStreamMaxK = GemvStreamMaxK;
+constexpr int kRecs = kStreamMaxK / 4;                      // 16-byte x records
+constexpr int kLdsWords = (kRecs + kRecs / 16) * 4 + kStreamMaxK / 32;
+constexpr int kR = 3;                                       // row pairs per wave step
+constexpr int kRowsPerWave = 2 * kR;
+constexpr int kTileRows = 4 * kRowsPerWave;                 // rows per workgroup tile
+
+struct Frag {
+    uint4 hd, a0, a1, b0, b1; // header, quant group p (32 B), quant group p+2 (32 B)
+    bool ok;
+};
+
+__device__ __forceinline__ uint32_t word8(const uint4 &a, const uint4 &b, int i)
+{
+    return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : i == 3 ? a.w
+         : i == 4 ? b.x : i == 5 ? b.y : i == 6 ? b.z : b.w;
+}
+
+} // namespace
+
+__global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry *__restrict__ table,
+                                                                 GemvEntry inline0, int n,
+                                                                 long long total)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+    uint32_t *xrec = lds;
+    float *ssum = reinterpret_cast<float *>(lds + (kRecs + kRecs / 16) * 4);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, p = lane & 1, sbl = (lane & 31) >> 1;
+    const long long lo = total * (long long)blockIdx.x / gridDim.x;
+    const long long hi = total * (long long)(blockIdx.x + 1) / gridDim.x;
+
+    auto entry = [&](int i) -> GemvEntry { return table ? table[i] : inline0; };
+    int di = 0;
+    while (di + 1 < n && entry(di + 1).byte_begin <= lo)
+        ++di;
+
+    GemvEntry e = entry(di);
+    int nsb = e.K >> 8;
+    size_t rowb = (size_t)nsb * kQ4kBytes;
+    long long tile_bytes = (long long)kTileRows * (long long)rowb;
+    int ntile = (e.M + kTileRows - 1) / kTileRows;
+    int rt = (int)((lo - e.byte_begin + tile_bytes - 1) / tile_bytes);
+    while (rt >= ntile) {
+        if (++di >= n)
+            return;
+        e = entry(di);
+        if (e.byte_begin >= hi)
+            return;
+        nsb = e.K >> 8;
+        rowb = (size_t)nsb * kQ4kBytes;
+        tile_bytes = (long long)kTileRows * (long long)rowb;
+        ntile = (e.M + kTileRows - 1) / kTileRows;
+        rt = 0;
+    }
+    if (e.byte_begin + (long long)rt * tile_bytes >= hi)
+        return;
+
+    // Power-of-two scale that brings max|x| into [2^14, 2^15): keeps the
+    // binary16 hi/lo split accurate for any finite x of moderate magnitude.
+    __shared__ float s_amax[4];
+    float inv_scale = 1.f;
+    auto stage = [&]() {
+        const int nrec = e.K >> 2;
+        float amax = 0.f;
+        for (int i = tid; i < nrec; i += 256) {
+            const float4 v = gloadf4(e.x + 4 * i);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        if (lane == 0)
+            s_amax[wave] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+        int ex = 0;
+        if (amax > 0.f)
+            (void)frexpf(amax, &ex); // amax < 2^ex
+        const float scale = ldexpf(1.f, 15 - ex);
+        inv_scale = ldexpf(1.f, ex - 15);
+        // record i holds x[4i..4i+3]*scale as (hi(x0,x2), hi(x1,x3), lo(x0,x2),
+        // lo(x1,x3)); 16 bytes of padding after every 16 records.  ssum[j] is
+        // the plain binary32 sum of x over sub-block j.
+        for (int i = tid; i < nrec; i += 256) {
+            float4 v = gloadf4(e.x + 4 * i);
+            v.x *= scale;
+            v.y *= scale;
+            v.z *= scale;
+            v.w *= scale;
+            const h2_t h02 = {(_Float16)v.x, (_Float16)v.z}, h13 = {(_Float16)v.y, (_Float16)v.w};
+            const h2_t l02 = {(_Float16)(v.x - (float)h02.x), (_Float16)(v.z - (float)h02.y)};
+            const h2_t l13 = {(_Float16)(v.y - (float)h13.x), (_Float16)(v.w - (float)h13.y)};
+            *reinterpret_cast<uint4 *>(xrec + 4 * (i + (i >> 4))) =
+                make_uint4(__builtin_bit_cast(uint32_t, h02), __builtin_bit_cast(uint32_t, h13),
+                           __builtin_bit_cast(uint32_t, l02), __builtin_bit_cast(uint32_t, l13));
+        }
+        for (int j = tid; j < (e.K >> 5); j += 256) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; i += 4) {
+                const float4 v = gloadf4(e.x + 32 * j + i);
+                s += (v.x + v.y) + (v.z + v.w);
+            }
+            ssum[j] = s;
+        }
+    };
+
+    auto issue = [&](Frag (&f)[kR], int row0, int s) {
+        const int sc = s < nsb ? s : nsb - 1;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int row = row0 + 2 * r + half;
+            const int rc = row < e.M ? row : e.M - 1;
+            const uint8_t *blk = e.w + (size_t)rc * rowb + (size_t)sc * kQ4kBytes;
+            f[r].hd = gload16(blk);
+            f[r].a0 = gload16(blk + 16 + 32 * p);
+            f[r].a1 = gload16(blk + 32 + 32 * p);
+            f[r].b0 = gload16(blk + 80 + 32 * p);
+            f[r].b1 = gload16(blk + 96 + 32 * p);
+            f[r].ok = s < nsb && row < e.M;
+        }
+    };
+
+    stage();
+    __syncthreads();
+    for (;;) {
+        const int nchunk = (nsb + 15) >> 4;
+        const long long lim = (hi - e.byte_begin + tile_bytes - 1) / tile_bytes;
+        const int rt_end = (int)(lim < ntile ? lim : ntile);
+        const int step_hi = rt_end * nchunk;
+        int st = rt * nchunk;
+        Frag A[kR], B[kR];
+        float acc[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+            acc[r] = 0.f;
+        issue(A, rt * kTileRows + wave * kRowsPerWave, sbl);
+
+        auto step = [&](Frag (&cur)[kR], Frag (&nxt)[kR]) -> bool {
+            const int t = st / nchunk, c = st - t * nchunk;
+            const int nst = st + 1 < step_hi ? st + 1 : st;
+            const int nt = nst / nchunk, nc = nst - nt * nchunk;
+            issue(nxt, nt * kTileRows + wave * kRowsPerWave, nc * 16 + sbl);
+
+            const int s = min(c * 16 + sbl, nsb - 1);
+            const int r0 = 64 * s + 16 * p; // x record of sub-block 2p, position 0
+            const int r4 = r0 + 32;         // x record of sub-block 2p+4
+            float P0[kR], P1[kR], P4[kR], P5[kR];
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                P0[r] = 0.f;
+                P1[r] = 0.f;
+                P4[r] = 0.f;
+                P5[r] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int ia = r0 + i, ib = r0 + 8 + i, ic = r4 + i, id = r4 + 8 + i;
+                const uint4 xa = *reinterpret_cast<const uint4 *>(xrec + 4 * (ia + (ia >> 4)));
+                const uint4 xb = *reinterpret_cast<const uint4 *>(xrec + 4 * (ib + (ib >> 4)));
+                const uint4 xc = *reinterpret_cast<const uint4 *>(xrec + 4 * (ic + (ic >> 4)));
+                const uint4 xd = *reinterpret_cast<const uint4 *>(xrec + 4 * (id + (id >> 4)));
+#pragma unroll
+                for (int r = 0; r < kR; ++r) {
+                    const uint32_t D = word8(cur[r].a0, cur[r].a1, i);
+                    const uint32_t E = word8(cur[r].b0, cur[r].b1, i);
+                    const uint32_t td = D >> 8, te = E >> 8;
+                    // quant pairs as binary16 subnormals: low nibbles (q0,q2),(q1,q3)
+                    // and high nibbles as 16q
+                    const uint32_t dl02 = D & 0x000F000Fu, dl13 = td & 0x000F000Fu;
+                    const uint32_t dh02 = D & 0x00F000F0u, dh13 = td & 0x00F000F0u;
+                    const uint32_t el02 = E & 0x000F000Fu, el13 = te & 0x000F000Fu;
+                    const uint32_t eh02 = E & 0x00F000F0u, eh13 = te & 0x00F000F0u;
+                    P0[r] = dot2(dl02, xa.x, P0[r]);
+                    P0[r] = dot2(dl02, xa.z, P0[r]);
+                    P0[r] = dot2(dl13, xa.y, P0[r]);
+                    P0[r] = dot2(dl13, xa.w, P0[r]);
+                    P1[r] = dot2(dh02, xb.x, P1[r]);
+                    P1[r] = dot2(dh02, xb.z, P1[r]);
+                    P1[r] = dot2(dh13, xb.y, P1[r]);
+                    P1[r] = dot2(dh13, xb.w, P1[r]);
+                    P4[r] = dot2(el02, xc.x, P4[r]);
+                    P4[r] = dot2(el02, xc.z, P4[r]);
+                    P4[r] = dot2(el13, xc.y, P4[r]);
+                    P4[r] = dot2(el13, xc.w, P4[r]);
+                    P5[r] = dot2(eh02, xd.x, P5[r]);
+                    P5[r] = dot2(eh02, xd.z, P5[r]);
+                    P5[r] = dot2(eh13, xd.y, P5[r]);
+                    P5[r] = dot2(eh13, xd.w, P5[r]);
+                }
+            }
+            const float2 s01 = *reinterpret_cast<const float2 *>(ssum + 8 * s + 2 * p);
+            const float2 s45 = *reinterpret_cast<const float2 *>(ssum + 8 * s + 2 * p + 4);
+            const int o0 = 16 * p, o1 = 16 * p + 8; // bit offsets of scale bytes 2p, 2p+1
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                const uint32_t h0 = cur[r].ok ? cur[r].hd.x : 0u;
+                const uint32_t h1 = cur[r].hd.y, h2 = cur[r].hd.z, h3 = cur[r].hd.w;
+                // sub-blocks j in {2p, 2p+1}: whole 6-bit values in s[j], s[j+4];
+                // sub-blocks j+4: low nibbles of s[j+8], top bits of s[j], s[j+4]
+                const uint32_t sc0 = __builtin_amdgcn_ubfe(h1, o0, 6);
+                const uint32_t m0 = __builtin_amdgcn_ubfe(h2, o0, 6);
+                const uint32_t sc1 = __builtin_amdgcn_ubfe(h1, o1, 6);
+                const uint32_t m1 = __builtin_amdgcn_ubfe(h2, o1, 6);
+                const uint32_t sc4 =
+                    __builtin_amdgcn_ubfe(h3, o0, 4) | (__builtin_amdgcn_ubfe(h1, o0 + 6, 2) << 4);
+                const uint32_t m4 = __builtin_amdgcn_ubfe(h3, o0 + 4, 4) |
+                                    (__builtin_amdgcn_ubfe(h2, o0 + 6, 2) << 4);
+                const uint32_t sc5 =
+                    __builtin_amdgcn_ubfe(h3, o1, 4) | (__builtin_amdgcn_ubfe(h1, o1 + 6, 2) << 4);
+                const uint32_t m5 = __builtin_amdgcn_ubfe(h3, o1 + 4, 4) |
+                                    (__builtin_amdgcn_ubfe(h2, o1 + 6, 2) << 4);
+                // quants entered as q*2^-24 (low) and q*2^-20 (high): fold 2^24 into d
+                const float d24 = half_to_float(h0) * 16777216.f;
+                const float dmin = half_to_float(h0 >> 16);
+                float t1 = (float)sc0 * P0[r];
+                t1 = fmaf((float)sc1 * 0.0625f, P1[r], t1);
+                t1 = fmaf((float)sc4, P4[r], t1);
+                t1 = fmaf((float)sc5 * 0.0625f, P5[r], t1);
+                float t2 = (float)m0 * s01.x;
+                t2 = fmaf((float)m1, s01.y, t2);
+                t2 = fmaf((float)m4, s45.x, t2);
+                t2 = fmaf((float)m5, s45.y, t2);
+                acc[r] = fmaf(-dmin, t2, fmaf(d24, t1 * inv_scale, acc[r]));
+            }
+            if (c == nchunk - 1) {
+                const int row0 = t * kTileRows + wave * kRowsPerWave;
+#pragma unroll
+                for (int r = 0; r < kR; ++r) {
+                    const float v = rowsum16(acc[r]);
+                    const float v0 = lane_value(v, 0) + lane_value(v, 16);
+                    const float v1 = lane_value(v, 32) + lane_value(v, 48);
+                    if (lane == 0 && row0 + 2 * r < e.M)
+                        e.y[row0 + 2 * r] = v0;
+                    if (lane == 1 && row0 + 2 * r + 1 < e.M)
+                        e.y[row0 + 2 * r + 1] = v1;
+                    acc[r] = 0.f;
+                }
+            }
+            ++st;
+            return st < step_hi;
+        };
+        for (;;) {
+            if (!step(A, B))
+                break;
+            if (!step(B, A))
+                break;
+        }
+        // next matrix of the table, if it starts inside this workgroup's range
+        if (++di >= n)
+            return;
+        e = entry(di);
+        if (e.byte_begin >= hi)
+            return;
+        nsb = e.K >> 8;
+        rowb = (size_t)nsb * kQ4kBytes;
+        tile_bytes = (long long)kTileRows * (long long)rowb;
+        ntile = (e.M + kTileRows - 1) / kTileRows;
+        rt = 0;
+        __syncthreads();
+        stage();
+        __syncthreads();
+    }
+}
+
+static int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cus[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+int gemv_stream_grid(long long total_bytes, long long tiles)
+{
+    long long g = 4LL * device_cus();
+    if (tiles < g)
+        g = tiles;
+    return (int)(g > 0 ? g : 1);
+}
+
+long long gemv_stream_tiles(int64_t M, int64_t K)
+{
+    (void)K;
+    return (M + kTileRows - 1) / kTileRows;
+}
+
+hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
+                              long long total_bytes, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(gemv_q4k_stream_kernel, dim3((unsigned)grid), dim3(256), 0, s, table_dev,
+                       inline0, n, total_bytes);
+    return hipGetLastError();
+}
+
+} // namespace gq

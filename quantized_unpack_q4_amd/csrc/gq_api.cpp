@@ -151,7 +151,99 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
     GQ_TRY(gemv_checks(fn, w, x, y, M, K, B, 256));
     if (M == 0 || B == 0)
         return GQ_OK;
+    if (B == 1 && K <= gq::GemvStreamMaxK) {
+        gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0};
+        const long long total = (long long)M * (K / 256) * 144;
+        const int grid = gq::gemv_stream_grid(total, gq::gemv_stream_tiles(M, K));
+        return launched(fn, gq::launch_gemv_stream(nullptr, e, 1, total, grid, (hipStream_t)stream));
+    }
     return launched(fn, gq::launch_gemv_q4k(w, x, y, M, K, (int)B, (hipStream_t)stream));
+}
+
+// Table of a batch-1 multi-product: a 32-byte header, then n entries laid out
+// as gq::GemvEntry.  The same bytes are read on the host (checks, launch
+// shape) and on the device (the kernel).
+namespace {
+constexpr uint32_t kTableMagic = 0x544D5147u; // "GQMT"
+constexpr uint32_t kTableVersion = 1;
+struct TableHeader {
+    uint32_t magic, version;
+    int64_t n;
+    int64_t total_bytes;
+    int64_t total_tiles;
+};
+static_assert(sizeof(TableHeader) == 32, "table header layout");
+} // namespace
+
+size_t gq_gemv_q4k_multi_table_bytes(int64_t n)
+{
+    if (n < 1 || n > ((int64_t)1 << 20))
+        return 0;
+    return sizeof(TableHeader) + (size_t)n * sizeof(gq::GemvEntry);
+}
+
+gq_status gq_gemv_q4k_multi_plan(const gq_gemv_desc *descs, int64_t n, void *table,
+                                 size_t table_bytes)
+{
+    static const char fn[] = "gq_gemv_q4k_multi_plan";
+    if (!descs)
+        return fail(GQ_EINVAL, "%s: descs is NULL", fn);
+    if (n < 1 || n > ((int64_t)1 << 20))
+        return fail(GQ_EINVAL, "%s: n = %lld is outside [1, 2^20]", fn, (long long)n);
+    if (!table)
+        return fail(GQ_EINVAL, "%s: table is NULL", fn);
+    if (table_bytes < gq_gemv_q4k_multi_table_bytes(n))
+        return fail(GQ_EWORKSPACE, "%s: table_bytes = %zu is below the required %zu", fn,
+                    table_bytes, gq_gemv_q4k_multi_table_bytes(n));
+    int64_t total = 0, tiles = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const gq_gemv_desc &d = descs[i];
+        char name[64];
+        snprintf(name, sizeof name, "descs[%lld].M", (long long)i);
+        GQ_TRY(check_dim(fn, name, d.M, false));
+        snprintf(name, sizeof name, "descs[%lld].K", (long long)i);
+        GQ_TRY(check_k(fn, name, d.K, 256));
+        if (d.K > gq::GemvStreamMaxK)
+            return fail(GQ_ESHAPE, "%s: descs[%lld].K = %lld exceeds %d", fn, (long long)i,
+                        (long long)d.K, gq::GemvStreamMaxK);
+        snprintf(name, sizeof name, "descs[%lld].w", (long long)i);
+        GQ_TRY(check_ptr(fn, name, d.w));
+        snprintf(name, sizeof name, "descs[%lld].x", (long long)i);
+        GQ_TRY(check_ptr(fn, name, d.x));
+        snprintf(name, sizeof name, "descs[%lld].y", (long long)i);
+        GQ_TRY(check_ptr(fn, name, d.y));
+        total += d.M * (d.K / 256) * 144;
+        tiles += gq::gemv_stream_tiles(d.M, d.K);
+    }
+    TableHeader h{kTableMagic, kTableVersion, n, total, tiles};
+    memcpy(table, &h, sizeof h);
+    gq::GemvEntry *ent = reinterpret_cast<gq::GemvEntry *>((uint8_t *)table + sizeof h);
+    int64_t begin = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const gq_gemv_desc &d = descs[i];
+        gq::GemvEntry e{(const uint8_t *)d.w, d.x, d.y, (int)d.M, (int)d.K, begin};
+        memcpy(&ent[i], &e, sizeof e);
+        begin += d.M * (d.K / 256) * 144;
+    }
+    return GQ_OK;
+}
+
+gq_status gq_gemv_q4k_multi(const void *table, const void *table_dev, void *stream)
+{
+    static const char fn[] = "gq_gemv_q4k_multi";
+    if (!table)
+        return fail(GQ_EINVAL, "%s: table is NULL", fn);
+    TableHeader h;
+    memcpy(&h, table, sizeof h);
+    if (h.magic != kTableMagic || h.version != kTableVersion || h.n < 1)
+        return fail(GQ_EINVAL, "%s: table was not written by gq_gemv_q4k_multi_plan", fn);
+    GQ_TRY(check_ptr(fn, "table_dev", table_dev));
+    const gq::GemvEntry *dev = reinterpret_cast<const gq::GemvEntry *>(
+        (const uint8_t *)table_dev + sizeof(TableHeader));
+    const gq::GemvEntry none{};
+    const int grid = gq::gemv_stream_grid(h.total_bytes, h.total_tiles);
+    return launched(fn, gq::launch_gemv_stream(dev, none, (int)h.n, h.total_bytes, grid,
+                                               (hipStream_t)stream));
 }
 
 gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,

@@ -19,6 +19,22 @@ hipError_t launch_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, 
 hipError_t launch_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int B,
                            hipStream_t s);
 
+// Persistent batch-1 Q4_K matrix-vector products over a table of matrices.
+constexpr int GemvStreamMaxK = 16384;
+struct GemvEntry {
+    const uint8_t *w; // Q4_K weights, M rows of K/256 super-blocks
+    const float *x;   // [K]
+    float *y;         // [M]
+    int M, K;
+    long long byte_begin; // sum of the weight bytes of the entries before this one
+};
+static_assert(sizeof(GemvEntry) == 40, "table entry layout");
+long long gemv_stream_tiles(int64_t M, int64_t K);
+int gemv_stream_grid(long long total_bytes, long long tiles);
+// table_dev == nullptr: a single matrix given by inline0 (n must be 1)
+hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
+                              long long total_bytes, int grid, hipStream_t s);
+
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s);
 

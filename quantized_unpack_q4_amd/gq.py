@@ -23,7 +23,8 @@ GQ_EHIP = 5
 MAX_BATCH = 16
 
 EXPORTS = (
-    "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemm_q4k", "gq_moe_gemm_q4k",
+    "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
+    "gq_gemv_q4k_multi", "gq_gemm_q4k", "gq_moe_gemm_q4k",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
 )
@@ -53,6 +54,12 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.gq_gemv_q4k_multi_table_bytes.restype = sz
+        L.gq_gemv_q4k_multi_table_bytes.argtypes = [i64]
+        L.gq_gemv_q4k_multi_plan.restype = st
+        L.gq_gemv_q4k_multi_plan.argtypes = [vp, i64, vp, sz]
+        L.gq_gemv_q4k_multi.restype = st
+        L.gq_gemv_q4k_multi.argtypes = [vp, vp, vp]
         L.gq_gemm_q4k.restype = st
         L.gq_gemm_q4k.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.gq_moe_gemm_q4k.restype = st
@@ -111,6 +118,54 @@ def gq_gemv_q8_0(w, x, y, M, K, B, stream=None):
 
 def gq_gemv_q4k(w, x, y, M, K, B, stream=None):
     _check(lib().gq_gemv_q4k(_ptr(w), _ptr(x), _ptr(y), M, K, B, _stream(stream)))
+
+
+class GemvDesc(ctypes.Structure):
+    """Mirror of gq_gemv_desc."""
+    _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+def gq_gemv_q4k_multi_table_bytes(n) -> int:
+    return int(lib().gq_gemv_q4k_multi_table_bytes(n))
+
+
+def gq_gemv_q4k_multi_plan(descs, n, table, table_bytes):
+    _check(lib().gq_gemv_q4k_multi_plan(descs, n, table, table_bytes))
+
+
+def gq_gemv_q4k_multi(table, table_dev, stream=None):
+    _check(lib().gq_gemv_q4k_multi(table, _ptr(table_dev), _stream(stream)))
+
+
+class GemvTable:
+    """A planned batch-1 multi-product: host table + its device copy.
+
+    ``items`` is a list of (w, x, y, M, K) with torch device tensors; the
+    tensors must stay alive while the table is used.
+    """
+
+    def __init__(self, items):
+        import torch
+        n = len(items)
+        arr = (GemvDesc * n)()
+        for i, (w, x, y, M, K) in enumerate(items):
+            for t in (w, x, y):
+                if not t.is_contiguous():
+                    raise ValueError("tensors passed to libgq must be contiguous")
+            arr[i] = GemvDesc(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K)
+        nbytes = gq_gemv_q4k_multi_table_bytes(n)
+        if nbytes == 0:
+            raise ValueError("bad table size n=%d" % n)
+        self.host = (ctypes.c_uint8 * nbytes)()
+        gq_gemv_q4k_multi_plan(arr, n, self.host, nbytes)
+        host_t = torch.frombuffer(bytearray(bytes(self.host)), dtype=torch.uint8)
+        self.dev = host_t.to(items[0][0].device)
+        self.items = items
+        self.n = n
+
+    def run(self, stream=None):
+        gq_gemv_q4k_multi(self.host, self.dev, stream)
 
 
 def gq_gemm_q4k(w, x, y, M, K, N, stream=None):

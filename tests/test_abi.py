@@ -113,3 +113,48 @@ def test_binding_raises_on_refusal():
     with pytest.raises(gq.GQError) as ei:
         gq._check(gq.lib().gq_gemv_q4k(FAKE, FAKE, FAKE, 16, 100, 1, None))
     assert ei.value.status == gq.GQ_ESHAPE
+
+
+def test_multi_plan_checks_and_layout(L):
+    import struct
+    from quantized_unpack_q4_amd import gq
+    assert gq.gq_gemv_q4k_multi_table_bytes(0) == 0
+    n = 3
+    nbytes = gq.gq_gemv_q4k_multi_table_bytes(n)
+    assert nbytes == 32 + 40 * n
+    D = (gq.GemvDesc * n)()
+    base = 0x100000
+    shapes = [(24, 4096), (1, 256), (100, 14336)]
+    for i, (M, K) in enumerate(shapes):
+        D[i] = gq.GemvDesc(base + 0x1000000 * i, base + 0x1000000 * i + 0x800000,
+                           base + 0x1000000 * i + 0xC00000, M, K)
+    table = (ctypes.c_uint8 * nbytes)()
+    assert L.gq_gemv_q4k_multi_plan(D, n, table, nbytes) == 0
+    raw = bytes(table)
+    magic, version, nn, total, tiles = struct.unpack_from("<IIqqq", raw, 0)
+    assert magic == 0x544D5147 and version == 1 and nn == n
+    sizes = [M * (K // 256) * 144 for M, K in shapes]
+    assert total == sum(sizes)
+    begin = 0
+    for i, (M, K) in enumerate(shapes):
+        w, x, y, m, k, bb = struct.unpack_from("<QQQiiq", raw, 32 + 40 * i)
+        assert (w, m, k, bb) == (D[i].w, M, K, begin)
+        begin += sizes[i]
+    # refusals name the descriptor
+    D[1].K = 300
+    st = L.gq_gemv_q4k_multi_plan(D, n, table, nbytes)
+    assert L.gq_status_str(st).decode() == "GQ_ESHAPE" and "descs[1].K" in L.gq_last_error().decode()
+    D[1].K = 32768
+    assert L.gq_status_str(L.gq_gemv_q4k_multi_plan(D, n, table, nbytes)).decode() == "GQ_ESHAPE"
+    D[1].K = 256
+    D[2].y = base + 8
+    st = L.gq_gemv_q4k_multi_plan(D, n, table, nbytes)
+    assert L.gq_status_str(st).decode() == "GQ_EALIGN" and "descs[2].y" in L.gq_last_error().decode()
+    D[2].y = base
+    assert L.gq_status_str(L.gq_gemv_q4k_multi_plan(D, n, table, nbytes - 1)).decode() == "GQ_EWORKSPACE"
+    assert L.gq_status_str(L.gq_gemv_q4k_multi_plan(None, n, table, nbytes)).decode() == "GQ_EINVAL"
+    # the launch refuses a table that was not planned, before touching the GPU
+    bad = (ctypes.c_uint8 * nbytes)()
+    assert L.gq_status_str(L.gq_gemv_q4k_multi(bad, FAKE, None)).decode() == "GQ_EINVAL"
+    assert L.gq_status_str(L.gq_gemv_q4k_multi(table, None, None)).decode() == "GQ_EINVAL"
+    assert L.gq_status_str(L.gq_gemv_q4k_multi(table, MISALIGNED, None)).decode() == "GQ_EALIGN"

@@ -1,0 +1,123 @@
+"""Parity of the one-launch batch-1 multi-product (and of the single-matrix
+batch-1 product, which runs the same streaming kernel) with the oracle.
+
+Bound: |y - y_ref| <= 1e-5 * S per output.  Activations are split into two
+binary16 halves after a power-of-two scaling, so inputs of very different
+magnitudes are part of the check.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_unpack_q4_amd import gq, synth
+from tests._gpu import dev, host, say, torch_cuda, within
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def _table(shapes, workload, xscale=None):
+    torch = torch_cuda()
+    items, host_in = [], []
+    for i, (M, K) in enumerate(shapes):
+        w = synth.q4k_blocks(workload, i, M, K)
+        x = synth.activations_f32(workload, i, 1, K)
+        if xscale is not None:
+            x = (x * np.float32(xscale[i])).astype(np.float32)
+        y = torch.full((1, M), float("nan"), dtype=torch.float32, device="cuda")
+        items.append((dev(w), dev(x), y, M, K))
+        host_in.append((w, x))
+    return gq.GemvTable(items), host_in
+
+
+def _check(table, host_in, shapes, rows_cap=None, what=""):
+    worst = 0.0
+    g = np.random.default_rng(5)
+    for (w, x), (_, _, y, M, K), (M2, K2) in zip(host_in, table.items, shapes):
+        yg = host(y)
+        rows = None
+        if rows_cap is not None and M > rows_cap:
+            rows = np.sort(g.choice(M, rows_cap, replace=False))
+            rows[0], rows[-1] = 0, M - 1
+        yr, S = oracle.gemv(oracle.Q4_K, w, x, M, K, rows=rows)
+        got = yg if rows is None else yg[:, rows]
+        worst = max(worst, within(got, yr, S, TOL, "%s %dx%d" % (what, M, K)))
+    return worst
+
+
+def test_multi_mixed_shapes():
+    """Ragged rows, every K from one super-block up to the maximum, tables whose
+    byte ranges split inside matrices and across them."""
+    shapes = [(1, 256), (37, 1024), (24, 4096), (25, 4096), (100, 768), (5, 16384),
+              (300, 2048), (49, 14336), (7, 256), (1024, 4096)]
+    t, h = _table(shapes, 20)
+    t.run()
+    r = _check(t, h, shapes, what="mixed")
+    say("multi mixed max err/S", r)
+
+
+def test_multi_activation_magnitudes():
+    """Per-matrix activation scales from 1e-30 to 1e30, and zero vectors."""
+    shapes = [(64, 1024)] * 6
+    scales = [1e-30, 1e-8, 1.0, 3e4, 1e12, 1e30]
+    t, h = _table(shapes, 21, xscale=scales)
+    t.run()
+    r = _check(t, h, shapes, what="scaled")
+    say("multi scaled max err/S", r)
+    z, hz = _table([(40, 512)], 22, xscale=[0.0])
+    z.run()
+    assert np.all(host(z.items[0][2]) == 0)
+
+
+def test_multi_one_hot_exact_and_deterministic():
+    torch = torch_cuda()
+    M, K = 77, 4096
+    w = synth.q4k_blocks(23, 0, M, K)
+    w32, _ = oracle.dequant(oracle.Q4_K, w, M, K)
+    wd = dev(w)
+    ks = [0, 31, 32, 63, 100, 255, 256, 1000, 2047, 4095]
+    items = []
+    for k in ks:
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        items.append((wd, dev(x), torch.empty((1, M), dtype=torch.float32, device="cuda"), M, K))
+    t = gq.GemvTable(items)
+    t.run()
+    for k, it in zip(ks, items):
+        assert np.array_equal(host(it[2])[0], w32[:, k]), k
+    first = [host(it[2]).copy() for it in items]
+    t.run()
+    for a, it in zip(first, items):
+        assert np.array_equal(a.view(np.uint32), host(it[2]).view(np.uint32))
+
+
+def test_multi_decode_layer_full_size():
+    """One Llama-3-8B-shaped layer (q, k, v, o, gate, up, down) at full size in
+    one launch, with the generator streams the benchmark uses; sampled rows."""
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096),
+              (14336, 4096), (4096, 14336)]
+    torch = torch_cuda()
+    items, host_in = [], []
+    for t, (M, K) in enumerate(shapes):
+        w = synth.q4k_blocks(2, t, M, K)
+        x = synth.activations_f32(2, 100 * t + 1, 1, K)
+        items.append((dev(w), dev(x), torch.empty((1, M), dtype=torch.float32, device="cuda"),
+                      M, K))
+        host_in.append((w, x))
+    tab = gq.GemvTable(items)
+    tab.run()
+    r = _check(tab, host_in, shapes, rows_cap=64, what="layer")
+    say("multi layer max err/S", r)
+
+
+def test_single_matrix_batch1_large_k_and_ragged():
+    """The single-matrix entry point at batch 1 (same streaming kernel)."""
+    torch = torch_cuda()
+    for M, K in ((1, 16384), (333, 256), (61, 14336)):
+        w = synth.q4k_blocks(24, M, M, K)
+        x = synth.activations_f32(24, M, 1, K)
+        y = torch.empty((1, M), dtype=torch.float32, device="cuda")
+        gq.gq_gemv_q4k(dev(w), dev(x), y, M, K, 1)
+        yr, S = oracle.gemv(oracle.Q4_K, w, x, M, K)
+        within(host(y), yr, S, TOL, "single %dx%d" % (M, K))
