@@ -261,6 +261,8 @@ gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, 
     GQ_TRY(check_ptr(fn, "w", w));
     GQ_TRY(check_ptr(fn, "x", x));
     GQ_TRY(check_ptr(fn, "y", y));
+    if (gq::gemm_big_applies(M, K, N))
+        return launched(fn, gq::launch_gemm_big(w, x, y, M, K, N, (hipStream_t)stream));
     return launched(fn, gq::launch_gemm_q4k(w, x, y, M, K, N, (hipStream_t)stream));
 }
 

@@ -24,6 +24,7 @@ constexpr int kQ80Weights = 32;
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float half_to_float(uint32_t bits16)
 {

@@ -37,6 +37,11 @@ hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inlin
 
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s);
+// Large-tile matrix product (prefill): 256 x 256 tiles; applies when there are
+// at least 256 of them and the operands fit 32-bit byte offsets.
+bool gemm_big_applies(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                           int64_t N, hipStream_t s);
 
 // Mixture-of-experts pieces; ws_off are the region offsets of gq_moe_workspace_offsets.
 struct MoeArgs {

@@ -57,6 +57,37 @@ def test_gemm_parity_prefill_sampled(M, K, N):
     say("  max err/S", r1, r2)
 
 
+@pytest.mark.parametrize("M,K,N", [(256, 256, 256), (600, 1024, 520), (512, 2048, 300),
+                                   (1000, 512, 1030)])
+def test_gemm_parity_large_tiles(M, K, N):
+    """Shapes with M >= 256 and N >= 256 (the 256 x 256 tile path) at sizes the
+    oracle computes in full: several tiles, ragged M and N, the smallest K."""
+    say("gemm large tiles", M, K, N)
+    w = synth.q4k_blocks(94, M, M, K)
+    x16 = synth.activations_f16(94, N, N, K)
+    y = _gemm(dev(w), x16, M, K)
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K)
+    r = within(y, yr, S, TOL, "gemm %dx%dx%d" % (M, K, N))
+    say("  max err/S", r)
+
+
+def test_gemm_one_hot_exact_large_tiles():
+    """One-hot activation rows read out the binary16 weights exactly on the
+    256 x 256 tile path, in every row of a ragged multi-tile output."""
+    M, K, N = 300, 1024, 270
+    w = synth.q4k_blocks(95, 0, M, K)
+    _, w16 = oracle.dequant(oracle.Q4_K, w, M, K)
+    ks = (np.arange(N) * 37 + 5) % K
+    x16 = np.zeros((N, K), np.float16)
+    x16[np.arange(N), ks] = 1.0
+    torch = torch_cuda()
+    y = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    gq.gq_gemm_q4k(dev(w), dev(x16), y, M, K, N)
+    yb = half_bits(y)
+    for i, k in enumerate(ks):
+        assert np.array_equal(yb[i].view(np.float16), w16[:, k].view(np.float16)), (i, k)
+
+
 def test_gemm_one_hot_exact():
     M, K = 256, 1024
     w = synth.q4k_blocks(92, 0, M, K)
@@ -74,8 +105,9 @@ def test_gemm_one_hot_exact():
         assert np.array_equal(a, b), k  # equal values (+0 and -0 compare equal)
 
 
-def test_gemm_deterministic():
-    M, K, N = 384, 2048, 200
+@pytest.mark.parametrize("N", [200, 300])
+def test_gemm_deterministic(N):
+    M, K = 384, 2048
     w = dev(synth.q4k_blocks(93, 0, M, K))
     x16 = synth.activations_f16(93, 0, N, K)
     a = _gemm(w, x16, M, K)
