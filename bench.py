@@ -109,6 +109,30 @@ def event_time(torch, stream, fn, reps=20, warmup=3):
     return ts[len(ts) // 2]
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_q4k_stream_decode_stack.md")
+TRAFFIC_SOURCES = ("quantized_unpack_q4_amd/csrc/gemv_stream.hip",
+                   "quantized_unpack_q4_amd/csrc/gq_device.h")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the streaming kernel on the decode stack, from the
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None when that
+    summary is missing or was taken on other kernel sources."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines()
+                  if l.startswith(("traffic_bytes_per_launch:", "source_sha256:")))
+    if fields.get("source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(synth, budget_s=12.0):
     """The binary64 oracle on whole matrices of the stack (layer 0 onwards, in
     order) until about budget_s seconds of oracle time are spent; one thread.
@@ -138,8 +162,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time the step only (skip the secondary measurements)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run a plain device-to-device copy of MIB MiB five times (the "
+                         "reference kernel for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
@@ -189,14 +217,26 @@ def main():
 
     extra = {"stack_b1_one_launch": {"ms_per_step": round(sec * 1e3, 4),
                                      "kernel_ms_events": round(avg_dur * 1e3, 4)}}
-    # the same 224 products as 224 launches, replayed as one HIP graph
-    g1, _ = stack_graph(torch, gq, synth, stack, 1, stream)
-    s224 = time_graph(torch, g1, max(3, args.steps // 2), 2)
-    extra["stack_b1_224_launch_graph"] = {"ms_per_step": round(s224 * 1e3, 4),
-                                          "weight_GB/s": round(stack.weight_bytes / s224 / 1e9, 1)}
-    del g1
+    if args.copy_probe > 0:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(5):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_probe_bytes"] = n
+        del src, dst
 
     if not args.no_extra:
+        # the same 224 products as 224 launches, replayed as one HIP graph
+        g1, _ = stack_graph(torch, gq, synth, stack, 1, stream)
+        s224 = time_graph(torch, g1, max(3, args.steps // 2), 2)
+        extra["stack_b1_224_launch_graph"] = {
+            "ms_per_step": round(s224 * 1e3, 4),
+            "weight_GB/s": round(stack.weight_bytes / s224 / 1e9, 1)}
+        del g1
+
         for B in (4, 16):
             log("stack batch", B)
             gB, _ = stack_graph(torch, gq, synth, stack, B, stream)
@@ -292,7 +332,7 @@ def main():
                    "global_batch": 1, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "kernel": "gemv_q4k_stream_kernel (224 products per launch)",
                      "avg_launch_us": round(avg_dur * 1e6, 3),
                      "alg_bytes_per_launch": int(alg_bytes)},
