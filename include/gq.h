@@ -80,7 +80,12 @@ gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64
 
 /* Q4_K matrix-vector product, binary32 activations; same contract as
  * gq_gemv_q8_0 with w holding M rows of K/256 super-blocks (M*K/256*144
- * bytes).  Requires K % 256 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH. */
+ * bytes).  Requires K % 256 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH.  Batch 1 runs
+ * binary32 arithmetic on the vector units (the activation split into two
+ * binary16 parts for the packed dot products); batches 2..16 run the
+ * 4-bit-quant x binary16-split-activation products on the matrix cores
+ * (see gq_gemv_q4k_multi_batched); both keep |y - y_exact| within 1e-5 of
+ * sum_k |w_k x_k|. */
 gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                       void *stream);
 
@@ -112,6 +117,16 @@ size_t gq_gemv_q4k_multi_table_bytes(int64_t n); /* 0 if n is outside [1, 2^20] 
 gq_status gq_gemv_q4k_multi_plan(const gq_gemv_desc *descs, int64_t n, void *table,
                                  size_t table_bytes);
 gq_status gq_gemv_q4k_multi(const void *table, const void *table_dev, void *stream);
+
+/* The same planned products at batch B (1 <= B <= 16): descriptor i's x is
+ * [B][K] and y is [B][M] (row-major), y_i[b] = W_i x_i[b].  B = 1 is
+ * gq_gemv_q4k_multi.  For B >= 2 the products run on the matrix cores (the
+ * 4-bit quants times a binary16 hi + lo split of each activation, scaled per
+ * activation row and super-block by a power of two; binary32 sums; error
+ * bound as for gq_gemv_q4k) and every matrix needs fewer than 2^32 bytes of
+ * weights and fewer than 2^31 bytes of activations (GQ_ESHAPE otherwise). */
+gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, int64_t B,
+                                    void *stream);
 
 /* Q4_K matrix product for prefill, binary16 activations and output:
  *   Y[n][r] = binary16( sum_k X[n][k] * w16[r][k] ),  accumulated in binary32,

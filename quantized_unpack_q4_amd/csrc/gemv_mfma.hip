@@ -1,0 +1,374 @@
+// gemv_mfma.hip -- small-batch Q4_K matrix-vector products on the matrix cores.
+//
+// y[b][r] = sum_k w[r][k] * x[b][k] for 2 <= B <= 16 activation rows, with
+// binary32 activations and results (page "Building a Rust Inference Engine
+// That Matches Llama.cpp", section "Where the wins came from": the dequant is
+// fused into the dot product; page "Frink", the paragraph on K-quant logits:
+// activations stay binary32, never requantized).  Each output is computed in
+// the factored form of a Q4_K super-block,
+//     sum over sub-blocks j of  (d*sc_j) * sum_k q_k x_k  -  (dmin*m_j) * sum_k x_k,
+// with both sums exact or binary32-accurate:
+//   * sum_k q_k x_k runs on v_mfma_f32_16x16x32_f16, one sub-block (32
+//     weights) per instruction: the 4-bit quant enters as the binary16
+//     subnormal q*2^-24 (exact; high nibbles as 16q*2^-24) and the activation
+//     as two binary16 halves hi + lo of x * 2^e, where 2^e (per activation row
+//     and super-block) brings the largest |x| of the slice to [2^14, 2^15); the
+//     products are exact and the sums binary32, so the activation keeps about
+//     22 significant bits;
+//   * (d*sc_j) * D_j is applied in binary32 per sub-block, 2^-e per super-block;
+//   * sum_j (dmin*m_j) * sum_k x_k is a 16 x 16 x 8 product per super-block on
+//     v_mfma_f32_16x16x4f32 from the binary32 sub-block sums of x.
+//
+// Work split.  A block is 128 consecutive rows of one matrix (4 waves x 2
+// tiles x 16 rows) over the whole K.  The 256 threads first stage the
+// activations of one super-block (B rows x 256) into LDS in the matrix-core
+// layout, then every wave multiplies its two 16-row tiles against them; the
+// staging of super-block s+1 and the packed weight loads of s+2 overlap the
+// work on s.  Blocks of all matrices of a table are dealt to the workgroups by
+// byte ranges of packed weights, as in the batch-1 streaming kernel.
+#include "gq_device.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int RB = 128; // rows per block
+constexpr int NT = 256; // threads per workgroup
+
+struct Smem {
+    // activations of one super-block, [buffer][sub-block j][quarter q][slot]:
+    // the 8 binary16 values of quarter q (k = 32j + 8q + {0,2,1,3,4,6,5,7}) of
+    // activation row b sit in slot b ^ swz(j, q)
+    uint4 xh[2][8][4][16];
+    uint4 xl[2][8][4][16];
+    float sx[2][8][16]; // [buffer][j][b] binary32 sum of x over sub-block j
+    float inv[2][16];   // [buffer][b] 2^-e
+};
+
+// Slot swizzle: the 16 staging threads of one activation row write 16
+// different (j, q) pairs at once; xor-ing the row index with a function of
+// (j, q) spreads those writes over the banks (the reads, 16 rows of one (j, q),
+// stay a permutation of 16 consecutive slots).
+__device__ __forceinline__ int swz(int j, int q) { return (2 * j + (q >> 1)) & 15; }
+
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel)
+{
+    int r;
+    const int iv = __builtin_bit_cast(int, v);
+    switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false); break;  // quad [1,0,3,2]
+    case 1: r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false); break;  // quad [2,3,0,1]
+    case 2: r = __builtin_amdgcn_update_dpp(0, iv, 0x124, 0xF, 0xF, false); break; // row_ror:4
+    default: r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false); break; // row_ror:8
+    }
+    return __builtin_bit_cast(float, r);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b)
+{
+    return __builtin_bit_cast(uint32_t, h2_t{a, b});
+}
+
+// hi and lo binary16 parts of xa*s and xb*s (s a power of two), packed
+__device__ __forceinline__ void split2(float xa, float xb, float s, uint32_t &hi, uint32_t &lo)
+{
+    const _Float16 ha = (_Float16)(xa * s), hb = (_Float16)(xb * s);
+    const _Float16 la = (_Float16)fmaf(xa, s, -(float)ha);
+    const _Float16 lb = (_Float16)fmaf(xb, s, -(float)hb);
+    hi = pack_h2(ha, hb);
+    lo = pack_h2(la, lb);
+}
+
+__device__ __forceinline__ const void *uniform_ptr(const void *p)
+{
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void *)(((uint64_t)hi << 32) | lo);
+}
+
+// Packed weights of one 16-row tile for one super-block, as this lane needs
+// them: the 16-byte header of its row and its 8 quant bytes of each 32-byte group.
+struct WTile {
+    uint4 h;
+    u32x2 q[4];
+};
+
+} // namespace
+
+__global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *__restrict__ table,
+                                                               GemvEntry inline0, int n,
+                                                               long long total, int B)
+{
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, quarter = lane >> 4; // matrix-core lane coordinates
+
+    // staging coordinates: activation row sb, 16 consecutive k from 16*sc_
+    const int sb = 4 * wave + (lane >> 4), sc_ = lane & 15;
+    const int sj = sc_ >> 1, sq0 = 2 * (sc_ & 1);
+
+    // this workgroup's byte range of the concatenated packed weights
+    const long long G = gridDim.x;
+    const long long lo_b = total * (long long)blockIdx.x / G;
+    const long long hi_b = total * ((long long)blockIdx.x + 1) / G;
+    // entries are the same for the whole wave: say so, so that the buffer
+    // resources built from them stay in scalar registers
+    auto entry = [&](int e) -> GemvEntry {
+        GemvEntry r = table ? table[e] : inline0;
+        r.w = (const uint8_t *)uniform_ptr(r.w);
+        r.x = (const float *)uniform_ptr(r.x);
+        r.y = (float *)uniform_ptr(r.y);
+        r.M = __builtin_amdgcn_readfirstlane(r.M);
+        r.K = __builtin_amdgcn_readfirstlane(r.K);
+        r.byte_begin = (long long)uniform_ptr((const void *)r.byte_begin);
+        return r;
+    };
+    // first entry whose bytes reach past lo_b
+    int e = 0;
+    if (table) {
+        int a = 0, z = n - 1;
+        while (a < z) { // last entry with byte_begin <= lo_b
+            const int mid = (a + z + 1) >> 1;
+            if (table[mid].byte_begin <= lo_b)
+                a = mid;
+            else
+                z = mid - 1;
+        }
+        e = a;
+    }
+    GemvEntry E = entry(e);
+    long long rowb = (long long)(E.K >> 8) * kQ4kBytes;
+    long long blkb = rowb * RB;
+    // first block of entry e starting at or after lo_b
+    int row0 = lo_b > E.byte_begin ? (int)((lo_b - E.byte_begin + blkb - 1) / blkb) * RB : 0;
+
+    for (;;) {
+        while (row0 >= E.M) {
+            if (++e >= n)
+                return;
+            E = entry(e);
+            rowb = (long long)(E.K >> 8) * kQ4kBytes;
+            blkb = rowb * RB;
+            row0 = 0;
+        }
+        if (E.byte_begin + (long long)row0 * rowb >= hi_b)
+            return;
+
+        // ---- one block: rows [row0, row0 + 128) of entry E, all of K ----
+        const int K = E.K, M = E.M, nsb = K >> 8;
+        // buffer loads: the matrix (and the activations) as a raw buffer
+        // resource in scalar registers, one 32-bit byte offset per lane, the
+        // super-block offset as the scalar offset (every matrix on this path
+        // has fewer than 2^32 bytes of weights and of activations; reads past
+        // the end return zeros)
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)E.w, (short)0, (int)(uint32_t)((long long)M * rowb), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)E.x, (short)0, (int)(uint32_t)((long long)B * K * 4), 0x00020000);
+        int rows[2];
+        uint32_t woff[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            rows[t] = row0 + 32 * wave + 16 * t + col;
+            woff[t] = (uint32_t)min(rows[t], M - 1) * (uint32_t)rowb;
+        }
+        auto load_w = [&](int s, WTile(&wt)[2]) {
+            const int so = s * kQ4kBytes;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff[t], so, 0);
+                wt[t].h = make_uint4(h.x, h.y, h.z, h.w);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    wt[t].q[g] = __builtin_amdgcn_raw_buffer_load_b64(
+                        rw, (int)(woff[t] + 8 * quarter) + 16 + 32 * g, so, 0);
+            }
+        };
+        const bool stager = sb < B;
+        const int xoff = (sb * K + 16 * sc_) * 4;
+        float4_t xr[4];
+        auto load_x = [&](int s) {
+            if (stager) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xr[i] = __builtin_bit_cast(
+                        float4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 16 * i, s * 1024, 0));
+            }
+        };
+        // binary16 hi/lo parts, sub-block sums and scale of the staged slice
+        auto store_x = [&](int buf) {
+            if (!stager)
+                return;
+            float m = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(xr[i].x), fabsf(xr[i].y)),
+                                   fmaxf(fabsf(xr[i].z), fabsf(xr[i].w))));
+            m = fmaxf(m, dpp_f(m, 0));
+            m = fmaxf(m, dpp_f(m, 1));
+            m = fmaxf(m, dpp_f(m, 2));
+            m = fmaxf(m, dpp_f(m, 3)); // max over the 16 lanes of this row
+            // 2^e with the largest |x| in [2^14, 2^15): exponent field 268 - ex,
+            // kept in [1, 253] (zero or tiny slices get 2^126)
+            const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 255u);
+            const int fe = min(max(268 - ex, 1), 253);
+            const float s = __builtin_bit_cast(float, (uint32_t)fe << 23);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sum += (xr[i].x + xr[i].y) + (xr[i].z + xr[i].w);
+            sum += dpp_f(sum, 0); // the partner lane holds the other half of sub-block sj
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // quarter sq0 + h: elements k = 8h .. 8h+7 of this lane's 16
+                const float4_t a = xr[2 * h], c = xr[2 * h + 1];
+                uint4 hv, lv;
+                split2(a.x, a.z, s, hv.x, lv.x); // k0, k2
+                split2(a.y, a.w, s, hv.y, lv.y); // k1, k3
+                split2(c.x, c.z, s, hv.z, lv.z); // k4, k6
+                split2(c.y, c.w, s, hv.w, lv.w); // k5, k7
+                const int q = sq0 + h;
+                sm.xh[buf][sj][q][sb ^ swz(sj, q)] = hv;
+                sm.xl[buf][sj][q][sb ^ swz(sj, q)] = lv;
+            }
+            if ((sc_ & 1) == 0)
+                sm.sx[buf][sj][sb] = sum;
+            if (sc_ == 0)
+                sm.inv[buf][sb] = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
+        };
+
+        float4_t acc[2], macc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+            macc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+        // one super-block from LDS buffer buf and packed weights wt
+        auto compute = [&](int buf, const WTile(&wt)[2]) {
+            float4_t ch[2];
+            float mb[2][2]; // dmin*m_j for j = quarter and 4 + quarter, per tile
+            float sl[2][8]; // d*sc_j * 2^24 (even j) or 2^20 (odd j), per tile
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                ch[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+                const uint4 h = wt[t].h;
+                const float d = half_to_float(h.x), dmin = half_to_float(h.x >> 16);
+                const float d24 = d * 16777216.f, d20 = d * 1048576.f;
+                const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
+                const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+                const uint32_t m03 = h.z & 0x3F3F3F3Fu;
+                const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+                sl[t][0] = ubyte_to_float<0>(sc03) * d24;
+                sl[t][1] = ubyte_to_float<1>(sc03) * d20;
+                sl[t][2] = ubyte_to_float<2>(sc03) * d24;
+                sl[t][3] = ubyte_to_float<3>(sc03) * d20;
+                sl[t][4] = ubyte_to_float<0>(sc47) * d24;
+                sl[t][5] = ubyte_to_float<1>(sc47) * d20;
+                sl[t][6] = ubyte_to_float<2>(sc47) * d24;
+                sl[t][7] = ubyte_to_float<3>(sc47) * d20;
+                mb[t][0] = dmin * (float)__builtin_amdgcn_ubfe(m03, 8 * quarter, 8);
+                mb[t][1] = dmin * (float)__builtin_amdgcn_ubfe(m47, 8 * quarter, 8);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int j = 2 * g + hh;
+                    const uint4 xh = sm.xh[buf][j][quarter][col ^ swz(j, quarter)];
+                    const uint4 xl = sm.xl[buf][j][quarter][col ^ swz(j, quarter)];
+                    const half8_t ah = __builtin_bit_cast(half8_t, xh);
+                    const half8_t al = __builtin_bit_cast(half8_t, xl);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const uint32_t D0 = wt[t].q[g].x, D1 = wt[t].q[g].y;
+                        const uint32_t mk = hh ? 0x00F000F0u : 0x000F000Fu;
+                        // (k0,k2), (k1,k3), (k4,k6), (k5,k7) of this lane's 8
+                        const uint4 qv = make_uint4(D0 & mk, (D0 >> 8) & mk, D1 & mk, (D1 >> 8) & mk);
+                        const half8_t bq = __builtin_bit_cast(half8_t, qv);
+                        float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, D, 0, 0, 0);
+                        ch[t] = sl[t][j] * D + ch[t];
+                    }
+                }
+                // bound the live ranges: one group's operands at a time
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const float4_t iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][4 * quarter]);
+            const float sx0 = sm.sx[buf][quarter][col], sx1 = sm.sx[buf][4 + quarter][col];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                acc[t] = iv * ch[t] + acc[t];
+                macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx0, mb[t][0], macc[t], 0, 0, 0);
+                macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx1, mb[t][1], macc[t], 0, 0, 0);
+            }
+        };
+
+        WTile wa[2], wb[2];
+        load_x(0);
+        load_w(0, wa);
+        load_w(min(1, nsb - 1), wb);
+        store_x(0);
+        __syncthreads();
+        // two super-blocks per iteration so that the register sets stay fixed;
+        // prefetches past the end reload the last super-block (unused)
+        for (int s = 0; s < nsb; s += 2) {
+            load_x(min(s + 1, nsb - 1));
+            compute(0, wa);
+            load_w(min(s + 2, nsb - 1), wa);
+            store_x(1);
+            __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's LDS writes
+            __builtin_amdgcn_s_barrier();
+            if (s + 1 >= nsb)
+                break;
+            load_x(min(s + 2, nsb - 1));
+            compute(1, wb);
+            load_w(min(s + 3, nsb - 1), wb);
+            store_x(0);
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+        }
+
+        // y[b][row] for b = 4*quarter + i
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (rows[t] < M) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int b = 4 * quarter + i;
+                    if (b < B)
+                        E.y[(size_t)b * M + rows[t]] = acc[t][i] - macc[t][i];
+                }
+            }
+        }
+        row0 += RB;
+    }
+}
+
+long long gemv_mfma_blocks(int64_t M) { return (M + RB - 1) / RB; }
+
+hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
+                            long long total_bytes, long long blocks, int B, hipStream_t s)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return hipErrorInvalidDevice;
+        cus = prop.multiProcessorCount;
+    }
+    const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
+    hipLaunchKernelGGL(gemv_q4k_mfma_kernel, dim3((unsigned)grid), dim3(NT), 0, s, table_dev,
+                       inline0, n, total_bytes, B);
+    return hipGetLastError();
+}
+
+} // namespace gq

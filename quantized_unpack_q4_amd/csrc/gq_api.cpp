@@ -144,6 +144,13 @@ gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64
     return launched(fn, gq::launch_gemv_q8_0(w, x, y, M, K, (int)B, (hipStream_t)stream));
 }
 
+// The matrix-core small-batch kernel addresses a matrix and its activations
+// with 32-bit byte offsets.
+static bool gemv_mfma_fits(int64_t M, int64_t K, int64_t B)
+{
+    return M * (K / 256) * 144 < ((int64_t)1 << 32) && B * K * 4 < ((int64_t)1 << 31);
+}
+
 gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                       void *stream)
 {
@@ -156,6 +163,12 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
         const long long total = (long long)M * (K / 256) * 144;
         const int grid = gq::gemv_stream_grid(total, gq::gemv_stream_tiles(M, K));
         return launched(fn, gq::launch_gemv_stream(nullptr, e, 1, total, grid, (hipStream_t)stream));
+    }
+    if (B >= 2 && gemv_mfma_fits(M, K, B)) {
+        gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0};
+        const long long total = (long long)M * (K / 256) * 144;
+        return launched(fn, gq::launch_gemv_mfma(nullptr, e, 1, total, gq::gemv_mfma_blocks(M),
+                                                 (int)B, (hipStream_t)stream));
     }
     return launched(fn, gq::launch_gemv_q4k(w, x, y, M, K, (int)B, (hipStream_t)stream));
 }
@@ -244,6 +257,43 @@ gq_status gq_gemv_q4k_multi(const void *table, const void *table_dev, void *stre
     const int grid = gq::gemv_stream_grid(h.total_bytes, h.total_tiles);
     return launched(fn, gq::launch_gemv_stream(dev, none, (int)h.n, h.total_bytes, grid,
                                                (hipStream_t)stream));
+}
+
+gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, int64_t B,
+                                    void *stream)
+{
+    static const char fn[] = "gq_gemv_q4k_multi_batched";
+    if (!table)
+        return fail(GQ_EINVAL, "%s: table is NULL", fn);
+    TableHeader h;
+    memcpy(&h, table, sizeof h);
+    if (h.magic != kTableMagic || h.version != kTableVersion || h.n < 1)
+        return fail(GQ_EINVAL, "%s: table was not written by gq_gemv_q4k_multi_plan", fn);
+    if (B < 1 || B > GQ_GEMV_MAX_BATCH)
+        return fail(GQ_EINVAL, "%s: B = %lld is outside [1, %d]", fn, (long long)B,
+                    GQ_GEMV_MAX_BATCH);
+    GQ_TRY(check_ptr(fn, "table_dev", table_dev));
+    const gq::GemvEntry *dev = reinterpret_cast<const gq::GemvEntry *>(
+        (const uint8_t *)table_dev + sizeof(TableHeader));
+    const gq::GemvEntry none{};
+    if (B == 1) {
+        const int grid = gq::gemv_stream_grid(h.total_bytes, h.total_tiles);
+        return launched(fn, gq::launch_gemv_stream(dev, none, (int)h.n, h.total_bytes, grid,
+                                                   (hipStream_t)stream));
+    }
+    const gq::GemvEntry *ent =
+        reinterpret_cast<const gq::GemvEntry *>((const uint8_t *)table + sizeof h);
+    long long blocks = 0;
+    for (int64_t i = 0; i < h.n; ++i) {
+        gq::GemvEntry e;
+        memcpy(&e, &ent[i], sizeof e);
+        if (!gemv_mfma_fits(e.M, e.K, B))
+            return fail(GQ_ESHAPE, "%s: entry %lld (M = %d, K = %d) is too large for batch %lld",
+                        fn, (long long)i, e.M, e.K, (long long)B);
+        blocks += gq::gemv_mfma_blocks(e.M);
+    }
+    return launched(fn, gq::launch_gemv_mfma(dev, none, (int)h.n, h.total_bytes, blocks, (int)B,
+                                             (hipStream_t)stream));
 }
 
 gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,

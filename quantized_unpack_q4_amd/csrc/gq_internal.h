@@ -35,6 +35,13 @@ int gemv_stream_grid(long long total_bytes, long long tiles);
 hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
                               long long total_bytes, int grid, hipStream_t s);
 
+// Small-batch (2 <= B <= 16) products on the matrix cores, over a table of
+// entries (or the single entry inline0 when table_dev is null); blocks of 128
+// rows are dealt to workgroups by byte ranges of the packed weights.
+long long gemv_mfma_blocks(int64_t M);
+hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
+                            long long total_bytes, long long blocks, int B, hipStream_t s);
+
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s);
 // Large-tile matrix product (prefill): 256 x 256 tiles; applies when there are

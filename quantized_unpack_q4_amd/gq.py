@@ -24,7 +24,7 @@ MAX_BATCH = 16
 
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
-    "gq_gemv_q4k_multi", "gq_gemm_q4k", "gq_moe_gemm_q4k",
+    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemm_q4k", "gq_moe_gemm_q4k",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
 )
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.gq_gemv_q4k_multi_plan.argtypes = [vp, i64, vp, sz]
         L.gq_gemv_q4k_multi.restype = st
         L.gq_gemv_q4k_multi.argtypes = [vp, vp, vp]
+        L.gq_gemv_q4k_multi_batched.restype = st
+        L.gq_gemv_q4k_multi_batched.argtypes = [vp, vp, i64, vp]
         L.gq_gemm_q4k.restype = st
         L.gq_gemm_q4k.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.gq_moe_gemm_q4k.restype = st
@@ -138,14 +140,19 @@ def gq_gemv_q4k_multi(table, table_dev, stream=None):
     _check(lib().gq_gemv_q4k_multi(table, _ptr(table_dev), _stream(stream)))
 
 
-class GemvTable:
-    """A planned batch-1 multi-product: host table + its device copy.
+def gq_gemv_q4k_multi_batched(table, table_dev, B, stream=None):
+    _check(lib().gq_gemv_q4k_multi_batched(table, _ptr(table_dev), B, _stream(stream)))
 
-    ``items`` is a list of (w, x, y, M, K) with torch device tensors; the
-    tensors must stay alive while the table is used.
+
+class GemvTable:
+    """A planned multi-product: host table + its device copy.
+
+    ``items`` is a list of (w, x, y, M, K) with torch device tensors, x of
+    shape [batch][K] and y [batch][M]; the tensors must stay alive while the
+    table is used.
     """
 
-    def __init__(self, items):
+    def __init__(self, items, batch=1):
         import torch
         n = len(items)
         arr = (GemvDesc * n)()
@@ -163,9 +170,13 @@ class GemvTable:
         self.dev = host_t.to(items[0][0].device)
         self.items = items
         self.n = n
+        self.batch = batch
 
     def run(self, stream=None):
-        gq_gemv_q4k_multi(self.host, self.dev, stream)
+        if self.batch == 1:
+            gq_gemv_q4k_multi(self.host, self.dev, stream)
+        else:
+            gq_gemv_q4k_multi_batched(self.host, self.dev, self.batch, stream)
 
 
 def gq_gemm_q4k(w, x, y, M, K, N, stream=None):

@@ -158,3 +158,12 @@ def test_multi_plan_checks_and_layout(L):
     assert L.gq_status_str(L.gq_gemv_q4k_multi(bad, FAKE, None)).decode() == "GQ_EINVAL"
     assert L.gq_status_str(L.gq_gemv_q4k_multi(table, None, None)).decode() == "GQ_EINVAL"
     assert L.gq_status_str(L.gq_gemv_q4k_multi(table, MISALIGNED, None)).decode() == "GQ_EALIGN"
+    # the batched launch: batch range, table and device copy checked on the host
+    f = L.gq_gemv_q4k_multi_batched
+    for B in (0, 17, -1):
+        st = f(table, FAKE, B, None)
+        assert L.gq_status_str(st).decode() == "GQ_EINVAL" and "B = " in L.gq_last_error().decode()
+    assert L.gq_status_str(f(bad, FAKE, 4, None)).decode() == "GQ_EINVAL"
+    assert L.gq_status_str(f(None, FAKE, 4, None)).decode() == "GQ_EINVAL"
+    assert L.gq_status_str(f(table, None, 4, None)).decode() == "GQ_EINVAL"
+    assert L.gq_status_str(f(table, MISALIGNED, 4, None)).decode() == "GQ_EALIGN"

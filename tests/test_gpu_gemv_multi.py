@@ -121,3 +121,90 @@ def test_single_matrix_batch1_large_k_and_ragged():
         gq.gq_gemv_q4k(dev(w), dev(x), y, M, K, 1)
         yr, S = oracle.gemv(oracle.Q4_K, w, x, M, K)
         within(host(y), yr, S, TOL, "single %dx%d" % (M, K))
+
+
+# -- batches 2..16 (matrix cores) ---------------------------------------------------
+
+def _table_b(shapes, workload, B, xrow_scale=None):
+    torch = torch_cuda()
+    items, host_in = [], []
+    for i, (M, K) in enumerate(shapes):
+        w = synth.q4k_blocks(workload, i, M, K)
+        x = synth.activations_f32(workload, 1000 + i, B, K)
+        if xrow_scale is not None:
+            x = (x * np.asarray(xrow_scale[i], np.float32)[:, None]).astype(np.float32)
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
+        items.append((dev(w), dev(x), y, M, K))
+        host_in.append((w, x))
+    return gq.GemvTable(items, batch=B), host_in
+
+
+@pytest.mark.parametrize("B", [2, 5, 16])
+def test_multi_batched_mixed_shapes(B):
+    """Ragged row counts (partial 16-row tiles and 128-row blocks), K from one
+    super-block to the maximum, block ranges that split across matrices."""
+    shapes = [(1, 256), (37, 1024), (130, 4096), (100, 768), (5, 16384), (300, 2048),
+              (49, 14336), (7, 256), (1024, 4096)]
+    t, h = _table_b(shapes, 30, B)
+    t.run()
+    say("multi batched B", B)
+    r = _check(t, h, shapes, what="batched B=%d" % B)
+    say("  max err/S", r)
+
+
+def test_multi_batched_activation_magnitudes():
+    """Activation rows of one batch at very different magnitudes (each row and
+    super-block gets its own power-of-two scale), and an all-zero row."""
+    shapes = [(64, 1024), (40, 2048)]
+    scales = [[1e-30, 1e-8, 1.0, 3e4, 1e12, 1e30], [0.0, 1.0, 1e-20, 1e20, 7.0, 0.5]]
+    t, h = _table_b(shapes, 31, 6, xrow_scale=scales)
+    t.run()
+    r = _check(t, h, shapes, what="batched scaled")
+    assert np.all(host(t.items[1][2])[0] == 0)
+    say("multi batched scaled max err/S", r)
+
+
+def test_multi_batched_one_hot_exact_and_deterministic():
+    """One-hot activation rows read out the binary32 weights exactly."""
+    torch = torch_cuda()
+    M, K, B = 150, 2048, 16
+    w = synth.q4k_blocks(32, 0, M, K)
+    w32, _ = oracle.dequant(oracle.Q4_K, w, M, K)
+    wd = dev(w)
+    items, kss = [], []
+    for rep in range(3):
+        ks = [(37 * b + 101 * rep + 5) % K for b in range(B)]
+        x = np.zeros((B, K), np.float32)
+        x[np.arange(B), ks] = 1.0
+        items.append((wd, dev(x), torch.empty((B, M), dtype=torch.float32, device="cuda"), M, K))
+        kss.append(ks)
+    t = gq.GemvTable(items, batch=B)
+    t.run()
+    for ks, it in zip(kss, items):
+        y = host(it[2])
+        for b, k in enumerate(ks):
+            assert np.array_equal(y[b], w32[:, k]), (b, k)
+    first = [host(it[2]).copy() for it in items]
+    t.run()
+    for a, it in zip(first, items):
+        assert np.array_equal(a.view(np.uint32), host(it[2]).view(np.uint32))
+
+
+@pytest.mark.parametrize("B", [4, 16])
+def test_multi_batched_decode_layer_full_size(B):
+    """One Llama-3-8B-shaped layer at full size in one launch, batch 4 and 16,
+    with the generator streams the benchmark uses; sampled rows."""
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096),
+              (14336, 4096), (4096, 14336)]
+    torch = torch_cuda()
+    items, host_in = [], []
+    for t, (M, K) in enumerate(shapes):
+        w = synth.q4k_blocks(2, t, M, K)
+        x = synth.activations_f32(2, 100 * t + B, B, K)
+        items.append((dev(w), dev(x), torch.empty((B, M), dtype=torch.float32, device="cuda"),
+                      M, K))
+        host_in.append((w, x))
+    tab = gq.GemvTable(items, batch=B)
+    tab.run()
+    r = _check(tab, host_in, shapes, rows_cap=48, what="layer B=%d" % B)
+    say("multi batched layer B=%d max err/S" % B, r)
