@@ -162,7 +162,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU needs ~0.1 s of sustained load to reach steady clocks: 200
+    # untimed steps of the decode stack are about 0.16 s
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extra", action="store_true",
                     help="time the step only (skip the secondary measurements)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

@@ -146,11 +146,23 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
     __shared__ float s_amax[4];
     float inv_scale = 1.f;
     auto stage = [&]() {
-        const int nrec = e.K >> 2;
+        // thread t owns sub-blocks t and t + 256 (32 activations each, at most
+        // 512 sub-blocks): every activation is loaded once, all loads in flight
+        // together, and kept in registers for the scale, split and sums
+        const int nsub = e.K >> 5;
+        float4 v[2][8];
         float amax = 0.f;
-        for (int i = tid; i < nrec; i += 256) {
-            const float4 v = gloadf4(e.x + 4 * i);
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = tid + 256 * u;
+            if (j < nsub) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    v[u][i] = gloadf4(e.x + 32 * j + 4 * i);
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][i].x), fabsf(v[u][i].y)),
+                                             fmaxf(fabsf(v[u][i].z), fabsf(v[u][i].w))));
+                }
+            }
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
@@ -167,27 +179,30 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
         // record i holds x[4i..4i+3]*scale as (hi(x0,x2), hi(x1,x3), lo(x0,x2),
         // lo(x1,x3)); 16 bytes of padding after every 16 records.  ssum[j] is
         // the plain binary32 sum of x over sub-block j.
-        for (int i = tid; i < nrec; i += 256) {
-            float4 v = gloadf4(e.x + 4 * i);
-            v.x *= scale;
-            v.y *= scale;
-            v.z *= scale;
-            v.w *= scale;
-            const h2_t h02 = {(_Float16)v.x, (_Float16)v.z}, h13 = {(_Float16)v.y, (_Float16)v.w};
-            const h2_t l02 = {(_Float16)(v.x - (float)h02.x), (_Float16)(v.z - (float)h02.y)};
-            const h2_t l13 = {(_Float16)(v.y - (float)h13.x), (_Float16)(v.w - (float)h13.y)};
-            *reinterpret_cast<uint4 *>(xrec + 4 * (i + (i >> 4))) =
-                make_uint4(__builtin_bit_cast(uint32_t, h02), __builtin_bit_cast(uint32_t, h13),
-                           __builtin_bit_cast(uint32_t, l02), __builtin_bit_cast(uint32_t, l13));
-        }
-        for (int j = tid; j < (e.K >> 5); j += 256) {
-            float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < 32; i += 4) {
-                const float4 v = gloadf4(e.x + 32 * j + i);
-                s += (v.x + v.y) + (v.z + v.w);
+        for (int u = 0; u < 2; ++u) {
+            const int j = tid + 256 * u;
+            if (j < nsub) {
+                float sum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float4 w = v[u][i];
+                    sum += (w.x + w.y) + (w.z + w.w);
+                    w.x *= scale;
+                    w.y *= scale;
+                    w.z *= scale;
+                    w.w *= scale;
+                    const h2_t h02 = {(_Float16)w.x, (_Float16)w.z};
+                    const h2_t h13 = {(_Float16)w.y, (_Float16)w.w};
+                    const h2_t l02 = {(_Float16)(w.x - (float)h02.x), (_Float16)(w.z - (float)h02.y)};
+                    const h2_t l13 = {(_Float16)(w.y - (float)h13.x), (_Float16)(w.w - (float)h13.y)};
+                    const int ri = 8 * j + i;
+                    *reinterpret_cast<uint4 *>(xrec + 4 * (ri + (ri >> 4))) = make_uint4(
+                        __builtin_bit_cast(uint32_t, h02), __builtin_bit_cast(uint32_t, h13),
+                        __builtin_bit_cast(uint32_t, l02), __builtin_bit_cast(uint32_t, l13));
+                }
+                ssum[j] = sum;
             }
-            ssum[j] = s;
         }
     };
 
