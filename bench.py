@@ -290,6 +290,23 @@ def main():
                 del x16, y16
             del w
         extra["prefill_gemm"] = pre
+        # achievable ceilings measured beside the kernels: a plain 1 GiB device
+        # copy (read + write streaming) and the vendor library's binary16 product
+        # on unquantized operands of the prefill shapes (torch -> hipBLASLt)
+        ceil = {}
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        s = event_time(torch, stream, lambda: dst.copy_(src), reps=10)
+        ceil["d2d_copy_1GiB_read+write_GB/s"] = round(2 * (1 << 30) / s / 1e9, 1)
+        del src, dst
+        for M, K in ((14336, 4096), (4096, 14336)):
+            a16 = torch.randn(4096, K, device="cuda").half()
+            b16 = torch.randn(M, K, device="cuda").half()
+            s = event_time(torch, stream, lambda: torch.matmul(a16, b16.t()), reps=10)
+            ceil["fp16_library_matmul_%dx%dxN4096_TFLOP/s" % (M, K)] = round(
+                2.0 * M * K * 4096 / s / 1e12, 1)
+            del a16, b16
+        extra["measured_ceilings"] = ceil
         # mixture of experts, OLMoE-1B-7B shape
         import oracle  # routing only: the oracle's binary64 softmax/top-k on the host
         H, I, E, k = 2048, 1024, 64, 8
