@@ -20,7 +20,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgq.so")
 ARCH = os.environ.get("GQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["dequant.hip", "gemv.hip", "gemv_stream.hip", "gemv_mfma.hip", "gemm.hip", "gemm_big.hip", "moe.hip", "gq_api.cpp"]
+SOURCES = ["dequant.hip", "gemv.hip", "gemv_stream.hip", "gemv_mfma.hip", "gemm.hip", "gemm_big.hip", "moe.hip", "moe_skinny.hip", "gq_api.cpp"]
 
 FLAGS = [
     "--offload-arch=" + ARCH,

@@ -39,7 +39,6 @@ struct GemmParams {
     int64_t expert_bytes;  // bytes of one expert's weight matrix
 };
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)

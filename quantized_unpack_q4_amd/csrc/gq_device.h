@@ -64,6 +64,10 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t h1, uint32_t h2, uint32_t
     }
 }
 
+// SwiGLU gate activation silu(z) = z / (1 + e^-z) in binary32 (the mixture-of-
+// experts gate/up epilogues; the oracle evaluates it in binary64).
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll

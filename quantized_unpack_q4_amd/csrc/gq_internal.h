@@ -65,5 +65,8 @@ hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 
 // Token-tile size used by the grouped products for a given mean tokens per expert.
 int moe_token_tile(int64_t assignments, int64_t experts);
+// Expert products streamed once per chunk of 64 tokens (few tokens per expert).
+bool moe_skinny_applies(int64_t assignments, int64_t experts);
+hipError_t launch_moe_skinny(const MoeArgs &a, hipStream_t s);
 
 } // namespace gq

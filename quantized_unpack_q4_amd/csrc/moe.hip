@@ -9,8 +9,9 @@
 //               lists the token tiles of every expert and gives each
 //               (token, slot) assignment a stable position in expert order
 //               (ties keep assignment order, so the result is deterministic);
-//   2. gate/up  grouped matrix product with the SwiGLU epilogue (gemm.hip);
-//   3. down     grouped matrix product into binary32 rows (gemm.hip);
+//   2. gate/up  grouped matrix product with the SwiGLU epilogue (gemm.hip, or
+//               moe_skinny.hip when the experts average 48 tokens or fewer);
+//   3. down     grouped matrix product into binary32 rows (likewise);
 //   4. combine  out[t] = sum over slots, in slot order, of weight * row.
 // No atomics touch the outputs and nothing waits on the host.
 #include "gq_device.h"
@@ -157,7 +158,8 @@ hipError_t launch_moe(const MoeArgs &a, hipStream_t s)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    err = launch_moe_gemms(a, bn, max_tiles, s);
+    err = moe_skinny_applies(A, a.E) ? launch_moe_skinny(a, s)
+                                     : launch_moe_gemms(a, bn, max_tiles, s);
     if (err != hipSuccess)
         return err;
     const int col_blocks = (int)((a.H / 4 + 255) / 256);

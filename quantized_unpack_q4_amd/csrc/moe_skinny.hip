@@ -1,0 +1,309 @@
+// moe_skinny.hip -- the grouped expert products of the mixture-of-experts layer
+// when each expert sees few tokens.
+//
+// With 256 tokens, top-8 routing and 64 experts (the OLMoE-shaped layer the
+// pages run, page "Building a Rust Inference Engine That Matches Llama.cpp",
+// section "Utility"), an expert gets about 32 tokens: the expert products are
+// skinny and the layer is bound by streaming the 226 MB of packed expert
+// weights, not by the matrix cores.  This kernel streams each weight once per
+// chunk of up to 64 tokens of its expert:
+//   * a workgroup (4 waves) owns 64 rows of one expert's matrix (64 rows of
+//     gate and the same 64 rows of up in the gate/up product), all of K;
+//   * per super-block, the token slices it needs (up to 64 rows x 256 binary16
+//     activations, gathered through the expert's sorted assignment list) are
+//     copied global -> LDS by direct-to-LDS loads, one super-block ahead, into
+//     a bank-swizzled layout;
+//   * each lane dequantizes its own weights straight into the operand of
+//     v_mfma_f32_16x16x32_f16, w16 = binary16(binary32(d*sc*q - dmin*m)) by one
+//     mixed-precision FMA per weight from the quant taken as the binary16
+//     subnormal q*2^-24 (the same binary16 weights as the tiled products), no
+//     LDS round trip;
+//   * binary32 accumulation over all of K, then the SwiGLU epilogue
+//     h = binary16(silu(g) * u) (gate/up) or binary32 rows (down), written in
+//     the expert-sorted order the combine step reads.
+#include "gq_device.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+
+constexpr int SR = 64;  // weight rows per workgroup
+constexpr int ST = 64;  // tokens per chunk (up to 4 groups of 16)
+constexpr int NT = 256; // threads per workgroup
+
+struct SkinnyParams {
+    const uint8_t *w, *w2;  // stacked Q4_K expert matrices (w2: up, gate/up product only)
+    const uint16_t *x;      // gate/up: x [T][K]; down: h [A][K] in sorted order
+    void *y;                // gate/up: h [A][M] binary16; down: d [A][M] binary32
+    const int32_t *offsets; // expert start positions in sorted order, [E] = total
+    const int32_t *sorted;  // assignment t*topk + s at each sorted position
+    int M, K, topk;
+    int64_t expert_bytes;
+};
+
+// 16 bytes per lane, global -> LDS; lane l lands at lds_base + 16*l (lds_base
+// wave-uniform).  Inline assembly keeps it out of the compiler's wait
+// insertion: the kernel retires it with an explicit vmcnt(0) before the
+// barrier that publishes the data.
+__device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0)
+                 : "memory", "m0");
+}
+
+// Two binary16 weights from two quants taken as binary16 subnormals and the
+// binary32 scale s and offset o: binary16(binary32(s*q + o)) each, packed.
+__device__ __forceinline__ uint32_t deq2(uint32_t qa, int sela, uint32_t qb, int selb, float s,
+                                         float o)
+{
+    const h2_t a = __builtin_bit_cast(h2_t, qa), b = __builtin_bit_cast(h2_t, qb);
+    const _Float16 lo = (_Float16)fmaf((float)(sela ? a.y : a.x), s, o);
+    const _Float16 hi = (_Float16)fmaf((float)(selb ? b.y : b.x), s, o);
+    return __builtin_bit_cast(uint32_t, h2_t{lo, hi});
+}
+
+// This lane's packed weights of one super-block: the header of its row and its
+// 8 quant bytes (k = 8q .. 8q+7 of each 32-byte group).
+struct WSb {
+    uint4 h;
+    u32x2 q[4];
+};
+
+__device__ __forceinline__ void load_wsb(const uint8_t *row, int sb, int quarter, WSb &w)
+{
+    const uint8_t *blk = row + (size_t)sb * kQ4kBytes;
+    const u32x4 h = *(g_u32x4 *)blk;
+    w.h = make_uint4(h.x, h.y, h.z, h.w);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        w.q[g] = *(g_u32x2 *)(blk + 16 + 32 * g + 8 * quarter);
+}
+
+// One chunk of up to 16*NG tokens of expert e: positions [p0, p0 + nc) of the
+// sorted list.
+template <int MODE, int NG>
+__device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, int nc,
+                                          _Float16 *xs0, _Float16 *xs1)
+{
+    constexpr int NMAT = MODE == 0 ? 2 : 1;
+    constexpr int NDMA = NG * 2; // direct-to-LDS copies per wave per super-block
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, quarter = lane >> 4;
+    const int K = p.K, M = p.M, nsb = K >> 8;
+    const size_t rowb = (size_t)(K >> 8) * kQ4kBytes;
+    const int row = (int)blockIdx.x * SR + wave * 16 + col;
+
+    const uint8_t *wrow[NMAT];
+    wrow[0] = p.w + (size_t)e * p.expert_bytes + (size_t)row * rowb;
+    if constexpr (NMAT == 2)
+        wrow[1] = p.w2 + (size_t)e * p.expert_bytes + (size_t)row * rowb;
+
+    // copy i of this wave fills LDS bytes [1 KB * (NDMA*wave + i), +1 KB):
+    // tokens t = 2*(NDMA*wave + i) + lane/32, slot lane%32, holding 16-byte
+    // chunk (lane%32) ^ (t%32) of the token's 512-byte super-block slice
+    const uint16_t *src[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int t = 2 * (NDMA * wave + i) + (lane >> 5);
+        const int tc = t < nc ? t : nc - 1;
+        const int64_t xrow =
+            MODE == 0 ? (int64_t)(p.sorted[p0 + tc] / p.topk) : (int64_t)(p0 + tc);
+        src[i] = p.x + xrow * K + 8 * ((lane & 31) ^ (t & 31));
+    }
+    auto issue_x = [&](int sb, _Float16 *buf) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i)
+            dma16(src[i] + 256 * sb, buf + 512 * (NDMA * wave + i));
+    };
+
+    float4_t acc[NMAT][NG];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            acc[m][g] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const _Float16 *buf, const WSb (&w)[NMAT]) {
+        float sl[NMAT][8], ol[NMAT][8];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            const uint4 h = w[m].h;
+            const float d = half_to_float(h.x), dmin = half_to_float(h.x >> 16);
+            const float d24 = d * 16777216.f, d20 = d * 1048576.f;
+            const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
+            const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+            const uint32_t m03 = h.z & 0x3F3F3F3Fu;
+            const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+            sl[m][0] = ubyte_to_float<0>(sc03) * d24;
+            sl[m][1] = ubyte_to_float<1>(sc03) * d20;
+            sl[m][2] = ubyte_to_float<2>(sc03) * d24;
+            sl[m][3] = ubyte_to_float<3>(sc03) * d20;
+            sl[m][4] = ubyte_to_float<0>(sc47) * d24;
+            sl[m][5] = ubyte_to_float<1>(sc47) * d20;
+            sl[m][6] = ubyte_to_float<2>(sc47) * d24;
+            sl[m][7] = ubyte_to_float<3>(sc47) * d20;
+            ol[m][0] = -dmin * ubyte_to_float<0>(m03);
+            ol[m][1] = -dmin * ubyte_to_float<1>(m03);
+            ol[m][2] = -dmin * ubyte_to_float<2>(m03);
+            ol[m][3] = -dmin * ubyte_to_float<3>(m03);
+            ol[m][4] = -dmin * ubyte_to_float<0>(m47);
+            ol[m][5] = -dmin * ubyte_to_float<1>(m47);
+            ol[m][6] = -dmin * ubyte_to_float<2>(m47);
+            ol[m][7] = -dmin * ubyte_to_float<3>(m47);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            half8_t bop[NMAT][2]; // [matrix][sub-block 2g, 2g+1], k = 8q .. 8q+7 in order
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const uint32_t D0 = w[m].q[g].x, D1 = w[m].q[g].y;
+                const uint32_t t0 = D0 >> 8, t1 = D1 >> 8;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t mk = hh ? 0x00F000F0u : 0x000F000Fu;
+                    const uint32_t a0 = D0 & mk, a1 = t0 & mk; // bytes (0,2), (1,3)
+                    const uint32_t a2 = D1 & mk, a3 = t1 & mk; // bytes (4,6), (5,7)
+                    const float s = sl[m][2 * g + hh], o = ol[m][2 * g + hh];
+                    const uint4 v = make_uint4(deq2(a0, 0, a1, 0, s, o), deq2(a0, 1, a1, 1, s, o),
+                                               deq2(a2, 0, a3, 0, s, o), deq2(a2, 1, a3, 1, s, o));
+                    bop[m][hh] = __builtin_bit_cast(half8_t, v);
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int c = 4 * (2 * g + hh) + quarter; // 16-byte chunk of the 512-byte slice
+#pragma unroll
+                for (int tg = 0; tg < NG; ++tg) {
+                    const int t = 16 * tg + col;
+                    const half8_t a =
+                        *reinterpret_cast<const half8_t *>(buf + 256 * t + 8 * (c ^ (t & 31)));
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m)
+                        acc[m][tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[m][hh],
+                                                                            acc[m][tg], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // the previous chunk's readers are done with both buffers
+    __syncthreads();
+    WSb wa[NMAT], wb[NMAT];
+    issue_x(0, xs0);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+        load_wsb(wrow[m], 0, quarter, wa[m]);
+    // two super-blocks per iteration so that buffers and register sets stay fixed
+    for (int sb = 0; sb < nsb; sb += 2) {
+        // retire this wave's copies and weight loads of super-block sb, then
+        // publish the copies of every wave
+        __builtin_amdgcn_s_waitcnt(0); // vmcnt(0) expcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (sb + 1 < nsb) {
+            issue_x(sb + 1, xs1);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+                load_wsb(wrow[m], sb + 1, quarter, wb[m]);
+        }
+        compute(xs0, wa);
+        if (sb + 1 >= nsb)
+            break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        if (sb + 2 < nsb) {
+            issue_x(sb + 2, xs0);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+                load_wsb(wrow[m], sb + 2, quarter, wa[m]);
+        }
+        compute(xs1, wb);
+    }
+
+    // element i of group tg: token 16*tg + 4*quarter + i, weight row `row`
+#pragma unroll
+    for (int tg = 0; tg < NG; ++tg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * tg + 4 * quarter + i;
+            if (t >= nc)
+                continue;
+            const int64_t pos = p0 + t;
+            if constexpr (MODE == 0) {
+                const float v = silu(acc[0][tg][i]) * acc[1][tg][i];
+                reinterpret_cast<uint16_t *>(p.y)[pos * M + row] = (uint16_t)pack_half2(v, 0.f);
+            } else {
+                reinterpret_cast<float *>(p.y)[pos * M + row] = acc[0][tg][i];
+            }
+        }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT, 2) void moe_skinny_kernel(SkinnyParams p)
+{
+    __shared__ __attribute__((aligned(16))) _Float16 xs0[ST * 256];
+    __shared__ __attribute__((aligned(16))) _Float16 xs1[ST * 256];
+    const int e = blockIdx.y;
+    const int begin = p.offsets[e], end = p.offsets[e + 1];
+    for (int c0 = begin; c0 < end; c0 += ST) {
+        const int nc = end - c0 < ST ? end - c0 : ST;
+        switch ((nc + 15) >> 4) {
+        case 1: run_chunk<MODE, 1>(p, e, c0, nc, xs0, xs1); break;
+        case 2: run_chunk<MODE, 2>(p, e, c0, nc, xs0, xs1); break;
+        case 3: run_chunk<MODE, 3>(p, e, c0, nc, xs0, xs1); break;
+        default: run_chunk<MODE, 4>(p, e, c0, nc, xs0, xs1); break;
+        }
+    }
+}
+
+} // namespace
+
+bool moe_skinny_applies(int64_t assignments, int64_t experts)
+{
+    return assignments <= 48 * experts;
+}
+
+hipError_t launch_moe_skinny(const MoeArgs &a, hipStream_t s)
+{
+    SkinnyParams p{};
+    p.offsets = reinterpret_cast<const int32_t *>(a.ws + a.off[0]);
+    p.sorted = reinterpret_cast<const int32_t *>(a.ws + a.off[1]);
+    p.topk = (int)a.topk;
+
+    // gate/up with the SwiGLU epilogue: h[pos][0..I) in binary16
+    p.w = a.w_gate;
+    p.w2 = a.w_up;
+    p.x = a.x;
+    p.y = a.ws + a.off[4];
+    p.M = (int)a.I;
+    p.K = (int)a.H;
+    p.expert_bytes = a.I * (a.H / kQ4kWeights) * kQ4kBytes;
+    hipLaunchKernelGGL(moe_skinny_kernel<0>, dim3((unsigned)(a.I / SR), (unsigned)a.E), dim3(NT),
+                       0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+
+    // down: d[pos][0..H) in binary32
+    p.w = a.w_down;
+    p.w2 = nullptr;
+    p.x = reinterpret_cast<const uint16_t *>(a.ws + a.off[4]);
+    p.y = a.ws + a.off[5];
+    p.M = (int)a.H;
+    p.K = (int)a.I;
+    p.expert_bytes = a.H * (a.I / kQ4kWeights) * kQ4kBytes;
+    hipLaunchKernelGGL(moe_skinny_kernel<1>, dim3((unsigned)(a.H / SR), (unsigned)a.E), dim3(NT),
+                       0, s, p);
+    return hipGetLastError();
+}
+
+} // namespace gq

@@ -156,3 +156,21 @@ def test_moe_olmoe_shape_sampled(T):
     toks = [0, T // 2, T - 1]
     worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks)
     say("  staged worst ratios", worst)
+
+
+def test_moe_few_tokens_per_expert_chunks():
+    """Few tokens per expert on average (the weight-streaming path), with one
+    expert over its 64-token chunk (80 tokens) and ragged counts elsewhere;
+    every token checked in stages."""
+    T, H, I, E, k = 100, 512, 256, 8, 2
+    wg, wu, wd, x16, _, _ = _setup(62, T, H, I, E, k)
+    ids = np.zeros((T, k), np.int32)
+    for t in range(T):
+        ids[t] = [0, 1 + t % 7] if t < 80 else [2 + t % 5, 7]
+    g = np.random.default_rng(63)
+    wts = g.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
+                    range(T))
+    say("moe chunks staged", worst)
