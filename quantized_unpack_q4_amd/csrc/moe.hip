@@ -31,89 +31,136 @@ int moe_token_tile(int64_t assignments, int64_t experts)
     return mean <= 48 ? 32 : mean <= 96 ? 64 : 128;
 }
 
+// Lanes of this wave whose valid expert id equals this lane's (8 ballots over
+// the id bits, E <= 256).
+__device__ __forceinline__ uint64_t same_expert_lanes(bool valid, int e)
+{
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const bool set = valid && ((e >> bit) & 1);
+        const uint64_t b = __ballot(set);
+        peers &= set ? b : ~b;
+    }
+    return peers;
+}
+
+// Exclusive prefix sum of v over threads 0 .. 64*nw - 1 (nw <= 4 waves);
+// every thread of the workgroup must call it.  Returns the exclusive prefix
+// and sets *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int nw, int *scratch, int *total)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(inc, off, 64);
+        if (lane >= off)
+            inc += u;
+    }
+    if (wave < nw && lane == 63)
+        scratch[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < nw; ++w) {
+        before += w < wave ? scratch[w] : 0;
+        all += scratch[w];
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
 // offsets[0..E-1]: first sorted position of each expert; offsets[E]: number of
 // valid assignments; offsets[E+1]: number of token tiles; offsets[E+2]:
 // assignments dropped because their id lies outside [0, E).
+//
+// Wave w owns the contiguous slice [w*S, (w+1)*S) of the assignments: it
+// counts its slice per expert (ballot ranking, no atomics), one scan across
+// waves and experts turns the counts into starting positions, and a second
+// walk of the slice hands out positions in assignment order, so the order is
+// stable by (expert, assignment index).
 __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
     const int32_t *__restrict__ ids, int A, int E, int BN, int max_tiles,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ pos_of,
     int32_t *__restrict__ tiles)
 {
-    __shared__ int cnt[kMaxExperts];
-    __shared__ int base[kMaxExperts];
-    __shared__ int wcnt[kGroupWaves][kMaxExperts];
-    __shared__ int ndrop;
+    __shared__ int wstart[kGroupWaves][kMaxExperts]; // per wave: count, then first position
+    __shared__ int wdrop[kGroupWaves];
+    __shared__ int scratch[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    for (int e = tid; e < E; e += kGroupThreads)
-        cnt[e] = 0;
-    if (tid == 0)
-        ndrop = 0;
-    __syncthreads();
-    for (int a = tid; a < A; a += kGroupThreads) {
-        const int e = ids[a];
-        if (e >= 0 && e < E)
-            atomicAdd(&cnt[e], 1);
-        else
-            atomicAdd(&ndrop, 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int off = 0, nt = 0;
-        for (int e = 0; e < E; ++e) {
-            base[e] = off;
-            offsets[e] = off;
-            for (int p = off; p < off + cnt[e]; p += BN) {
-                tiles[nt] = e;
-                tiles[max_tiles + nt] = p;
-                ++nt;
-            }
-            off += cnt[e];
-        }
-        offsets[E] = off;
-        offsets[E + 1] = nt;
-        offsets[E + 2] = ndrop;
-    }
-    __syncthreads();
-
+    const int S = (A + kGroupWaves - 1) / kGroupWaves;
+    const int a_begin = wave * S, a_end = min(A, a_begin + S);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int c0 = 0; c0 < A; c0 += kGroupThreads) {
-        const int a = c0 + tid;
-        const int e = a < A ? ids[a] : -1;
+
+    for (int i = tid; i < kGroupWaves * kMaxExperts; i += kGroupThreads)
+        wstart[i / kMaxExperts][i % kMaxExperts] = 0;
+    __syncthreads();
+
+    // 1. per-wave counts
+    int drop = 0;
+    for (int c = a_begin; c < a_end; c += 64) {
+        const int a = c + lane;
+        const int e = a < a_end ? ids[a] : -1;
         const bool valid = e >= 0 && e < E;
-        // lanes of this wave holding the same expert id
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const bool set = valid && ((e >> bit) & 1);
-            const uint64_t b = __ballot(set);
-            peers &= set ? b : ~b;
+        const uint64_t peers = same_expert_lanes(valid, e);
+        if (valid && __popcll(peers & below) == 0)
+            wstart[wave][e] += __popcll(peers);
+        drop += __popcll(__ballot(a < a_end && !valid));
+    }
+    if (lane == 0)
+        wdrop[wave] = drop;
+    __syncthreads();
+
+    // 2. per expert: total count, then expert bases and token tiles (scans
+    // over experts, E <= 256 = 4 waves of threads)
+    const int nw = (E + 63) / 64;
+    int cnt = 0;
+    if (tid < E) {
+        for (int w = 0; w < kGroupWaves; ++w)
+            cnt += wstart[w][tid];
+    }
+    int total_valid = 0, total_tiles = 0;
+    const int base = block_exclusive_scan(tid < E ? cnt : 0, nw, scratch, &total_valid);
+    const int ntile = tid < E ? (cnt + BN - 1) / BN : 0;
+    const int tbase = block_exclusive_scan(ntile, nw, scratch, &total_tiles);
+    if (tid < E) {
+        offsets[tid] = base;
+        int run = base;
+        for (int w = 0; w < kGroupWaves; ++w) {
+            const int t = wstart[w][tid];
+            wstart[w][tid] = run;
+            run += t;
         }
+        for (int i = 0; i < ntile; ++i) {
+            tiles[tbase + i] = tid;
+            tiles[max_tiles + tbase + i] = base + i * BN;
+        }
+    }
+    if (tid == 0) {
+        int nd = 0;
+        for (int w = 0; w < kGroupWaves; ++w)
+            nd += wdrop[w];
+        offsets[E] = total_valid;
+        offsets[E + 1] = total_tiles;
+        offsets[E + 2] = nd;
+    }
+    __syncthreads();
+
+    // 3. positions, in assignment order within each wave's slice
+    for (int c = a_begin; c < a_end; c += 64) {
+        const int a = c + lane;
+        const int e = a < a_end ? ids[a] : -1;
+        const bool valid = e >= 0 && e < E;
+        const uint64_t peers = same_expert_lanes(valid, e);
         const int rank = __popcll(peers & below);
-        for (int i = tid; i < kGroupWaves * E; i += kGroupThreads)
-            wcnt[i / E][i % E] = 0;
-        __syncthreads();
+        const int pos = valid ? wstart[wave][e] + rank : -1;
         if (valid && rank == 0)
-            wcnt[wave][e] = __popcll(peers);
-        __syncthreads();
-        for (int x = tid; x < E; x += kGroupThreads) {
-            int run = base[x];
-            for (int w = 0; w < kGroupWaves; ++w) {
-                const int t = wcnt[w][x];
-                wcnt[w][x] = run;
-                run += t;
-            }
-            base[x] = run;
-        }
-        __syncthreads();
-        if (valid) {
-            const int pos = wcnt[wave][e] + rank;
+            wstart[wave][e] += __popcll(peers);
+        if (valid)
             sorted[pos] = a;
+        if (a < a_end)
             pos_of[a] = pos;
-        } else if (a < A) {
-            pos_of[a] = -1;
-        }
-        __syncthreads();
     }
 }
 
