@@ -99,14 +99,33 @@ constexpr int FM = TM / 32, FN = TN / 32; // 32 x 32 fragments per wave
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
 constexpr int waitcnt_vm(int vm) { return waitcnt_vm_lgkm0(vm) | (15 << 8); }
 
+enum { kBigDense = 0, kBigGateUp = 1, kBigDown = 2 };
+
+struct BigParams {
+    const uint8_t *w, *w2; // Q4_K weights (gate/up: gate, up; experts stacked)
+    const uint16_t *x;     // binary16 activations, rows of K
+    void *y;               // dense: Y [N][M] binary16; gate/up: h [A][M] binary16; down: d [A][M] binary32
+    int M, K, N;           // weight rows (per expert), reduction length, activation rows (dense)
+    int tiles_m, tiles_total;
+    // grouped experts: token tiles of 256 sorted positions, one expert each
+    const int32_t *sorted, *tiles, *offsets;
+    int max_tiles, topk, E;
+    int64_t expert_bytes;
+};
+
 } // namespace
 
-__global__ __launch_bounds__(NT, 1) void gemm_q4k_big_kernel(const uint8_t *__restrict__ w,
-                                                             const uint16_t *__restrict__ x,
-                                                             uint16_t *__restrict__ y, int M,
-                                                             int K, int N, int tiles_m,
-                                                             int tiles_total)
+// MODE kBigDense: Y = X W^T over 256 x 256 tiles.  MODE kBigGateUp: a tile is
+// 128 rows of an expert's gate matrix and the same 128 rows of its up matrix
+// (waves 0-3 and 4-7) against up to 256 of the expert's tokens, gathered
+// through the sorted assignment list; the gate accumulators are passed to the
+// up waves through LDS and h = binary16(silu(g) * u) is written.  MODE
+// kBigDown: 256 rows of an expert's down matrix against its rows of h,
+// binary32 outputs.
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void gemm_q4k_big_kernel(BigParams p)
 {
+    const int M = p.M, K = p.K;
     // four distinct LDS objects (not one array of buffers) so that the
     // compiler can tell the copies into one buffer from the reads of the other
     __shared__ __attribute__((aligned(16))) _Float16 sX0[BN * KS];
@@ -118,15 +137,30 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4k_big_kernel(const uint8_t *__re
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
-    // XCD-aware tile order: the hardware deals consecutive workgroups to the
-    // 8 XCDs in turn; give XCD x the contiguous tile run [x*T/8, (x+1)*T/8).
-    const int b = blockIdx.x;
-    const int per = (tiles_total + 7) / 8;
-    const int tile = (b % 8) * per + b / 8;
-    if (tile >= tiles_total)
-        return;
-    const int n_t = tile / tiles_m, m_t = tile % tiles_m;
-    const int m0 = m_t * BM, n0 = n_t * BN;
+    int m0, n0, nvalid, e = 0;
+    if constexpr (MODE == kBigDense) {
+        // XCD-aware tile order: the hardware deals consecutive workgroups to
+        // the 8 XCDs in turn; give XCD x the contiguous tile run
+        // [x*T/8, (x+1)*T/8).
+        const int b = blockIdx.x;
+        const int per = (p.tiles_total + 7) / 8;
+        const int tile = (b % 8) * per + b / 8;
+        if (tile >= p.tiles_total)
+            return;
+        const int n_t = tile / p.tiles_m, m_t = tile % p.tiles_m;
+        m0 = m_t * BM;
+        n0 = n_t * BN;
+        nvalid = p.N - n0 < BN ? p.N - n0 : BN;
+    } else {
+        const int t = blockIdx.y;
+        if (t >= p.offsets[p.E + 1])
+            return;
+        e = p.tiles[t];
+        n0 = p.tiles[p.max_tiles + t]; // first sorted position of the tile
+        const int end = p.offsets[e + 1];
+        nvalid = end - n0 < BN ? end - n0 : BN;
+        m0 = (int)blockIdx.x * (MODE == kBigGateUp ? BM / 2 : BM);
+    }
 
     const int nsb = K >> 8;
     const size_t rowb = (size_t)nsb * kQ4kBytes;
@@ -137,10 +171,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4k_big_kernel(const uint8_t *__re
     // are chunks 2p, 2p+1 of the row's LDS slice, their high nibbles chunks
     // 4+2p, 5+2p
     const int drow = tid >> 1, dp = tid & 1;
-    const bool wrow_ok = m0 + drow < M;
-    const int wr = wrow_ok ? m0 + drow : M - 1;
-    // byte offset of this thread's row (+16 for the second half); the whole
-    // weight matrix is below 2^31 bytes on this path
+    // this thread's weight row: dense and down rows m0 + drow; gate/up rows
+    // m0 + drow of gate (waves 0-3) and m0 + drow - 128 of up (waves 4-7)
+    const uint8_t *w = p.w;
+    int wr_want = m0 + drow;
+    if constexpr (MODE != kBigDense)
+        w = ((MODE == kBigGateUp && wave >= 4) ? p.w2 : p.w) + (size_t)e * p.expert_bytes;
+    if constexpr (MODE == kBigGateUp)
+        wr_want = m0 + (drow & (BM / 2 - 1));
+    const bool wrow_ok = wr_want < M;
+    const int wr = wrow_ok ? wr_want : M - 1;
+    // byte offset of this thread's row (+16 for the second half); the weight
+    // matrix (one expert's) is below 2^31 bytes on this path
     const uint32_t woff = (uint32_t)wr * (uint32_t)rowb + 16u * dp;
 
     // activation copies: copy i of wave v fills LDS slots [(4v + i) * 64, +64),
@@ -153,10 +195,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4k_big_kernel(const uint8_t *__re
         const int xchunk = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int n = min(n0 + xr0 + 8 * i, N - 1);
-            xoff[i] = ((uint32_t)n * (uint32_t)K + 8u * xchunk) * 2u;
+            const int nl = min(xr0 + 8 * i, nvalid - 1); // rows past the tile repeat its last
+            int row = n0 + nl;
+            if constexpr (MODE == kBigGateUp)
+                row = p.sorted[row] / p.topk; // the token of that sorted position
+            xoff[i] = ((uint32_t)row * (uint32_t)K + 8u * xchunk) * 2u;
         }
     }
+    const uint16_t *x = p.x;
     auto issue_x = [&](int kt, auto buf_c) {
         constexpr int buf = decltype(buf_c)::value;
         const uint16_t *xk = x + (size_t)kt * KS; // wave-uniform
@@ -328,16 +374,69 @@ __global__ __launch_bounds__(NT, 1) void gemm_q4k_big_kernel(const uint8_t *__re
     mfma(a1, b1); // last sub-step of the last step
 
     // epilogue: element v of fragment (i, j) is weight row
-    // 8*(v/4) + 4*(lane/32) + v%4 and activation row lane % 32
+    // 8*(v/4) + 4*(lane/32) + v%4 and activation row lane % 32 of the wave's tile
+    if constexpr (MODE == kBigGateUp) {
+        // gate waves (wm = 0) hand their accumulators to the up waves with the
+        // same wn through LDS buffer wn (32 KB: 64 lanes x 128 floats, in the
+        // fragment layout both waves share); the K loop's last barrier has
+        // released every buffer
+        float4_t *xch = reinterpret_cast<float4_t *>(wn == 0 ? sX0 : wn == 1 ? sX1 : wn == 2 ? sW0 : sW1);
+        if (wm == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        const float16_t a = acc[i][j];
+                        xch[((i * FN + j) * 4 + v4) * 64 + lane] =
+                            float4_t{a[4 * v4], a[4 * v4 + 1], a[4 * v4 + 2], a[4 * v4 + 3]};
+                    }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (wm == 1) {
+            uint16_t *h = reinterpret_cast<uint16_t *>(p.y);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int nl = wn * TN + 32 * j + (lane & 31);
+                    if (nl >= nvalid)
+                        continue;
+                    uint16_t *hr = h + (size_t)(n0 + nl) * M;
+                    const float16_t u = acc[i][j];
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        const float4_t g = xch[((i * FN + j) * 4 + v4) * 64 + lane];
+                        const int m = m0 + 32 * i + 8 * v4 + 4 * (lane >> 5);
+                        *reinterpret_cast<uint2 *>(hr + m) = make_uint2(
+                            pack_half2(silu(g[0]) * u[4 * v4], silu(g[1]) * u[4 * v4 + 1]),
+                            pack_half2(silu(g[2]) * u[4 * v4 + 2], silu(g[3]) * u[4 * v4 + 3]));
+                    }
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * TN + 32 * j + (lane & 31);
-            if (n >= N)
+            const int nl = wn * TN + 32 * j + (lane & 31);
+            if (nl >= nvalid)
                 continue;
-            uint16_t *yr = y + (size_t)n * M;
             const float16_t a = acc[i][j];
+            if constexpr (MODE == kBigDown) {
+                float *dr = reinterpret_cast<float *>(p.y) + (size_t)(n0 + nl) * M;
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int m = m0 + wm * TM + 32 * i + 8 * v4 + 4 * (lane >> 5);
+                    *reinterpret_cast<float4_t *>(dr + m) =
+                        float4_t{a[4 * v4], a[4 * v4 + 1], a[4 * v4 + 2], a[4 * v4 + 3]};
+                }
+                continue;
+            }
+            uint16_t *yr = reinterpret_cast<uint16_t *>(p.y) + (size_t)(n0 + nl) * M;
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int m = m0 + wm * TM + 32 * i + 8 * v4 + 4 * (lane >> 5);
@@ -366,11 +465,64 @@ bool gemm_big_applies(int64_t M, int64_t K, int64_t N)
 hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s)
 {
-    const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-    const int total = tm * tn;
-    const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(gemm_q4k_big_kernel, dim3((unsigned)grid), dim3(NT), 0, s,
-                       (const uint8_t *)w, x, y, (int)M, (int)K, (int)N, tm, total);
+    BigParams p{};
+    p.w = (const uint8_t *)w;
+    p.x = x;
+    p.y = y;
+    p.M = (int)M;
+    p.K = (int)K;
+    p.N = (int)N;
+    p.tiles_m = (int)((M + BM - 1) / BM);
+    p.tiles_total = p.tiles_m * (int)((N + BN - 1) / BN);
+    const int grid = (p.tiles_total + 7) / 8 * 8;
+    hipLaunchKernelGGL(gemm_q4k_big_kernel<kBigDense>, dim3((unsigned)grid), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+int moe_big_token_tile() { return BN; }
+
+bool moe_big_applies(int64_t assignments, int64_t experts, int64_t H, int64_t I)
+{
+    // about 160 or more tokens per expert on average, and 32-bit byte offsets
+    // for one expert's matrices and for the activations and h
+    return assignments >= 160 * experts && I * (H / 256) * kQ4kBytes < (1ll << 31) &&
+           assignments * I * 2 < (1ll << 31) && assignments * H * 2 < (1ll << 31);
+}
+
+hipError_t launch_moe_big(const MoeArgs &a, int max_tiles, hipStream_t s)
+{
+    BigParams p{};
+    p.offsets = reinterpret_cast<const int32_t *>(a.ws + a.off[0]);
+    p.sorted = reinterpret_cast<const int32_t *>(a.ws + a.off[1]);
+    p.tiles = reinterpret_cast<const int32_t *>(a.ws + a.off[3]);
+    p.max_tiles = max_tiles;
+    p.topk = (int)a.topk;
+    p.E = (int)a.E;
+
+    // gate/up with the SwiGLU epilogue: h[pos][0..I) in binary16
+    p.w = a.w_gate;
+    p.w2 = a.w_up;
+    p.x = a.x;
+    p.y = a.ws + a.off[4];
+    p.M = (int)a.I;
+    p.K = (int)a.H;
+    p.expert_bytes = a.I * (a.H / kQ4kWeights) * kQ4kBytes;
+    hipLaunchKernelGGL(gemm_q4k_big_kernel<kBigGateUp>,
+                       dim3((unsigned)(a.I / (BM / 2)), (unsigned)max_tiles), dim3(NT), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+
+    // down: d[pos][0..H) in binary32
+    p.w = a.w_down;
+    p.w2 = nullptr;
+    p.x = reinterpret_cast<const uint16_t *>(a.ws + a.off[4]);
+    p.y = a.ws + a.off[5];
+    p.M = (int)a.H;
+    p.K = (int)a.I;
+    p.expert_bytes = a.H * (a.I / kQ4kWeights) * kQ4kBytes;
+    hipLaunchKernelGGL(gemm_q4k_big_kernel<kBigDown>, dim3((unsigned)(a.H / BM), (unsigned)max_tiles),
+                       dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

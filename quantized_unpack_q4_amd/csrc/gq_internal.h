@@ -68,5 +68,10 @@ int moe_token_tile(int64_t assignments, int64_t experts);
 // Expert products streamed once per chunk of 64 tokens (few tokens per expert).
 bool moe_skinny_applies(int64_t assignments, int64_t experts);
 hipError_t launch_moe_skinny(const MoeArgs &a, hipStream_t s);
+// Expert products on 256 x 256 tiles (many tokens per expert); token tiles of
+// moe_big_token_tile() sorted positions.
+bool moe_big_applies(int64_t assignments, int64_t experts, int64_t H, int64_t I);
+int moe_big_token_tile();
+hipError_t launch_moe_big(const MoeArgs &a, int max_tiles, hipStream_t s);
 
 } // namespace gq

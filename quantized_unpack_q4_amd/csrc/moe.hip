@@ -9,8 +9,9 @@
 //               lists the token tiles of every expert and gives each
 //               (token, slot) assignment a stable position in expert order
 //               (ties keep assignment order, so the result is deterministic);
-//   2. gate/up  grouped matrix product with the SwiGLU epilogue (gemm.hip, or
-//               moe_skinny.hip when the experts average 48 tokens or fewer);
+//   2. gate/up  grouped matrix product with the SwiGLU epilogue (gemm.hip;
+//               moe_skinny.hip when the experts average 48 tokens or fewer,
+//               the 256 x 256 tiles of gemm_big.hip from 160 on);
 //   3. down     grouped matrix product into binary32 rows (likewise);
 //   4. combine  out[t] = sum over slots, in slot order, of weight * row.
 // No atomics touch the outputs and nothing waits on the host.
@@ -194,7 +195,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restric
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s)
 {
     const int64_t A = a.T * a.topk;
-    const int bn = moe_token_tile(A, a.E);
+    const bool big = moe_big_applies(A, a.E, a.H, a.I);
+    const int bn = big ? moe_big_token_tile() : moe_token_tile(A, a.E);
     const int max_tiles = (int)((A + bn - 1) / bn + a.E);
     int32_t *offsets = reinterpret_cast<int32_t *>(a.ws + a.off[0]);
     int32_t *sorted = reinterpret_cast<int32_t *>(a.ws + a.off[1]);
@@ -205,8 +207,9 @@ hipError_t launch_moe(const MoeArgs &a, hipStream_t s)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    err = moe_skinny_applies(A, a.E) ? launch_moe_skinny(a, s)
-                                     : launch_moe_gemms(a, bn, max_tiles, s);
+    err = big ? launch_moe_big(a, max_tiles, s)
+              : moe_skinny_applies(A, a.E) ? launch_moe_skinny(a, s)
+                                           : launch_moe_gemms(a, bn, max_tiles, s);
     if (err != hipSuccess)
         return err;
     const int col_blocks = (int)((a.H / 4 + 255) / 256);

@@ -174,3 +174,25 @@ def test_moe_few_tokens_per_expert_chunks():
     worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
                     range(T))
     say("moe chunks staged", worst)
+
+
+def test_moe_many_tokens_per_expert_tiles():
+    """Many tokens per expert on average (the 256 x 256 tile path): an expert
+    with more than one ragged 256-token tile, an expert with none, every token
+    checked in stages."""
+    T, H, I, E, k = 700, 512, 256, 8, 2
+    wg, wu, wd, x16, _, _ = _setup(64, T, H, I, E, k)
+    g = np.random.default_rng(65)
+    ids = np.zeros((T, k), np.int32)
+    for t in range(T):
+        first = 0 if t < 380 else int(g.integers(1, 7))
+        second = int(g.integers(1, 7))
+        while second == first:
+            second = int(g.integers(1, 7))
+        ids[t] = [first, second]  # expert 7 gets nothing, expert 0 gets 380 tokens
+    wts = g.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
+                    range(T))
+    say("moe tiles staged", worst)
