@@ -92,11 +92,19 @@ def time_graph(torch, g, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def event_time(torch, stream, fn, reps=20, warmup=3):
-    """Median per-call time (s) of fn() on `stream`, HIP events per rep."""
+def event_time(torch, stream, fn, reps=20, warmup=3, warm_s=0.05):
+    """Median per-call time (s) of fn() on `stream`, HIP events per rep, after
+    at least `warmup` calls and `warm_s` seconds of untimed calls (steady clocks
+    and caches for this workload)."""
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
             a = torch.cuda.Event(enable_timing=True)

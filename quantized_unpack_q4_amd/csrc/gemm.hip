@@ -285,7 +285,15 @@ hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_
     p.N = (int)N;
     if (N <= 64)
         return gemm_go<128, 32, 4, 1>(p, s);
-    return gemm_go<128, 128, 2, 2>(p, s);
+    // smaller tiles when the large ones would leave CUs idle: 128 x 128 from
+    // 448 tiles (1.75 per CU of a 256-CU part), 64 x 128 from 384, else 64 x 64
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t t64x128 = ((M + 63) / 64) * ((N + 127) / 128);
+    if (t128 >= 448)
+        return gemm_go<128, 128, 2, 2>(p, s);
+    if (t64x128 >= 384)
+        return gemm_go<64, 128, 1, 4>(p, s);
+    return gemm_go<64, 64, 2, 2>(p, s);
 }
 
 // ---- grouped products of the mixture-of-experts layer ----
