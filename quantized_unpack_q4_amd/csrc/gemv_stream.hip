@@ -222,8 +222,6 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
         }
     };
 
-    stage();
-    __syncthreads();
     for (;;) {
         const int nchunk = (nsb + 15) >> 4;
         const long long lim = (hi - e.byte_begin + tile_bytes - 1) / tile_bytes;
@@ -235,7 +233,13 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
 #pragma unroll
         for (int r = 0; r < kR; ++r)
             acc[r] = 0.f;
+        // the matrix's first weight loads go out before its activations are
+        // staged, so that the two latencies overlap; the barrier before the
+        // staging waits for the previous matrix's readers of the LDS records
         issue(A, rt * kTileRows + wave * kRowsPerWave, sbl);
+        __syncthreads();
+        stage();
+        __syncthreads();
 
         auto step = [&](Frag (&cur)[kR], Frag (&nxt)[kR]) -> bool {
             const int t = st / nchunk, c = st - t * nchunk;
@@ -358,9 +362,6 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
         tile_bytes = (long long)kTileRows * (long long)rowb;
         ntile = (e.M + kTileRows - 1) / kTileRows;
         rt = 0;
-        __syncthreads();
-        stage();
-        __syncthreads();
     }
 }
 
