@@ -135,6 +135,17 @@ gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, in
 gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                       int64_t N, void *stream);
 
+/* gq_gemm_q4k with the kernel family pinned instead of chosen from the shape:
+ * tile_rows = 0 is the automatic choice of gq_gemm_q4k, 64 the small-tile
+ * kernels (64 or 128 weight rows per tile, chosen from the shape), 128 and 256
+ * the large-tile kernel with tiles of that many weight rows by 256 activation
+ * rows.  Same arguments, result and rounding as gq_gemm_q4k (the summation
+ * order inside a tile differs between families, so results agree to binary32
+ * rounding, not bit for bit).  Errors: GQ_EINVAL for any other tile_rows;
+ * GQ_ESHAPE when N*K*2 >= 2^31 with tile_rows 128 or 256. */
+gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                            int64_t N, int64_t tile_rows, void *stream);
+
 /* Mixture-of-experts feed-forward over Q4_K experts (the grouped form):
  *   for every token t and slot s < topk, with e = topk_ids[t][s]:
  *     g = Wg_e x_t, u = Wu_e x_t            (binary16 matrix cores, binary32 sums)

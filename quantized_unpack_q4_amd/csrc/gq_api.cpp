@@ -296,10 +296,9 @@ gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, in
                                              (hipStream_t)stream));
 }
 
-gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
-                      int64_t N, void *stream)
+static gq_status gemm_common(const char *fn, const void *w, const uint16_t *x, uint16_t *y,
+                             int64_t M, int64_t K, int64_t N, int64_t tile_rows, void *stream)
 {
-    static const char fn[] = "gq_gemm_q4k";
     GQ_TRY(check_dim(fn, "M", M, true));
     GQ_TRY(check_k(fn, "K", K, 256));
     GQ_TRY(check_dim(fn, "N", N, true));
@@ -311,9 +310,30 @@ gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, 
     GQ_TRY(check_ptr(fn, "w", w));
     GQ_TRY(check_ptr(fn, "x", x));
     GQ_TRY(check_ptr(fn, "y", y));
-    if (gq::gemm_big_applies(M, K, N))
-        return launched(fn, gq::launch_gemm_big(w, x, y, M, K, N, (hipStream_t)stream));
-    return launched(fn, gq::launch_gemm_q4k(w, x, y, M, K, N, (hipStream_t)stream));
+    if (tile_rows == 0)
+        tile_rows = gq::gemm_big_choice(M, K, N);
+    if (tile_rows == 0 || tile_rows == 64)
+        return launched(fn, gq::launch_gemm_q4k(w, x, y, M, K, N, (hipStream_t)stream));
+    if (!gq::gemm_big_fits(M, K, N))
+        return fail(GQ_ESHAPE, "%s: N*K = %lld is too large for the %lld-row tiles", fn,
+                    (long long)(N * K), (long long)tile_rows);
+    return launched(fn, gq::launch_gemm_big(w, x, y, M, K, N, (int)tile_rows, (hipStream_t)stream));
+}
+
+gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                      int64_t N, void *stream)
+{
+    return gemm_common("gq_gemm_q4k", w, x, y, M, K, N, 0, stream);
+}
+
+gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                            int64_t N, int64_t tile_rows, void *stream)
+{
+    static const char fn[] = "gq_gemm_q4k_tiles";
+    if (tile_rows != 0 && tile_rows != 64 && tile_rows != 128 && tile_rows != 256)
+        return fail(GQ_EINVAL, "%s: tile_rows = %lld must be 0, 64, 128 or 256", fn,
+                    (long long)tile_rows);
+    return gemm_common(fn, w, x, y, M, K, N, tile_rows, stream);
 }
 
 size_t gq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk)

@@ -44,11 +44,15 @@ hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0
 
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s);
-// Large-tile matrix product (prefill): 256 x 256 tiles; applies when there are
-// at least 256 of them and the operands fit 32-bit byte offsets.
-bool gemm_big_applies(int64_t M, int64_t K, int64_t N);
+// Large-tile matrix product (prefill): tiles of bm = 256 or 128 weight rows by
+// 256 activation rows.  gemm_big_fits: the shape fits the kernel's 32-bit
+// activation offsets.  gemm_big_choice: the tile height the automatic
+// dispatch uses (256 when there are 256 such tiles or more, else 128 when
+// there are 192 or more), 0 for the small-tile kernels.
+bool gemm_big_fits(int64_t M, int64_t K, int64_t N);
+int gemm_big_choice(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, hipStream_t s);
+                           int64_t N, int bm, hipStream_t s);
 
 // Mixture-of-experts pieces; ws_off are the region offsets of gq_moe_workspace_offsets.
 struct MoeArgs {

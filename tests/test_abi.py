@@ -72,6 +72,13 @@ def test_gemm_refusals(L):
     assert status_and_msg(L, f(FAKE, None, FAKE, 64, 256, 8, None))[0] == "GQ_EINVAL"
     assert status_and_msg(L, f(FAKE, FAKE, FAKE, 64, 256, 1 << 22, None))[0] == "GQ_ESHAPE"
     assert f(None, None, None, 64, 256, 0, None) == 0
+    g = L.gq_gemm_q4k_tiles
+    assert status_and_msg(L, g(FAKE, FAKE, FAKE, 64, 256, 8, 32, None))[0] == "GQ_EINVAL"
+    assert status_and_msg(L, g(FAKE, FAKE, FAKE, 64, 300, 8, 256, None))[0] == "GQ_ESHAPE"
+    st = g(FAKE, FAKE, FAKE, 64, 1 << 20, 1 << 10, 128, None)
+    s, m = status_and_msg(L, st)
+    assert s == "GQ_ESHAPE" and "128-row" in m
+    assert g(None, None, None, 64, 256, 0, 256, None) == 0
 
 
 def test_moe_workspace_and_refusals(L):

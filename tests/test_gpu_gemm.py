@@ -16,11 +16,14 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _gemm(w_d, x16, M, K):
+def _gemm(w_d, x16, M, K, tile_rows=None):
     torch = torch_cuda()
     N = x16.shape[0]
     y = torch.empty((N, M), dtype=torch.float16, device="cuda")
-    gq.gq_gemm_q4k(w_d, dev(x16), y, M, K, N)
+    if tile_rows is None:
+        gq.gq_gemm_q4k(w_d, dev(x16), y, M, K, N)
+    else:
+        gq.gq_gemm_q4k_tiles(w_d, dev(x16), y, M, K, N, tile_rows)
     return half_bits(y).view(np.float16).astype(np.float64)
 
 
@@ -57,23 +60,28 @@ def test_gemm_parity_prefill_sampled(M, K, N):
     say("  max err/S", r1, r2)
 
 
+@pytest.mark.parametrize("tile_rows", [256, 128, 64])
 @pytest.mark.parametrize("M,K,N", [(256, 256, 256), (600, 1024, 520), (512, 2048, 300),
-                                   (1000, 512, 1030)])
-def test_gemm_parity_large_tiles(M, K, N):
-    """Shapes with M >= 256 and N >= 256 (the 256 x 256 tile path) at sizes the
-    oracle computes in full: several tiles, ragged M and N, the smallest K."""
-    say("gemm large tiles", M, K, N)
+                                   (1000, 512, 1030), (130, 768, 37)])
+def test_gemm_parity_pinned_tiles(M, K, N, tile_rows):
+    """Each kernel family pinned through gq_gemm_q4k_tiles, at sizes the oracle
+    computes in full: several tiles, ragged M and N (also fewer rows than one
+    tile), the smallest K."""
+    say("gemm tiles", tile_rows, M, K, N)
     w = synth.q4k_blocks(94, M, M, K)
     x16 = synth.activations_f16(94, N, N, K)
-    y = _gemm(dev(w), x16, M, K)
+    y = _gemm(dev(w), x16, M, K, tile_rows)
     yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K)
-    r = within(y, yr, S, TOL, "gemm %dx%dx%d" % (M, K, N))
+    r = within(y, yr, S, TOL, "gemm %d-row tiles %dx%dx%d" % (tile_rows, M, K, N))
     say("  max err/S", r)
 
 
-def test_gemm_one_hot_exact_large_tiles():
+@pytest.mark.parametrize("tile_rows", [256, 128])
+def test_gemm_one_hot_exact_large_tiles(tile_rows):
     """One-hot activation rows read out the binary16 weights exactly on the
-    256 x 256 tile path, in every row of a ragged multi-tile output."""
+    large-tile kernel, in every row of a ragged multi-tile output; the k of row
+    i walks every position of a 64-weight step, so each lane and sub-step of
+    the k permutation is checked."""
     M, K, N = 300, 1024, 270
     w = synth.q4k_blocks(95, 0, M, K)
     _, w16 = oracle.dequant(oracle.Q4_K, w, M, K)
@@ -82,7 +90,7 @@ def test_gemm_one_hot_exact_large_tiles():
     x16[np.arange(N), ks] = 1.0
     torch = torch_cuda()
     y = torch.empty((N, M), dtype=torch.float16, device="cuda")
-    gq.gq_gemm_q4k(dev(w), dev(x16), y, M, K, N)
+    gq.gq_gemm_q4k_tiles(dev(w), dev(x16), y, M, K, N, tile_rows)
     yb = half_bits(y)
     for i, k in enumerate(ks):
         assert np.array_equal(yb[i].view(np.float16), w16[:, k].view(np.float16)), (i, k)
