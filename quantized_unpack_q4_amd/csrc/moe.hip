@@ -23,6 +23,7 @@ namespace gq {
 constexpr int kMaxExperts = 256;
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
+constexpr int kGroupBatch = 16;
 
 hipError_t launch_moe_gemms(const MoeArgs &a, int bn, int max_tiles, hipStream_t s);
 
@@ -80,7 +81,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int nw, int *scratch,
 // counts its slice per expert (ballot ranking, no atomics), one scan across
 // waves and experts turns the counts into starting positions, and a second
 // walk of the slice hands out positions in assignment order, so the order is
-// stable by (expert, assignment index).
+// stable by (expert, assignment index).  Both walks load the ids of up to
+// kGroupBatch 64-id chunks at once before processing them in order, so a
+// walk waits for one load latency per batch rather than one per chunk.
 __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
     const int32_t *__restrict__ ids, int A, int E, int BN, int max_tiles,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ pos_of,
@@ -98,16 +101,32 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
         wstart[i / kMaxExperts][i % kMaxExperts] = 0;
     __syncthreads();
 
+    // ids of chunks c0, c0 + 64, ... (kGroupBatch of them), -1 past the slice
+    auto load_batch = [&](int c0, int (&ev)[kGroupBatch]) {
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int a = c0 + 64 * u + lane;
+            ev[u] = a < a_end ? ids[a] : -1;
+        }
+    };
+
     // 1. per-wave counts
     int drop = 0;
-    for (int c = a_begin; c < a_end; c += 64) {
-        const int a = c + lane;
-        const int e = a < a_end ? ids[a] : -1;
-        const bool valid = e >= 0 && e < E;
-        const uint64_t peers = same_expert_lanes(valid, e);
-        if (valid && __popcll(peers & below) == 0)
-            wstart[wave][e] += __popcll(peers);
-        drop += __popcll(__ballot(a < a_end && !valid));
+    for (int c0 = a_begin; c0 < a_end; c0 += 64 * kGroupBatch) {
+        int ev[kGroupBatch];
+        load_batch(c0, ev);
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int a = c0 + 64 * u + lane;
+            if (c0 + 64 * u >= a_end)
+                break; // wave-uniform
+            const int e = ev[u];
+            const bool valid = e >= 0 && e < E;
+            const uint64_t peers = same_expert_lanes(valid, e);
+            if (valid && __popcll(peers & below) == 0)
+                wstart[wave][e] += __popcll(peers);
+            drop += __popcll(__ballot(a < a_end && !valid));
+        }
     }
     if (lane == 0)
         wdrop[wave] = drop;
@@ -149,19 +168,26 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
     __syncthreads();
 
     // 3. positions, in assignment order within each wave's slice
-    for (int c = a_begin; c < a_end; c += 64) {
-        const int a = c + lane;
-        const int e = a < a_end ? ids[a] : -1;
-        const bool valid = e >= 0 && e < E;
-        const uint64_t peers = same_expert_lanes(valid, e);
-        const int rank = __popcll(peers & below);
-        const int pos = valid ? wstart[wave][e] + rank : -1;
-        if (valid && rank == 0)
-            wstart[wave][e] += __popcll(peers);
-        if (valid)
-            sorted[pos] = a;
-        if (a < a_end)
-            pos_of[a] = pos;
+    for (int c0 = a_begin; c0 < a_end; c0 += 64 * kGroupBatch) {
+        int ev[kGroupBatch];
+        load_batch(c0, ev);
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int a = c0 + 64 * u + lane;
+            if (c0 + 64 * u >= a_end)
+                break; // wave-uniform
+            const int e = ev[u];
+            const bool valid = e >= 0 && e < E;
+            const uint64_t peers = same_expert_lanes(valid, e);
+            const int rank = __popcll(peers & below);
+            const int pos = valid ? wstart[wave][e] + rank : -1;
+            if (valid && rank == 0)
+                wstart[wave][e] += __popcll(peers);
+            if (valid)
+                sorted[pos] = a;
+            if (a < a_end)
+                pos_of[a] = pos;
+        }
     }
 }
 

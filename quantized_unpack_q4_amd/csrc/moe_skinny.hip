@@ -62,13 +62,18 @@ __device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base)
 
 // Two binary16 weights from two quants taken as binary16 subnormals and the
 // binary32 scale s and offset o: binary16(binary32(s*q + o)) each, packed.
+// Two binary32 mixed-precision FMAs and one packed round-to-nearest
+// conversion, written out: the fused binary16-result forms of the FMA take
+// about twice the issue time of either.
 __device__ __forceinline__ uint32_t deq2(uint32_t qa, int sela, uint32_t qb, int selb, float s,
                                          float o)
 {
     const h2_t a = __builtin_bit_cast(h2_t, qa), b = __builtin_bit_cast(h2_t, qb);
-    const _Float16 lo = (_Float16)fmaf((float)(sela ? a.y : a.x), s, o);
-    const _Float16 hi = (_Float16)fmaf((float)(selb ? b.y : b.x), s, o);
-    return __builtin_bit_cast(uint32_t, h2_t{lo, hi});
+    const float lo = fmaf((float)(sela ? a.y : a.x), s, o);
+    const float hi = fmaf((float)(selb ? b.y : b.x), s, o);
+    uint32_t r;
+    asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
 }
 
 // This lane's packed weights of one super-block: the header of its row and its
