@@ -381,9 +381,12 @@ static int device_cus()
     return cus[dev];
 }
 
+// Two workgroups per CU, all resident at once: with more (two or more rounds)
+// the second round starts staggered behind the first and the last CUs finish
+// later (measured on the decode stack: 2 x CUs 741 us, 3 x 751, 4 x 763).
 int gemv_stream_grid(long long total_bytes, long long tiles)
 {
-    long long g = 4LL * device_cus();
+    long long g = 2LL * device_cus();
     if (tiles < g)
         g = tiles;
     return (int)(g > 0 ? g : 1);
