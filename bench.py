@@ -92,6 +92,60 @@ def time_graph(torch, g, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def probe_ceilings(torch, stream, prefill, decode_gbs, stack_bytes):
+    """Achievable ceilings from the measurement probes (libgq_probe.so, built
+    beside libgq.so): a plain streaming read of the decode stack's byte count
+    and a register-only binary16 matrix-instruction loop over every CU; and
+    the decode and prefill results as fractions of them."""
+    import ctypes
+    from quantized_unpack_q4_amd import build as gqbuild
+    if not os.path.exists(gqbuild.PROBE_LIB):
+        return {"probes": "libgq_probe.so not built"}
+    P = ctypes.CDLL(gqbuild.PROBE_LIB)
+    vp = ctypes.c_void_p
+    P.gqp_stream_read.argtypes = [vp, ctypes.c_longlong, vp, ctypes.c_int, ctypes.c_int, vp]
+    P.gqp_mfma_f16.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    P.gqp_mfma_f16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    P.gqp_mfma_f16_flops.restype = ctypes.c_longlong
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    nbytes = (stack_bytes + 15) // 16 * 16
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(16 * cus * 4, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    # the best of two read forms and four grid sizes
+    read_gbs, read_cfg = 0.0, None
+    for kind in (0, 1):
+        for mult in (2, 4, 8, 16):
+            grid = mult * cus
+
+            def read():
+                if P.gqp_stream_read(vp(buf.data_ptr()), nbytes, vp(sink.data_ptr()), grid,
+                                     kind, sp) != 0:
+                    raise RuntimeError("gqp_stream_read launch failed")
+            s = event_time(torch, stream, read, reps=10, warm_s=0.02)
+            if nbytes / s / 1e9 > read_gbs:
+                read_gbs, read_cfg = nbytes / s / 1e9, "%s, %d workgroups" % (
+                    ("grid-stride", "per-workgroup range")[kind], grid)
+    out["stream_read_%dB_GB/s" % nbytes] = round(read_gbs, 1)
+    out["stream_read_form"] = read_cfg
+    out["decode_stack_frac_of_stream_read"] = round(decode_gbs / read_gbs, 4)
+    del buf, sink
+    iters = 4096
+    msink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        if P.gqp_mfma_f16(vp(msink.data_ptr()), iters, cus, sp) != 0:
+            raise RuntimeError("gqp_mfma_f16 launch failed")
+    s = event_time(torch, stream, mfma, reps=10)
+    mfma_tf = P.gqp_mfma_f16_flops(iters, cus) / s / 1e12
+    out["mfma_f16_register_loop_TFLOP/s"] = round(mfma_tf, 1)
+    for key, v in prefill.items():
+        out["prefill_%s_frac_of_mfma_loop" % key] = round(v["TFLOP/s"] / mfma_tf, 4)
+    del msink
+    return out
+
+
 def event_time(torch, stream, fn, reps=20, warmup=3, warm_s=0.05):
     """Median per-call time (s) of fn() on `stream`, HIP events per rep, after
     at least `warmup` calls and `warm_s` seconds of untimed calls (steady clocks
@@ -314,6 +368,7 @@ def main():
             ceil["fp16_library_matmul_%dx%dxN4096_TFLOP/s" % (M, K)] = round(
                 2.0 * M * K * 4096 / s / 1e12, 1)
             del a16, b16
+        ceil.update(probe_ceilings(torch, stream, pre, value, stack_bytes_total()))
         extra["measured_ceilings"] = ceil
         # mixture of experts, OLMoE-1B-7B shape
         import oracle  # routing only: the oracle's binary64 softmax/top-k on the host

@@ -1,4 +1,5 @@
-"""Build libgq.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Build libgq.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+libgq_probe.so (the measurement probes the benchmark compares against).
 
 Run ``python -m quantized_unpack_q4_amd.build``.  Objects go to ``_build/`` at
 the repository root; the library lands next to this file so the Python
@@ -18,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgq.so")
+PROBE_LIB = os.path.join(PKG, "libgq_probe.so")
+PROBE_SOURCES = ["probes.hip"]
 ARCH = os.environ.get("GQ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["dequant.hip", "gemv.hip", "gemv_stream.hip", "gemv_mfma.hip", "gemm.hip", "gemm_big.hip", "moe.hip", "moe_skinny.hip", "gq_api.cpp"]
@@ -56,17 +59,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

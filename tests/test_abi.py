@@ -174,3 +174,24 @@ def test_multi_plan_checks_and_layout(L):
     assert L.gq_status_str(f(None, FAKE, 4, None)).decode() == "GQ_EINVAL"
     assert L.gq_status_str(f(table, None, 4, None)).decode() == "GQ_EINVAL"
     assert L.gq_status_str(f(table, MISALIGNED, 4, None)).decode() == "GQ_EALIGN"
+
+
+def test_probe_library_loads_and_refuses_bad_arguments():
+    """The measurement probes (a separate library, not part of the gq ABI) load
+    and refuse invalid arguments before launching anything."""
+    from quantized_unpack_q4_amd import build as gqbuild
+    if not os.path.exists(gqbuild.PROBE_LIB):
+        pytest.skip("libgq_probe.so not built")
+    P = ctypes.CDLL(gqbuild.PROBE_LIB)
+    for n in ("gqp_stream_read", "gqp_mfma_f16", "gqp_mfma_f16_flops"):
+        assert hasattr(P, n), n
+    vp = ctypes.c_void_p
+    P.gqp_stream_read.argtypes = [vp, ctypes.c_longlong, vp, ctypes.c_int, ctypes.c_int, vp]
+    P.gqp_mfma_f16.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    P.gqp_mfma_f16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    P.gqp_mfma_f16_flops.restype = ctypes.c_longlong
+    assert P.gqp_stream_read(FAKE, 100, FAKE, 4, 0, None) != 0      # not a multiple of 16
+    assert P.gqp_stream_read(FAKE, 1024, FAKE, 4, 2, None) != 0     # unknown form
+    assert P.gqp_stream_read(None, 1024, FAKE, 4, 0, None) != 0
+    assert P.gqp_mfma_f16(FAKE, 0, 4, None) != 0
+    assert P.gqp_mfma_f16_flops(10, 2) == 2 * 8 * 10 * 8 * 2 * 32 * 32 * 16
