@@ -78,10 +78,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int nw, int *scratch,
 // assignments dropped because their id lies outside [0, E).
 //
 // Wave w owns the contiguous slice [w*S, (w+1)*S) of the assignments: it
-// counts its slice per expert (ballot ranking, no atomics), one scan across
-// waves and experts turns the counts into starting positions, and a second
-// walk of the slice hands out positions in assignment order, so the order is
-// stable by (expert, assignment index).  Both walks load the ids of up to
+// counts its slice per expert (LDS adds into its own counters), one scan
+// across waves and experts turns the counts into starting positions, and a
+// second walk of the slice hands out positions in assignment order (ballot
+// ranking among the lanes of a chunk with the same expert), so the order is
+// stable by (expert, assignment index) and no atomic touches a position.  Both walks load the ids of up to
 // kGroupBatch 64-id chunks at once before processing them in order, so a
 // walk waits for one load latency per batch rather than one per chunk.
 __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
@@ -122,9 +123,10 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
                 break; // wave-uniform
             const int e = ev[u];
             const bool valid = e >= 0 && e < E;
-            const uint64_t peers = same_expert_lanes(valid, e);
-            if (valid && __popcll(peers & below) == 0)
-                wstart[wave][e] += __popcll(peers);
+            // counts only: one LDS add per assignment (a sum, so the order
+            // of the adds does not matter)
+            if (valid)
+                atomicAdd(&wstart[wave][e], 1);
             drop += __popcll(__ballot(a < a_end && !valid));
         }
     }
