@@ -85,9 +85,8 @@ __device__ __forceinline__ float lane_value(float v, int lane)
 constexpr int kStreamMaxK = GemvStreamMaxK;
 constexpr int kRecs = kStreamMaxK / 4;                      // 16-byte x records
 constexpr int kLdsWords = (kRecs + kRecs / 16) * 4 + kStreamMaxK / 32;
-constexpr int kR = 3;                                       // row pairs per wave step
-constexpr int kRowsPerWave = 2 * kR;
-constexpr int kTileRows = 4 * kRowsPerWave;                 // rows per workgroup tile
+constexpr int kR = 3;          // row groups per wave step (a group is 2 or 4 rows)
+constexpr int kTileRowsMin = 24; // rows per workgroup tile with 32 lanes per row
 
 struct Frag {
     uint4 hd, a0, a1, b0, b1; // header, quant group p (32 B), quant group p+2 (32 B)
@@ -102,16 +101,21 @@ __device__ __forceinline__ uint32_t word8(const uint4 &a, const uint4 &b, int i)
 
 } // namespace
 
-__global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry *__restrict__ table,
-                                                                 GemvEntry inline0, int n,
-                                                                 long long total)
+// R row groups per wave step, NB weight-load buffers (loads run NB - 1 steps
+// ahead of the arithmetic), W waves per workgroup.
+template <int R, int NB, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
+    const GemvEntry *__restrict__ table, GemvEntry inline0, int n, long long total)
 {
+    constexpr int kR = R;
+    constexpr int kThreads = 64 * W;
+    constexpr int kSubPerThread = (kStreamMaxK / 32 + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
     uint32_t *xrec = lds;
     float *ssum = reinterpret_cast<float *>(lds + (kRecs + kRecs / 16) * 4);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int half = lane >> 5, p = lane & 1, sbl = (lane & 31) >> 1;
+    const int p = lane & 1;
     const long long lo = total * (long long)blockIdx.x / gridDim.x;
     const long long hi = total * (long long)(blockIdx.x + 1) / gridDim.x;
 
@@ -119,42 +123,25 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
     int di = 0;
     while (di + 1 < n && entry(di + 1).byte_begin <= lo)
         ++di;
-
     GemvEntry e = entry(di);
-    int nsb = e.K >> 8;
-    size_t rowb = (size_t)nsb * kQ4kBytes;
-    long long tile_bytes = (long long)kTileRows * (long long)rowb;
-    int ntile = (e.M + kTileRows - 1) / kTileRows;
-    int rt = (int)((lo - e.byte_begin + tile_bytes - 1) / tile_bytes);
-    while (rt >= ntile) {
-        if (++di >= n)
-            return;
-        e = entry(di);
-        if (e.byte_begin >= hi)
-            return;
-        nsb = e.K >> 8;
-        rowb = (size_t)nsb * kQ4kBytes;
-        tile_bytes = (long long)kTileRows * (long long)rowb;
-        ntile = (e.M + kTileRows - 1) / kTileRows;
-        rt = 0;
-    }
-    if (e.byte_begin + (long long)rt * tile_bytes >= hi)
-        return;
+
+    int nsb = e.K >> 8, r_end = 0, rpg = 2, sps = 16, rsub = 0, sbl = 0;
+    long long rowb = (long long)nsb * kQ4kBytes;
 
     // Power-of-two scale that brings max|x| into [2^14, 2^15): keeps the
     // binary16 hi/lo split accurate for any finite x of moderate magnitude.
-    __shared__ float s_amax[4];
+    __shared__ float s_amax[W];
     float inv_scale = 1.f;
     auto stage = [&]() {
-        // thread t owns sub-blocks t and t + 256 (32 activations each, at most
-        // 512 sub-blocks): every activation is loaded once, all loads in flight
-        // together, and kept in registers for the scale, split and sums
+        // thread t owns sub-blocks t, t + kThreads, ... (32 activations each,
+        // at most 512 sub-blocks): every activation is loaded once, all loads
+        // in flight together, and kept in registers for the scale, split and sums
         const int nsub = e.K >> 5;
-        float4 v[2][8];
+        float4 v[kSubPerThread][8];
         float amax = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int j = tid + 256 * u;
+        for (int u = 0; u < kSubPerThread; ++u) {
+            const int j = tid + kThreads * u;
             if (j < nsub) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -170,7 +157,10 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
         if (lane == 0)
             s_amax[wave] = amax;
         __syncthreads();
-        amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+        amax = s_amax[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i)
+            amax = fmaxf(amax, s_amax[i]);
         int ex = 0;
         if (amax > 0.f)
             (void)frexpf(amax, &ex); // amax < 2^ex
@@ -180,8 +170,8 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
         // lo(x1,x3)); 16 bytes of padding after every 16 records.  ssum[j] is
         // the plain binary32 sum of x over sub-block j.
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int j = tid + 256 * u;
+        for (int u = 0; u < kSubPerThread; ++u) {
+            const int j = tid + kThreads * u;
             if (j < nsub) {
                 float sum = 0.f;
 #pragma unroll
@@ -210,25 +200,48 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
         const int sc = s < nsb ? s : nsb - 1;
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
-            const int row = row0 + 2 * r + half;
-            const int rc = row < e.M ? row : e.M - 1;
+            const int row = row0 + rpg * r + rsub;
+            const int rc = row < r_end ? row : r_end - 1;
             const uint8_t *blk = e.w + (size_t)rc * rowb + (size_t)sc * kQ4kBytes;
             f[r].hd = gload16(blk);
             f[r].a0 = gload16(blk + 16 + 32 * p);
             f[r].a1 = gload16(blk + 32 + 32 * p);
             f[r].b0 = gload16(blk + 80 + 32 * p);
             f[r].b1 = gload16(blk + 96 + 32 * p);
-            f[r].ok = s < nsb && row < e.M;
+            f[r].ok = s < nsb && row < r_end;
         }
     };
 
-    for (;;) {
-        const int nchunk = (nsb + 15) >> 4;
-        const long long lim = (hi - e.byte_begin + tile_bytes - 1) / tile_bytes;
-        const int rt_end = (int)(lim < ntile ? lim : ntile);
-        const int step_hi = rt_end * nchunk;
-        int st = rt * nchunk;
-        Frag A[kR], B[kR];
+    // A workgroup owns every row whose first byte lies in [lo, hi): rows of
+    // one matrix are split between workgroups at row granularity, so every
+    // workgroup streams the same bytes to within one row.
+    for (;; ++di) {
+        if (di >= n)
+            return;
+        e = entry(di);
+        if (e.byte_begin >= hi)
+            return;
+        nsb = e.K >> 8;
+        rowb = (long long)nsb * kQ4kBytes;
+        const long long rel_lo = lo - e.byte_begin, rel_hi = hi - e.byte_begin;
+        const int r_lo = rel_lo <= 0 ? 0 : (int)min((long long)e.M, (rel_lo + rowb - 1) / rowb);
+        r_end = (int)min((long long)e.M, (rel_hi + rowb - 1) / rowb);
+        if (r_lo >= r_end)
+            continue;
+        // 32 lanes per row (16 super-blocks per step), or 16 lanes per row
+        // (8 per step) when that leaves fewer idle lanes in a row's last step
+        const int pad32 = ((nsb + 15) & ~15) - nsb, pad16 = ((nsb + 7) & ~7) - nsb;
+        const int lsh = pad16 < pad32 ? 4 : 5;
+        rpg = 64 >> lsh;
+        sps = 1 << (lsh - 1);
+        rsub = lane >> lsh;
+        sbl = (lane & ((1 << lsh) - 1)) >> 1;
+        const int wave_rows = kR * rpg, tile_rows = W * wave_rows;
+        const int nchunk = (nsb + sps - 1) / sps;
+        const int ntile = (r_end - r_lo + tile_rows - 1) / tile_rows;
+        const int step_hi = ntile * nchunk;
+        int st = 0;
+        Frag A[kR], B[kR], C[kR];
         float acc[kR];
 #pragma unroll
         for (int r = 0; r < kR; ++r)
@@ -236,18 +249,23 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
         // the matrix's first weight loads go out before its activations are
         // staged, so that the two latencies overlap; the barrier before the
         // staging waits for the previous matrix's readers of the LDS records
-        issue(A, rt * kTileRows + wave * kRowsPerWave, sbl);
+        auto issue_step = [&](Frag (&f)[kR], int sx) {
+            const int t = sx / nchunk, c = sx - t * nchunk;
+            issue(f, r_lo + t * tile_rows + wave * wave_rows, c * sps + sbl);
+        };
+        issue_step(A, 0);
+        if (NB == 3)
+            issue_step(B, min(1, step_hi - 1));
         __syncthreads();
         stage();
         __syncthreads();
 
-        auto step = [&](Frag (&cur)[kR], Frag (&nxt)[kR]) -> bool {
+        // cur holds step st; far receives step st + NB - 1 (clamped to the last)
+        auto step = [&](Frag (&cur)[kR], Frag (&far)[kR]) -> bool {
             const int t = st / nchunk, c = st - t * nchunk;
-            const int nst = st + 1 < step_hi ? st + 1 : st;
-            const int nt = nst / nchunk, nc = nst - nt * nchunk;
-            issue(nxt, nt * kTileRows + wave * kRowsPerWave, nc * 16 + sbl);
+            issue_step(far, min(st + NB - 1, step_hi - 1));
 
-            const int s = min(c * 16 + sbl, nsb - 1);
+            const int s = min(c * sps + sbl, nsb - 1);
             const int r0 = 64 * s + 16 * p; // x record of sub-block 2p, position 0
             const int r4 = r0 + 32;         // x record of sub-block 2p+4
             float P0[kR], P1[kR], P4[kR], P5[kR];
@@ -329,39 +347,45 @@ __global__ __launch_bounds__(256, 2) void gemv_q4k_stream_kernel(const GemvEntry
                 acc[r] = fmaf(-dmin, t2, fmaf(d24, t1 * inv_scale, acc[r]));
             }
             if (c == nchunk - 1) {
-                const int row0 = t * kTileRows + wave * kRowsPerWave;
+                const int row0 = r_lo + t * tile_rows + wave * wave_rows;
 #pragma unroll
                 for (int r = 0; r < kR; ++r) {
+                    // every lane of a 16-lane row ends with that row's sum
                     const float v = rowsum16(acc[r]);
-                    const float v0 = lane_value(v, 0) + lane_value(v, 16);
-                    const float v1 = lane_value(v, 32) + lane_value(v, 48);
-                    if (lane == 0 && row0 + 2 * r < e.M)
-                        e.y[row0 + 2 * r] = v0;
-                    if (lane == 1 && row0 + 2 * r + 1 < e.M)
-                        e.y[row0 + 2 * r + 1] = v1;
+                    const float q0 = lane_value(v, 0), q1 = lane_value(v, 16);
+                    const float q2 = lane_value(v, 32), q3 = lane_value(v, 48);
+                    if (rpg == 2) {
+                        const int row = row0 + 2 * r + lane;
+                        if (lane < 2 && row < r_end)
+                            e.y[row] = lane == 0 ? q0 + q1 : q2 + q3;
+                    } else {
+                        const int row = row0 + 4 * r + lane;
+                        if (lane < 4 && row < r_end)
+                            e.y[row] = lane == 0 ? q0 : lane == 1 ? q1 : lane == 2 ? q2 : q3;
+                    }
                     acc[r] = 0.f;
                 }
             }
             ++st;
             return st < step_hi;
         };
-        for (;;) {
-            if (!step(A, B))
-                break;
-            if (!step(B, A))
-                break;
+        if (NB == 2) {
+            for (;;) {
+                if (!step(A, B))
+                    break;
+                if (!step(B, A))
+                    break;
+            }
+        } else {
+            for (;;) {
+                if (!step(A, C))
+                    break;
+                if (!step(B, A))
+                    break;
+                if (!step(C, B))
+                    break;
+            }
         }
-        // next matrix of the table, if it starts inside this workgroup's range
-        if (++di >= n)
-            return;
-        e = entry(di);
-        if (e.byte_begin >= hi)
-            return;
-        nsb = e.K >> 8;
-        rowb = (size_t)nsb * kQ4kBytes;
-        tile_bytes = (long long)kTileRows * (long long)rowb;
-        ntile = (e.M + kTileRows - 1) / kTileRows;
-        rt = 0;
     }
 }
 
@@ -395,14 +419,14 @@ int gemv_stream_grid(long long total_bytes, long long tiles)
 long long gemv_stream_tiles(int64_t M, int64_t K)
 {
     (void)K;
-    return (M + kTileRows - 1) / kTileRows;
+    return (M + kTileRowsMin - 1) / kTileRowsMin;
 }
 
 hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
                               long long total_bytes, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(gemv_q4k_stream_kernel, dim3((unsigned)grid), dim3(256), 0, s, table_dev,
-                       inline0, n, total_bytes);
+    hipLaunchKernelGGL((gemv_q4k_stream_kernel<kR, 2, 4>), dim3((unsigned)grid), dim3(256), 0, s,
+                       table_dev, inline0, n, total_bytes);
     return hipGetLastError();
 }
 
