@@ -12,7 +12,12 @@
 // command-buffer waits per token cut from 192 to 20, one submission per group
 // of layers).  Here the whole table is one launch: the total weight bytes are
 // split into equal contiguous byte ranges, one per workgroup, and a workgroup
-// processes every row tile that starts inside its range.
+// processes every row whose first byte lies inside its range (so every
+// workgroup streams the same bytes to within one row).
+//
+// Lanes per row.  A weight row is covered by 32 lanes (16 super-blocks per
+// step) or, when K/256 is a multiple of 8 but not of 16 (K = 14336), by 16
+// lanes (8 super-blocks per step), so that no step of a row is half empty.
 //
 // Arithmetic per lane.  Two lanes share a 256-weight super-block: lane p
 // (0 or 1) owns quant groups p and p + 2, i.e. sub-blocks 2p, 2p+1, 2p+4 and
