@@ -265,19 +265,21 @@ def main():
         for _ in range(args.warmup):
             table.run(stream)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event pair around each launch, on the stream the kernel runs on: the
+    # kernel's average duration without the gaps between launches
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(args.steps):
+        for a, b in evs:
+            a.record(stream)
             table.run(stream)
-        ev1.record(stream)
+            b.record(stream)
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / args.steps
     value = stack.weight_bytes / sec / 1e9
     # the step is one launch of the streaming kernel: its average duration
-    avg_dur = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    avg_dur = sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / args.steps
     achieved = alg_bytes / avg_dur / 1e9
 
     extra = {"stack_b1_one_launch": {"ms_per_step": round(sec * 1e3, 4),
