@@ -393,6 +393,13 @@ def main():
             flops = 2.0 * T * k * 3 * H * I
             moe["T%d" % T] = {"us": round(s * 1e6, 1), "TFLOP/s": round(flops / s / 1e12, 1),
                               "weight_GB/s": round(wbytes / s / 1e9, 1)}
+            # the routing step on the device (gq_moe_route), timed apart: the
+            # layer above takes the host's binary64 routing as its input
+            lg = torch.from_numpy(synth.router_logits(MOE_WORKLOAD, 0, T, E)).cuda()
+            rid = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            rwt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            s = event_time(torch, stream, lambda: gq.gq_moe_route(lg, rid, rwt, T, E, k, 0, stream))
+            moe["T%d" % T]["route_us"] = round(s * 1e6, 2)
         extra["moe_olmoe"] = moe
         del wg, wu, wd
         # Q8_0 matrix-vector product, 256 x 1024

@@ -165,6 +165,24 @@ gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_do
                           uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
                           int64_t topk, void *ws, size_t ws_bytes, void *stream);
 
+/* Expert routing on the device (the routing step of the mixture-of-experts
+ * layer; the pages' engine routes natively, page "Frink Inference: the Rust
+ * alternative to llama.cpp", opening paragraph).  For every token t:
+ *   topk_ids[t] = the topk experts with the largest logits[t][e], in
+ *                 descending order, equal logits going to the lower expert
+ *                 index (softmax is strictly increasing, so these are the
+ *                 experts with the largest probabilities; the choice is made
+ *                 on the binary32 logits exactly);
+ *   topk_w[t][s] = p[topk_ids[t][s]] with p = softmax(logits[t]) in binary32
+ *                 (exp(l - max) / sum), or, with renormalize != 0, that
+ *                 probability divided by the sum of the topk chosen ones.
+ * logits: [T][E] float.  topk_ids: [T][topk] int32.  topk_w: [T][topk] float
+ * (the inputs of gq_moe_gemm_q4k).  All device pointers, 16-byte aligned.
+ * Requires T >= 0 (T = 0 launches nothing), 1 <= topk <= E <= 256.
+ * Non-finite logits are outside the contract. */
+gq_status gq_moe_route(const float *logits, int32_t *topk_ids, float *topk_w, int64_t T,
+                       int64_t E, int64_t topk, int64_t renormalize, void *stream);
+
 /* Workspace size for gq_moe_gemm_q4k with these sizes (0 if they are invalid). */
 size_t gq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
 

@@ -66,7 +66,7 @@ def lib():
         L.orc_gemv.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, vp]
         L.orc_gemv_separate.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp]
         L.orc_gemm.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
-        L.orc_moe_route.argtypes = [vp, i64, i64, i64, vp, vp]
+        L.orc_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, ctypes.c_int]
         L.orc_moe_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                   vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -193,13 +193,14 @@ def gemm(fmt: int, w, x16, M: int, K: int, rows=None, toks=None):
     return y, S
 
 
-def moe_route(logits, topk: int):
-    """Top-k of the binary64 softmax of each row: (ids int32 [T][k], wts float64 [T][k])."""
+def moe_route(logits, topk: int, renormalize: bool = False):
+    """Top-k of the binary64 softmax of each row: (ids int32 [T][k], wts float64 [T][k]);
+    with renormalize the chosen weights are divided by their sum."""
     logits = np.ascontiguousarray(np.asarray(logits, dtype=np.float32))
     T, E = logits.shape
     ids = np.empty((T, topk), np.int32)
     wts = np.empty((T, topk), np.float64)
-    lib().orc_moe_route(_p(logits), T, E, topk, _p(ids), _p(wts))
+    lib().orc_moe_route(_p(logits), T, E, topk, _p(ids), _p(wts), 1 if renormalize else 0)
     return ids, wts
 
 

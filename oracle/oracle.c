@@ -320,9 +320,10 @@ void orc_gemm(int fmt, const uint8_t *w, const uint16_t *x16, int64_t M, int64_t
 
 /* Routing of one token: p = softmax(logits) in binary64; ids = the topk
  * largest p in descending order, equal values going to the lower expert
- * index; wts = those p as they are (no renormalisation). */
+ * index; wts = those p as they are (renorm == 0), or each divided by the sum
+ * of the topk chosen p (renorm != 0). */
 void orc_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, int32_t *ids,
-                   double *wts)
+                   double *wts, int renorm)
 {
     double *p = (double *)malloc((size_t)E * sizeof(double));
     char *taken = (char *)malloc((size_t)E);
@@ -348,6 +349,13 @@ void orc_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, int3
             taken[best] = 1;
             ids[t * topk + s] = (int32_t)best;
             wts[t * topk + s] = p[best];
+        }
+        if (renorm) {
+            double chosen = 0.0;
+            for (int64_t s = 0; s < topk; s++)
+                chosen += wts[t * topk + s];
+            for (int64_t s = 0; s < topk; s++)
+                wts[t * topk + s] /= chosen;
         }
     }
     free(p);

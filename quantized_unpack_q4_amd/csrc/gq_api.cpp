@@ -396,6 +396,27 @@ gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_do
     return launched(fn, gq::launch_moe(a, (hipStream_t)stream));
 }
 
+gq_status gq_moe_route(const float *logits, int32_t *topk_ids, float *topk_w, int64_t T,
+                       int64_t E, int64_t topk, int64_t renormalize, void *stream)
+{
+    static const char fn[] = "gq_moe_route";
+    GQ_TRY(check_dim(fn, "T", T, true));
+    if (E < 1 || E > 256)
+        return fail(GQ_EINVAL, "%s: E = %lld is outside [1, 256]", fn, (long long)E);
+    if (topk < 1 || topk > E)
+        return fail(GQ_EINVAL, "%s: topk = %lld is outside [1, E = %lld]", fn, (long long)topk,
+                    (long long)E);
+    if (T > ((int64_t)1 << 24))
+        return fail(GQ_ESHAPE, "%s: T = %lld exceeds 2^24 tokens", fn, (long long)T);
+    if (T == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "logits", logits));
+    GQ_TRY(check_ptr(fn, "topk_ids", topk_ids));
+    GQ_TRY(check_ptr(fn, "topk_w", topk_w));
+    return launched(fn, gq::launch_moe_route(logits, topk_ids, topk_w, T, E, topk,
+                                             renormalize != 0, (hipStream_t)stream));
+}
+
 gq_status gq_dequant_q8_0(const void *w, float *out32, uint16_t *out16, int64_t M, int64_t K,
                           void *stream)
 {

@@ -67,6 +67,10 @@ struct MoeArgs {
 };
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 
+// Top-k routing of T tokens over E <= 256 experts (one wave per token).
+hipError_t launch_moe_route(const float *logits, int32_t *ids, float *wts, int64_t T, int64_t E,
+                            int64_t topk, bool renorm, hipStream_t s);
+
 // Token-tile size used by the grouped products for a given mean tokens per expert.
 int moe_token_tile(int64_t assignments, int64_t experts);
 // Expert products streamed once per chunk of 64 tokens (few tokens per expert).

@@ -25,7 +25,7 @@ MAX_BATCH = 16
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
     "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemm_q4k", "gq_gemm_q4k_tiles",
-    "gq_moe_gemm_q4k",
+    "gq_moe_gemm_q4k", "gq_moe_route",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
 )
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.gq_moe_gemm_q4k.restype = st
         L.gq_moe_gemm_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                       vp, sz, vp]
+        L.gq_moe_route.restype = st
+        L.gq_moe_route.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.gq_moe_workspace_bytes.restype = sz
         L.gq_moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
         L.gq_moe_workspace_offsets.restype = st
@@ -259,6 +261,21 @@ def gemm_q4k(w, x16, M: int, K: int, out=None, stream=None):
     y = out if out is not None else torch.empty((N, M), dtype=torch.float16, device=x16.device)
     gq_gemm_q4k(w, x2, y, M, K, N, stream)
     return y
+
+
+def gq_moe_route(logits, topk_ids, topk_w, T, E, topk, renormalize=0, stream=None):
+    _check(lib().gq_moe_route(_ptr(logits), _ptr(topk_ids), _ptr(topk_w), T, E, topk,
+                              int(renormalize), _stream(stream)))
+
+
+def moe_route(logits, topk: int, renormalize=False, stream=None):
+    """Top-k expert routing of logits [T][E] (float32): (ids int32, weights float32)."""
+    import torch
+    T, E = logits.shape
+    ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    wts = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    gq_moe_route(logits, ids, wts, T, E, topk, renormalize, stream)
+    return ids, wts
 
 
 def moe_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, H: int, I: int, E: int, ws=None,

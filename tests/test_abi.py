@@ -109,6 +109,20 @@ def test_moe_workspace_and_refusals(L):
     assert f(*([None] * 7), 0, H, I, E, k, None, 0, None) == 0
 
 
+def test_moe_route_refusals(L):
+    f = L.gq_moe_route
+    for T, E, k, code in ((4, 257, 8, "GQ_EINVAL"), (4, 64, 65, "GQ_EINVAL"), (4, 64, 0, "GQ_EINVAL"),
+                          (4, 0, 1, "GQ_EINVAL"), (-1, 64, 8, "GQ_EINVAL"),
+                          ((1 << 24) + 1, 64, 8, "GQ_ESHAPE")):
+        s, m = status_and_msg(L, f(FAKE, FAKE, FAKE, T, E, k, 0, None))
+        assert s == code and "gq_moe_route" in m, (T, E, k, s, m)
+    s, m = status_and_msg(L, f(None, FAKE, FAKE, 4, 64, 8, 0, None))
+    assert s == "GQ_EINVAL" and "logits" in m
+    s, m = status_and_msg(L, f(FAKE, MISALIGNED, FAKE, 4, 64, 8, 1, None))
+    assert s == "GQ_EALIGN" and "topk_ids" in m
+    assert f(None, None, None, 0, 64, 8, 0, None) == 0  # no tokens: nothing launched
+
+
 def test_dequant_refusals(L):
     assert status_and_msg(L, L.gq_dequant_q4k(FAKE, None, None, 4, 256, None))[0] == "GQ_EINVAL"
     assert status_and_msg(L, L.gq_dequant_q8_0(FAKE, FAKE, None, 4, 40, None))[0] == "GQ_ESHAPE"

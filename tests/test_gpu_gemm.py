@@ -60,6 +60,26 @@ def test_gemm_parity_prefill_sampled(M, K, N):
     say("  max err/S", r1, r2)
 
 
+def test_gemm_parity_ragged_large_tiles():
+    """The automatic dispatch on a shape with 17 x 16 = 272 tiles of 256 x 256
+    (more than one round of the chip), ragged in weight rows (the last tile
+    holds 156) and in tokens (4000 = 15 x 256 + 160): all rows over sampled
+    tokens and all tokens over sampled rows, across tile boundaries."""
+    M, K, N = 4252, 256, 4000
+    say("gemm ragged large", M, K, N)
+    g = np.random.default_rng(93)
+    w = synth.q4k_blocks(95, M, M, K)
+    x16 = synth.activations_f16(95, N, N, K)
+    y = _gemm(dev(w), x16, M, K)
+    toks = np.unique(np.concatenate([[0, 3839, 3840, N - 1], g.choice(N, 60, replace=False)]))
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K, toks=toks)
+    r1 = within(y[toks], yr, S, TOL, "token sample")
+    rows = np.unique(np.concatenate([[0, 4095, 4096, M - 1], g.choice(M, 60, replace=False)]))
+    yr2, S2 = oracle.gemm(oracle.Q4_K, w, x16, M, K, rows=rows)
+    r2 = within(y[:, rows], yr2, S2, TOL, "row sample")
+    say("  max err/S", r1, r2)
+
+
 @pytest.mark.parametrize("tile_rows", [256, 128, 64])
 @pytest.mark.parametrize("M,K,N", [(256, 256, 256), (600, 1024, 520), (512, 2048, 300),
                                    (1000, 512, 1030), (130, 768, 37)])

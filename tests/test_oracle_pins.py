@@ -416,6 +416,27 @@ def test_moe_route_brute_force(orc):
     assert np.all(np.diff(wts, axis=1) <= 0)
 
 
+def test_moe_route_renormalized(orc):
+    """Renormalised top-k: the same experts, weights divided by their sum
+    (brute force in numpy; they sum to one and keep their ratios)."""
+    T, E, k = 200, 60, 6
+    logits = synth.router_logits(5, 0, T, E)
+    logits[2, :] = -1.25  # all tied: experts 0..k-1, equal weights 1/k
+    ids, wts = orc.moe_route(logits, k)
+    ids_r, wts_r = orc.moe_route(logits, k, renormalize=True)
+    assert np.array_equal(ids, ids_r)
+    l64 = logits.astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-p[t, e], e))[:k]
+        q = p[t, order]
+        assert np.allclose(wts_r[t], q / q.sum(), rtol=1e-14, atol=0)
+    assert np.allclose(wts_r.sum(axis=1), 1.0, rtol=0, atol=1e-15 * k)
+    assert np.allclose(wts_r / wts_r[:, :1], wts / wts[:, :1], rtol=1e-14, atol=0)
+    assert list(ids_r[2]) == list(range(k)) and np.allclose(wts_r[2], 1.0 / k, rtol=1e-15)
+
+
 def _silu(z):
     return z / (1.0 + np.exp(-z))
 
