@@ -351,6 +351,19 @@ def main():
                 tf = 2.0 * M * K * N / s / 1e12
                 pre["%dx%dxN%d" % (M, K, N)] = {"us": round(s * 1e6, 1), "TFLOP/s": round(tf, 1),
                                                 "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)}
+                if N == 512:
+                    # few tokens, long K: the split-K form with its own
+                    # choice of split count and a caller workspace
+                    need = gq.gq_gemm_q4k_splitk_workspace_bytes(M, K, N, 0)
+                    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+                    s = event_time(torch, stream, lambda: gq.gq_gemm_q4k_splitk(
+                        w, x16, y16, M, K, N, 0, ws, need, stream))
+                    tf = 2.0 * M * K * N / s / 1e12
+                    pre["%dx%dxN%d_splitk" % (M, K, N)] = {
+                        "us": round(s * 1e6, 1), "TFLOP/s": round(tf, 1),
+                        "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4),
+                        "splits": need // (4 * N * M)}
+                    del ws
                 del x16, y16
             del w
         extra["prefill_gemm"] = pre

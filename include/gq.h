@@ -146,6 +146,27 @@ gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, 
 gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                             int64_t N, int64_t tile_rows, void *stream);
 
+/* gq_gemm_q4k with K cut into `splits` equal runs of whole super-blocks, for
+ * products whose 256 x 256 tiles are too few to fill the device (prefill with
+ * few tokens and a long K): each run's product goes to the caller workspace
+ * as binary32 partials ws [splits][N][M], which are then summed in binary32
+ * in run order (deterministic) and rounded once to binary16 into y.  Same
+ * arguments and bound as gq_gemm_q4k otherwise (binary16 weights, binary32
+ * sums); the summation order differs, so results agree to binary32 rounding,
+ * not bit for bit.  splits = 0 lets the library choose: the divisor of K/256
+ * up to 32 with the least estimated time (rounds of tiles on this device
+ * against the traffic of the partials).
+ * ws: at least gq_gemm_q4k_splitk_workspace_bytes(M, K, N, splits) bytes,
+ * 16-byte aligned; contents on entry are ignored.  Requires M, N >= 1,
+ * K % 256 == 0, splits dividing K/256 (else GQ_ESHAPE), 0 <= splits <= 64
+ * (else GQ_EINVAL), N*K*2 < 2^31 and M*K*144/256 < 2^32 (else GQ_ESHAPE). */
+gq_status gq_gemm_q4k_splitk(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                             int64_t N, int64_t splits, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of gq_gemm_q4k_splitk (splits = 0: for the automatic
+ * choice); 0 if the arguments are invalid. */
+size_t gq_gemm_q4k_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t splits);
+
 /* Mixture-of-experts feed-forward over Q4_K experts (the grouped form):
  *   for every token t and slot s < topk, with e = topk_ids[t][s]:
  *     g = Wg_e x_t, u = Wu_e x_t            (binary16 matrix cores, binary32 sums)

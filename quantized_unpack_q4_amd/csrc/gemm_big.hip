@@ -104,7 +104,7 @@ constexpr int FN = BN / 32;
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
 constexpr int waitcnt_vm(int vm) { return waitcnt_vm_lgkm0(vm) | (15 << 8); }
 
-enum { kBigDense = 0, kBigGateUp = 1, kBigDown = 2 };
+enum { kBigDense = 0, kBigGateUp = 1, kBigDown = 2, kBigSplit = 3 };
 
 struct BigParams {
     const uint8_t *w, *w2; // Q4_K weights (gate/up: gate, up; experts stacked)
@@ -116,10 +116,14 @@ struct BigParams {
     const int32_t *sorted, *tiles, *offsets;
     int max_tiles, topk, E;
     int64_t expert_bytes;
+    int splits; // kBigSplit: K is cut into this many equal runs of whole super-blocks
 };
 
 } // namespace
 
+// MODE kBigSplit: the dense tiles, each over one of p.splits equal runs of
+// K; the binary32 partial tile goes to p.y as [split][N][M] for
+// gemm_splitk_reduce_kernel.
 // MODE kBigDense: Y = X W^T over (32 NW) x 256 tiles.  MODE kBigGateUp: a tile
 // is 16 NW rows of an expert's gate matrix and the same rows of its up matrix
 // against up to 256 of the expert's tokens, gathered through the sorted
@@ -138,16 +142,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
     const int r = lane & 31, h = lane >> 5;
-    int m0, n0, nvalid, e = 0;
-    if constexpr (MODE == kBigDense) {
+    int m0, n0, nvalid, e = 0, split = 0;
+    if constexpr (MODE == kBigDense || MODE == kBigSplit) {
         // XCD-aware tile order: the hardware deals consecutive workgroups to
         // the 8 XCDs in turn; give XCD x the contiguous tile run
-        // [x*T/8, (x+1)*T/8).
+        // [x*T/8, (x+1)*T/8) (split products: units split-major, so an XCD's
+        // run shares its splits' activation panels).
         const int b = blockIdx.x;
-        const int per = (p.tiles_total + 7) / 8;
-        const int tile = (b % 8) * per + b / 8;
-        if (tile >= p.tiles_total)
+        const int units = p.tiles_total * (MODE == kBigSplit ? p.splits : 1);
+        const int per = (units + 7) / 8;
+        int tile = (b % 8) * per + b / 8;
+        if (tile >= units)
             return;
+        if constexpr (MODE == kBigSplit) {
+            split = tile / p.tiles_total;
+            tile -= split * p.tiles_total;
+        }
         const int n_t = tile / p.tiles_m, m_t = tile % p.tiles_m;
         m0 = m_t * BM;
         n0 = n_t * BN;
@@ -165,7 +175,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
 
     const int nsb = K >> 8;
     const size_t rowb = (size_t)nsb * kQ4kBytes;
-    const int nk = K / KS;
+    // split products: this workgroup's run of K starts at super-block sb0
+    const int krun = MODE == kBigSplit ? K / p.splits : K;
+    const int sb0 = MODE == kBigSplit ? split * (krun >> 8) : 0;
+    const int nk = krun / KS;
 
     // this lane's weight row
     int wr_want = m0 + 32 * wave + r;
@@ -177,7 +190,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
     if constexpr (MODE != kBigDense)
         wbase += (size_t)e * p.expert_bytes;
     const bool wok = wr_want < M;
-    const uint8_t *wrow = wbase + (size_t)(wok ? wr_want : M - 1) * rowb;
+    const uint8_t *wrow =
+        wbase + (size_t)(wok ? wr_want : M - 1) * rowb + (size_t)sb0 * kQ4kBytes;
 
     // activation copies: copy q of wave v fills LDS 16-byte units
     // [(NQ v + q) * 64, +64), i.e. row (NQ v + q) * 8 + lane / 8, slot lane % 8,
@@ -198,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
     const uint32_t lds1 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)sX1;
     const uint32_t mb0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * (1024u * NQ));
     const uint32_t mb1 = __builtin_amdgcn_readfirstlane(lds1 + (uint32_t)wave * (1024u * NQ));
-    const uint16_t *x = p.x;
+    const uint16_t *x = p.x + (size_t)sb0 * 256;
     auto issue_x = [&](int kt, int buf) {
         const uint16_t *xk = x + (size_t)kt * KS; // wave-uniform
 #pragma unroll
@@ -359,6 +373,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
                 *reinterpret_cast<uint2 *>(hr + m) =
                     make_uint2(pack_half2(o[0], o[1]), pack_half2(o[2], o[3]));
             }
+        } else if constexpr (MODE == kBigSplit) {
+            float *dr = reinterpret_cast<float *>(p.y) + ((size_t)split * p.N + n0 + nl) * M;
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int m = m0 + 32 * wave + 8 * v4 + 4 * h;
+                if (m + 3 < M && (M & 3) == 0) {
+                    *reinterpret_cast<float4_t *>(dr + m) =
+                        float4_t{a[4 * v4], a[4 * v4 + 1], a[4 * v4 + 2], a[4 * v4 + 3]};
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (m + c < M)
+                            dr[m + c] = a[4 * v4 + c];
+                }
+            }
         } else if constexpr (MODE == kBigDown) {
             float *dr = reinterpret_cast<float *>(p.y) + (size_t)(n0 + nl) * M;
 #pragma unroll
@@ -384,6 +413,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
                 }
             }
         }
+    }
+}
+
+// Y[n][m] = binary16(sum over s = 0..splits-1 of part[s][n][m]), summed in
+// binary32 in split order (deterministic), one rounding to binary16.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float *__restrict__ part,
+                                                                 uint16_t *__restrict__ y,
+                                                                 int64_t count, int splits)
+{
+    // four outputs per thread (count is a multiple of 4: M % 4 == 0), else one
+    const bool vec = (count & 3) == 0;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (vec ? 4 : 1);
+    if (i >= count)
+        return;
+    if (vec) {
+        float4_t s = *reinterpret_cast<const float4_t *>(part + i);
+        for (int k = 1; k < splits; ++k)
+            s += *reinterpret_cast<const float4_t *>(part + (int64_t)k * count + i);
+        *reinterpret_cast<uint2 *>(y + i) = make_uint2(pack_half2(s[0], s[1]), pack_half2(s[2], s[3]));
+    } else {
+        float s = part[i];
+        for (int k = 1; k < splits; ++k)
+            s += part[(int64_t)k * count + i];
+        y[i] = (uint16_t)pack_half2(s, 0.f);
     }
 }
 
@@ -431,6 +484,74 @@ hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_
         hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 8>), dim3((unsigned)grid), dim3(512), 0, s, p);
     else
         hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 4>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+int gemm_splitk_choice(int64_t M, int64_t K, int64_t N)
+{
+    // the divisor s of K/256 (s <= 32) with the least estimated time, in
+    // units of one 64-weight step of a round of 256 x 256 tiles:
+    //   ceil(tiles*s / CUs) * (K/64)/s   (rounds of tiles, each K/s long)
+    // + 8*s*N*M / kBytesPerStep           (binary32 partials written and read)
+    // with kBytesPerStep = 1e7 bytes: a step takes about 2 us, in which HBM
+    // moves about 1e7 bytes.  Ties go to the smaller s.
+    constexpr double kBytesPerStep = 1e7;
+    if (M < 1 || N < 1 || K < 256 || K % 256 != 0)
+        return 0;
+    const int64_t tiles = dense_tiles(M, N, 256), nsb = K / 256;
+    int64_t cus = 0;
+    {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            cus = v;
+        if (cus <= 0)
+            cus = 256;
+    }
+    const double nk = (double)(K / 64);
+    auto cost = [&](int64_t s) {
+        return (double)((tiles * s + cus - 1) / cus) * nk / (double)s +
+               8.0 * (double)s * (double)N * (double)M / kBytesPerStep;
+    };
+    int best = 1;
+    double best_cost = cost(1);
+    for (int64_t s = 2; s <= 32 && s <= nsb; ++s) {
+        if (nsb % s)
+            continue;
+        const double c = cost(s);
+        if (c < best_cost - 1e-9) {
+            best = (int)s;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
+hipError_t launch_gemm_splitk(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                              int64_t N, int splits, float *ws, hipStream_t s)
+{
+    if (splits < 1 || (K / 256) % splits != 0 || !gemm_big_fits(M, K, N))
+        return hipErrorInvalidValue;
+    BigParams p{};
+    p.w = (const uint8_t *)w;
+    p.x = x;
+    p.y = ws;
+    p.M = (int)M;
+    p.K = (int)K;
+    p.N = (int)N;
+    p.splits = splits;
+    p.tiles_m = (int)((M + 255) / 256);
+    p.tiles_total = (int)dense_tiles(M, N, 256);
+    const int64_t units = (int64_t)p.tiles_total * splits;
+    const int grid = (int)((units + 7) / 8 * 8);
+    hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigSplit, 8>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int64_t count = M * N;
+    const int64_t threads = (count & 3) == 0 ? count / 4 : count;
+    hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, ws, y, count, splits);
     return hipGetLastError();
 }
 

@@ -336,6 +336,61 @@ gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64
     return gemm_common(fn, w, x, y, M, K, N, tile_rows, stream);
 }
 
+// Split count of the split-K product: `splits` as given, or the automatic choice.
+static gq_status splitk_count(const char *fn, int64_t M, int64_t K, int64_t N, int64_t splits,
+                              int *out)
+{
+    GQ_TRY(check_dim(fn, "M", M, false));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    GQ_TRY(check_dim(fn, "N", N, false));
+    if (!gq::gemm_big_fits(M, K, N) || M * (K / 256) * 144 >= ((int64_t)1 << 32))
+        return fail(GQ_ESHAPE, "%s: M = %lld, K = %lld, N = %lld is too large for the split tiles",
+                    fn, (long long)M, (long long)K, (long long)N);
+    if (splits == 0)
+        splits = gq::gemm_splitk_choice(M, K, N);
+    if (splits < 1 || splits > 64)
+        return fail(GQ_EINVAL, "%s: splits = %lld is outside [1, 64] (0: automatic)", fn,
+                    (long long)splits);
+    if ((K / 256) % splits != 0)
+        return fail(GQ_ESHAPE, "%s: splits = %lld does not divide the %lld super-blocks of K", fn,
+                    (long long)splits, (long long)(K / 256));
+    *out = (int)splits;
+    return GQ_OK;
+}
+
+size_t gq_gemm_q4k_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t splits)
+{
+    char saved[sizeof g_err];
+    memcpy(saved, g_err, sizeof g_err);
+    int s = 0;
+    const gq_status st = splitk_count("gq_gemm_q4k_splitk_workspace_bytes", M, K, N, splits, &s);
+    memcpy(g_err, saved, sizeof g_err);
+    if (st != GQ_OK)
+        return 0;
+    return (size_t)s * (size_t)N * (size_t)M * sizeof(float);
+}
+
+gq_status gq_gemm_q4k_splitk(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                             int64_t N, int64_t splits, void *ws, size_t ws_bytes, void *stream)
+{
+    static const char fn[] = "gq_gemm_q4k_splitk";
+    int s = 0;
+    GQ_TRY(splitk_count(fn, M, K, N, splits, &s));
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "y", y));
+    const size_t need = (size_t)s * (size_t)N * (size_t)M * sizeof(float);
+    if (!ws)
+        return fail(GQ_EWORKSPACE, "%s: ws is NULL (needs %zu bytes)", fn, need);
+    if (!aligned16(ws))
+        return fail(GQ_EALIGN, "%s: ws (%p) is not 16-byte aligned", fn, ws);
+    if (ws_bytes < need)
+        return fail(GQ_EWORKSPACE, "%s: ws_bytes = %zu is below the required %zu (splits = %d)", fn,
+                    ws_bytes, need, s);
+    return launched(fn, gq::launch_gemm_splitk(w, x, y, M, K, N, s, (float *)ws,
+                                               (hipStream_t)stream));
+}
+
 size_t gq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk)
 {
     size_t off[7];

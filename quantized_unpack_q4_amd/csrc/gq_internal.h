@@ -53,6 +53,14 @@ bool gemm_big_fits(int64_t M, int64_t K, int64_t N);
 int gemm_big_choice(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, int bm, hipStream_t s);
+// Split-K form of the 256 x 256 large-tile product: `splits` runs of K/splits
+// (whole super-blocks) into binary32 partials ws [splits][N][M], then a fixed
+// order sum rounded to binary16.  gemm_splitk_choice: the split count that
+// needs the fewest rounds of tiles on this device (1 when splitting does not
+// help).
+int gemm_splitk_choice(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_splitk(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                              int64_t N, int splits, float *ws, hipStream_t s);
 
 // Mixture-of-experts pieces; ws_off are the region offsets of gq_moe_workspace_offsets.
 struct MoeArgs {

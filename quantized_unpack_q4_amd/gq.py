@@ -24,7 +24,8 @@ MAX_BATCH = 16
 
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
-    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemm_q4k", "gq_gemm_q4k_tiles",
+    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemm_q4k", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
+    "gq_gemm_q4k_splitk_workspace_bytes",
     "gq_moe_gemm_q4k", "gq_moe_route",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
         L.gq_gemv_q4k_multi_batched.argtypes = [vp, vp, i64, vp]
         L.gq_gemm_q4k.restype = st
         L.gq_gemm_q4k.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.gq_gemm_q4k_splitk.restype = st
+        L.gq_gemm_q4k_splitk.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        L.gq_gemm_q4k_splitk_workspace_bytes.restype = sz
+        L.gq_gemm_q4k_splitk_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.gq_gemm_q4k_tiles.restype = st
         L.gq_gemm_q4k_tiles.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.gq_moe_gemm_q4k.restype = st
@@ -191,6 +196,17 @@ def gq_gemm_q4k(w, x, y, M, K, N, stream=None):
 def gq_gemm_q4k_tiles(w, x, y, M, K, N, tile_rows, stream=None):
     _check(lib().gq_gemm_q4k_tiles(_ptr(w), _ptr(x), _ptr(y), M, K, N, tile_rows,
                                    _stream(stream)))
+
+
+def gq_gemm_q4k_splitk_workspace_bytes(M, K, N, splits=0) -> int:
+    return lib().gq_gemm_q4k_splitk_workspace_bytes(M, K, N, splits)
+
+
+def gq_gemm_q4k_splitk(w, x, y, M, K, N, splits, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gq_gemm_q4k_splitk(_ptr(w), _ptr(x), _ptr(y), M, K, N, splits, _ptr(ws),
+                                    ws_bytes, _stream(stream)))
 
 
 def gq_moe_workspace_bytes(T, H, I, E, topk) -> int:

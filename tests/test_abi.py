@@ -109,6 +109,25 @@ def test_moe_workspace_and_refusals(L):
     assert f(*([None] * 7), 0, H, I, E, k, None, 0, None) == 0
 
 
+def test_gemm_splitk_workspace_and_refusals(L):
+    f, wsb = L.gq_gemm_q4k_splitk, L.gq_gemm_q4k_splitk_workspace_bytes
+    M, K, N = 4096, 14336, 512
+    assert wsb(M, K, N, 8) == 8 * N * M * 4
+    assert wsb(M, K, N, 5) == 0 and wsb(M, K, N, 65) == 0 and wsb(M, 1000, N, 2) == 0
+    need = wsb(M, K, N, 8)
+    for args, code in (((M, K, N, 5, FAKE, need), "GQ_ESHAPE"),
+                       ((M, K, N, 65, FAKE, need), "GQ_EINVAL"),
+                       ((M, K, N, -1, FAKE, need), "GQ_EINVAL"),
+                       ((M, K, N, 8, None, need), "GQ_EWORKSPACE"),
+                       ((M, K, N, 8, FAKE, need - 1), "GQ_EWORKSPACE"),
+                       ((M, K, N, 8, MISALIGNED, need), "GQ_EALIGN"),
+                       ((0, K, N, 8, FAKE, need), "GQ_EINVAL"),
+                       ((M, 300, N, 1, FAKE, need), "GQ_ESHAPE"),
+                       ((M, K, 1 << 20, 8, FAKE, 1 << 62), "GQ_ESHAPE")):
+        s, m = status_and_msg(L, f(FAKE, FAKE, FAKE, *args, None))
+        assert s == code and "gq_gemm_q4k_splitk" in m, (args, s, m)
+
+
 def test_moe_route_refusals(L):
     f = L.gq_moe_route
     for T, E, k, code in ((4, 257, 8, "GQ_EINVAL"), (4, 64, 65, "GQ_EINVAL"), (4, 64, 0, "GQ_EINVAL"),

@@ -141,3 +141,64 @@ def test_gemm_deterministic(N):
     a = _gemm(w, x16, M, K)
     b = _gemm(w, x16, M, K)
     assert np.array_equal(a, b)
+
+
+def _gemm_splitk(w_d, x16, M, K, splits):
+    torch = torch_cuda()
+    N = x16.shape[0]
+    y = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    need = gq.gq_gemm_q4k_splitk_workspace_bytes(M, K, N, splits)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    gq.gq_gemm_q4k_splitk(w_d, dev(x16), y, M, K, N, splits, ws)
+    return half_bits(y).view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4])
+@pytest.mark.parametrize("M,K,N", [(600, 1024, 300), (256, 1024, 256), (130, 2048, 37)])
+def test_gemm_splitk_parity(M, K, N, splits):
+    """Split-K product at sizes the oracle computes in full: ragged M and N,
+    1, 2 and 4 runs of K."""
+    say("gemm splitk", M, K, N, splits)
+    w = synth.q4k_blocks(96, M, M, K)
+    x16 = synth.activations_f16(96, N, N, K)
+    y = _gemm_splitk(dev(w), x16, M, K, splits)
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K)
+    r = within(y, yr, S, TOL, "gemm splitk %d %dx%dx%d" % (splits, M, K, N))
+    say("  max err/S", r)
+
+
+@pytest.mark.parametrize("M,K", [(4096, 14336), (14336, 4096)])
+def test_gemm_splitk_prefill_sampled(M, K):
+    """The 512-token prefill shapes at full size with the automatic split
+    count: sampled rows over all tokens, all rows over sampled tokens."""
+    N = 512
+    say("gemm splitk full", M, K, N)
+    g = np.random.default_rng(97)
+    w = synth.q4k_blocks(3, M, M, K)
+    x16 = synth.activations_f16(3, N, N, K)
+    y = _gemm_splitk(dev(w), x16, M, K, 0)
+    rows = np.sort(g.choice(M, 24, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K, rows=rows)
+    r1 = within(y[:, rows], yr, S, TOL, "rows sample")
+    t2 = np.array([0, 255, 256, N - 1])
+    yr2, S2 = oracle.gemm(oracle.Q4_K, w, x16, M, K, toks=t2)
+    r2 = within(y[t2], yr2, S2, TOL, "token sample")
+    say("  max err/S", r1, r2)
+
+
+def test_gemm_splitk_one_hot_exact():
+    """One-hot activation rows read out the binary16 weights exactly through
+    the split form too: only one run holds the non-zero product, the others
+    add exact zeros."""
+    M, K = 256, 1024
+    w = synth.q4k_blocks(98, 0, M, K)
+    cols = [0, 255, 256, 700, 1023]
+    x16 = np.zeros((len(cols), K), np.float16)
+    for i, c in enumerate(cols):
+        x16[i, c] = 1.0
+    y = _gemm_splitk(dev(w), x16, M, K, 4)
+    _, w16 = oracle.dequant(oracle.Q4_K, w, M, K)
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i].astype(np.float16).view(np.uint16), w16[:, c]), c
