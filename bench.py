@@ -235,7 +235,7 @@ def main():
                          "reference kernel for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
+        print("bench.py measures one GPU: the library runs the hot path on a single MI355X "
               "and has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
