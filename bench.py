@@ -338,6 +338,32 @@ def main():
                 "rotated_us": round(rotated * 1e6, 2),
                 "rotated_GB/s": round(q4k_bytes(M, K) / rotated / 1e9, 1),
                 "rotated_over_MB": round(len(mats) * q4k_bytes(M, K) / 1e6, 1)}
+        # a layer's gate and up products with the SwiGLU epilogue in one launch
+        # (gq_gemv_q4k_swiglu), rotated over the 32 layers' pairs, beside the
+        # same two products as two launches
+        M, K = 14336, 4096
+        gates = [m[4] for m in stack.mats if m[0] == "gate"]
+        ups = [m[4] for m in stack.mats if m[0] == "up"]
+        x = torch.from_numpy(synth.activations_f32(1, 2 * M, 1, K)).cuda()
+        hbuf = torch.empty((M,), dtype=torch.float32, device="cuda")
+        ybuf = torch.empty((2, M), dtype=torch.float32, device="cuda")
+        it = {"i": 0}
+
+        def fused():
+            i = it["i"] % len(gates)
+            it["i"] += 1
+            gq.gq_gemv_q4k_swiglu(gates[i], ups[i], x, hbuf, M, K, stream)
+
+        def separate():
+            i = it["i"] % len(gates)
+            it["i"] += 1
+            gq.gq_gemv_q4k(gates[i], x, ybuf[0], M, K, 1, stream)
+            gq.gq_gemv_q4k(ups[i], x, ybuf[1], M, K, 1, stream)
+        sf = event_time(torch, stream, fused, reps=len(gates), warmup=len(gates))
+        ss = event_time(torch, stream, separate, reps=len(gates), warmup=len(gates))
+        extra["gemv_swiglu_%dx%d_b1" % (M, K)] = {
+            "fused_us": round(sf * 1e6, 2), "fused_GB/s": round(2 * q4k_bytes(M, K) / sf / 1e9, 1),
+            "two_launches_us": round(ss * 1e6, 2)}
         del stack
         torch.cuda.empty_cache()
         # prefill matrix products

@@ -118,6 +118,19 @@ gq_status gq_gemv_q4k_multi_plan(const gq_gemv_desc *descs, int64_t n, void *tab
                                  size_t table_bytes);
 gq_status gq_gemv_q4k_multi(const void *table, const void *table_dev, void *stream);
 
+/* The gate and up products of a feed-forward layer with the SwiGLU epilogue,
+ * batch 1, in one launch (the pages credit fused projection kernels, page
+ * "Building a Rust Inference Engine That Matches Llama.cpp", section "Where
+ * the wins came from"):
+ *   h[r] = silu(g_r) * u_r,  g = W_gate x,  u = W_up x,  silu(z) = z / (1 + e^-z)
+ * with g and u computed as by gq_gemv_q4k (binary32 activations and sums) and
+ * the epilogue in binary32.  w_gate, w_up: M x K Q4_K matrices.  x: [K]
+ * binary32.  h: [M] binary32.  Requires K % 256 == 0, 256 <= K <= 16384,
+ * 0 <= M <= 2^29 (M = 0 launches nothing), 16-byte aligned pointers; h must
+ * not overlap the inputs. */
+gq_status gq_gemv_q4k_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,
+                             int64_t M, int64_t K, void *stream);
+
 /* The same planned products at batch B (1 <= B <= 16): descriptor i's x is
  * [B][K] and y is [B][M] (row-major), y_i[b] = W_i x_i[b].  B = 1 is
  * gq_gemv_q4k_multi.  For B >= 2 the products run on the matrix cores (the

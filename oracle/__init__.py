@@ -67,6 +67,7 @@ def lib():
         L.orc_gemv_separate.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp]
         L.orc_gemm.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
         L.orc_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, ctypes.c_int]
+        L.orc_swiglu.argtypes = [vp, vp, i64, vp]
         L.orc_moe_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                   vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -191,6 +192,17 @@ def gemm(fmt: int, w, x16, M: int, K: int, rows=None, toks=None):
     S = np.empty((nt, nr), np.float64)
     lib().orc_gemm(fmt, _p(w), _p(x16), M, K, N, _p(rows), nr, _p(toks), nt, _p(y), _p(S))
     return y, S
+
+
+def swiglu(g, u):
+    """h = silu(g) * u elementwise in binary64 (silu(z) = z / (1 + e^-z))."""
+    g = np.ascontiguousarray(np.asarray(g, dtype=np.float64))
+    u = np.ascontiguousarray(np.asarray(u, dtype=np.float64))
+    if g.shape != u.shape:
+        raise ValueError("g and u differ in shape")
+    h = np.empty_like(g)
+    lib().orc_swiglu(_p(g), _p(u), g.size, _p(h))
+    return h
 
 
 def moe_route(logits, topk: int, renormalize: bool = False):

@@ -364,6 +364,14 @@ void orc_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, int3
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* SwiGLU of a feed-forward layer's gate and up products: h = silu(g) * u,
+ * silu(z) = z / (1 + e^-z), in binary64, elementwise over n values. */
+void orc_swiglu(const double *g, const double *u, int64_t n, double *h)
+{
+    for (int64_t i = 0; i < n; i++)
+        h[i] = silu(g[i]) * u[i];
+}
+
 /* Dense product of one expert's weight matrix (R rows of C columns, Q4_K)
  * with a binary64 vector. */
 static void expert_matvec(const uint8_t *w, int64_t R, int64_t C, const double *v, double *out,

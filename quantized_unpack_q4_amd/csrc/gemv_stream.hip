@@ -108,9 +108,14 @@ __device__ __forceinline__ uint32_t word8(const uint4 &a, const uint4 &b, int i)
 
 // R row groups per wave step, NB weight-load buffers (loads run NB - 1 steps
 // ahead of the arithmetic), W waves per workgroup.
-template <int R, int NB, int W>
+// PAIR: one entry whose rows are the pairs (gate row r, up row r) of two
+// matrices with the same shape, e.w and w2; the row-group layout puts both
+// rows of a pair in one wave, so h[r] = silu(gate_r x) * (up_r x) is formed in
+// registers and e.y receives h (M values).  Ranges split at pair granularity.
+template <int R, int NB, int W, bool PAIR = false>
 __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
-    const GemvEntry *__restrict__ table, GemvEntry inline0, int n, long long total)
+    const GemvEntry *__restrict__ table, GemvEntry inline0, int n, long long total,
+    const uint8_t *__restrict__ w2)
 {
     constexpr int kR = R;
     constexpr int kThreads = 64 * W;
@@ -207,7 +212,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
         for (int r = 0; r < kR; ++r) {
             const int row = row0 + rpg * r + rsub;
             const int rc = row < r_end ? row : r_end - 1;
-            const uint8_t *blk = e.w + (size_t)rc * rowb + (size_t)sc * kQ4kBytes;
+            const uint8_t *base = PAIR && (rc & 1) ? w2 : e.w;
+            const size_t vr = PAIR ? (size_t)(rc >> 1) : (size_t)rc;
+            const uint8_t *blk = base + vr * rowb + (size_t)sc * kQ4kBytes;
             f[r].hd = gload16(blk);
             f[r].a0 = gload16(blk + 16 + 32 * p);
             f[r].a1 = gload16(blk + 32 + 32 * p);
@@ -229,8 +236,11 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
         nsb = e.K >> 8;
         rowb = (long long)nsb * kQ4kBytes;
         const long long rel_lo = lo - e.byte_begin, rel_hi = hi - e.byte_begin;
-        const int r_lo = rel_lo <= 0 ? 0 : (int)min((long long)e.M, (rel_lo + rowb - 1) / rowb);
-        r_end = (int)min((long long)e.M, (rel_hi + rowb - 1) / rowb);
+        // rows (pairs of rows) are owned whole: unit of `gr` rows
+        const int gr = PAIR ? 2 : 1;
+        const long long mrows = (long long)gr * e.M, unit = gr * rowb;
+        const int r_lo = rel_lo <= 0 ? 0 : (int)min(mrows, gr * ((rel_lo + unit - 1) / unit));
+        r_end = (int)min(mrows, gr * ((rel_hi + unit - 1) / unit));
         if (r_lo >= r_end)
             continue;
         // 32 lanes per row (16 super-blocks per step), or 16 lanes per row
@@ -359,7 +369,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
                     const float v = rowsum16(acc[r]);
                     const float q0 = lane_value(v, 0), q1 = lane_value(v, 16);
                     const float q2 = lane_value(v, 32), q3 = lane_value(v, 48);
-                    if (rpg == 2) {
+                    if (PAIR) {
+                        // rows come in (gate, up) pairs: rpg 2 holds one
+                        // pair per row group, rpg 4 two
+                        const int vrow = row0 + rpg * r + 2 * lane;
+                        const float g = rpg == 2 ? q0 + q1 : lane == 0 ? q0 : q2;
+                        const float u = rpg == 2 ? q2 + q3 : lane == 0 ? q1 : q3;
+                        if (lane < rpg / 2 && vrow < r_end)
+                            e.y[vrow >> 1] = silu(g) * u;
+                    } else if (rpg == 2) {
                         const int row = row0 + 2 * r + lane;
                         if (lane < 2 && row < r_end)
                             e.y[row] = lane == 0 ? q0 + q1 : q2 + q3;
@@ -431,7 +449,18 @@ hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inlin
                               long long total_bytes, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL((gemv_q4k_stream_kernel<kR, 2, 4>), dim3((unsigned)grid), dim3(256), 0, s,
-                       table_dev, inline0, n, total_bytes);
+                       table_dev, inline0, n, total_bytes, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,
+                              int64_t M, int64_t K, hipStream_t s)
+{
+    const GemvEntry e{(const uint8_t *)w_gate, x, h, (int)M, (int)K, 0};
+    const long long total = 2LL * M * (K / 256) * kQ4kBytes;
+    const int grid = gemv_stream_grid(total, gemv_stream_tiles(2 * M, K));
+    hipLaunchKernelGGL((gemv_q4k_stream_kernel<kR, 2, 4, true>), dim3((unsigned)grid), dim3(256),
+                       0, s, nullptr, e, 1, total, (const uint8_t *)w_up);
     return hipGetLastError();
 }
 

@@ -451,6 +451,25 @@ gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_do
     return launched(fn, gq::launch_moe(a, (hipStream_t)stream));
 }
 
+gq_status gq_gemv_q4k_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,
+                             int64_t M, int64_t K, void *stream)
+{
+    static const char fn[] = "gq_gemv_q4k_swiglu";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    if (K > gq::GemvStreamMaxK)
+        return fail(GQ_ESHAPE, "%s: K = %lld exceeds %d", fn, (long long)K, gq::GemvStreamMaxK);
+    if (M > ((int64_t)1 << 29))
+        return fail(GQ_ESHAPE, "%s: M = %lld exceeds 2^29 rows", fn, (long long)M);
+    if (M == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w_gate", w_gate));
+    GQ_TRY(check_ptr(fn, "w_up", w_up));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "h", h));
+    return launched(fn, gq::launch_gemv_swiglu(w_gate, w_up, x, h, M, K, (hipStream_t)stream));
+}
+
 gq_status gq_moe_route(const float *logits, int32_t *topk_ids, float *topk_w, int64_t T,
                        int64_t E, int64_t topk, int64_t renormalize, void *stream)
 {

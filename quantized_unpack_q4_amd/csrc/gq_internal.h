@@ -35,6 +35,11 @@ int gemv_stream_grid(long long total_bytes, long long tiles);
 hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
                               long long total_bytes, int grid, hipStream_t s);
 
+// h[r] = silu(w_gate_r x) * (w_up_r x), batch 1, both M x K Q4_K matrices
+// streamed by one launch of the batch-1 kernel (K <= GemvStreamMaxK).
+hipError_t launch_gemv_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,
+                              int64_t M, int64_t K, hipStream_t s);
+
 // Small-batch (2 <= B <= 16) products on the matrix cores, over a table of
 // entries (or the single entry inline0 when table_dev is null); blocks of 128
 // rows are dealt to workgroups by byte ranges of the packed weights.

@@ -24,7 +24,7 @@ MAX_BATCH = 16
 
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
-    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemm_q4k", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
+    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemm_q4k", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
     "gq_gemm_q4k_splitk_workspace_bytes",
     "gq_moe_gemm_q4k", "gq_moe_route",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.gq_gemv_q4k_multi_batched.argtypes = [vp, vp, i64, vp]
         L.gq_gemm_q4k.restype = st
         L.gq_gemm_q4k.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.gq_gemv_q4k_swiglu.restype = st
+        L.gq_gemv_q4k_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.gq_gemm_q4k_splitk.restype = st
         L.gq_gemm_q4k_splitk.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.gq_gemm_q4k_splitk_workspace_bytes.restype = sz
@@ -196,6 +198,11 @@ def gq_gemm_q4k(w, x, y, M, K, N, stream=None):
 def gq_gemm_q4k_tiles(w, x, y, M, K, N, tile_rows, stream=None):
     _check(lib().gq_gemm_q4k_tiles(_ptr(w), _ptr(x), _ptr(y), M, K, N, tile_rows,
                                    _stream(stream)))
+
+
+def gq_gemv_q4k_swiglu(w_gate, w_up, x, h, M, K, stream=None):
+    _check(lib().gq_gemv_q4k_swiglu(_ptr(w_gate), _ptr(w_up), _ptr(x), _ptr(h), M, K,
+                                    _stream(stream)))
 
 
 def gq_gemm_q4k_splitk_workspace_bytes(M, K, N, splits=0) -> int:

@@ -128,6 +128,19 @@ def test_gemm_splitk_workspace_and_refusals(L):
         assert s == code and "gq_gemm_q4k_splitk" in m, (args, s, m)
 
 
+def test_gemv_swiglu_refusals(L):
+    f = L.gq_gemv_q4k_swiglu
+    for M, K, code in ((16, 300, "GQ_ESHAPE"), (16, 16640, "GQ_ESHAPE"), (-1, 256, "GQ_EINVAL"),
+                       ((1 << 29) + 1, 256, "GQ_ESHAPE")):
+        s, m = status_and_msg(L, f(FAKE, FAKE, FAKE, FAKE, M, K, None))
+        assert s == code and "gq_gemv_q4k_swiglu" in m, (M, K, s, m)
+    s, m = status_and_msg(L, f(FAKE, None, FAKE, FAKE, 16, 256, None))
+    assert s == "GQ_EINVAL" and "w_up" in m
+    s, m = status_and_msg(L, f(FAKE, FAKE, FAKE, MISALIGNED, 16, 256, None))
+    assert s == "GQ_EALIGN" and "h" in m
+    assert f(None, None, None, None, 0, 256, None) == 0
+
+
 def test_moe_route_refusals(L):
     f = L.gq_moe_route
     for T, E, k, code in ((4, 257, 8, "GQ_EINVAL"), (4, 64, 65, "GQ_EINVAL"), (4, 64, 0, "GQ_EINVAL"),

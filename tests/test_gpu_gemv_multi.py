@@ -36,6 +36,10 @@ def _check(table, host_in, shapes, rows_cap=None, what=""):
     g = np.random.default_rng(5)
     for (w, x), (_, _, y, M, K), (M2, K2) in zip(host_in, table.items, shapes):
         yg = host(y)
+        # outputs start as NaN: every row must be written by exactly the
+        # workgroup whose byte range holds its first byte
+        assert np.isfinite(yg).all(), "%s %dx%d: rows %s not written" % (
+            what, M, K, np.argwhere(~np.isfinite(yg))[:5, -1].tolist())
         rows = None
         if rows_cap is not None and M > rows_cap:
             rows = np.sort(g.choice(M, rows_cap, replace=False))
@@ -208,3 +212,31 @@ def test_multi_batched_decode_layer_full_size(B):
     tab.run()
     r = _check(tab, host_in, shapes, rows_cap=48, what="layer B=%d" % B)
     say("multi batched layer B=%d max err/S" % B, r)
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (300, 1024), (1000, 768), (37, 14336), (14336, 4096)])
+def test_gemv_swiglu(M, K):
+    """Gate and up products with the SwiGLU epilogue in one launch: every
+    output against h = silu(g) * u from the oracle's binary64 products.
+    Bound: the 1e-5 * S bounds of g and u carried through silu(g) * u
+    (|silu'| <= 1.1), plus the binary32 epilogue: the exponential's argument
+    rounds once (|g| * 2^-24 relative in e^-g) and exp, the division and the
+    product add a few ulp, (4 + |g|) * 2^-23 relative in all."""
+    torch = torch_cuda()
+    say("swiglu", M, K)
+    wg = synth.q4k_blocks(52, 2 * M, M, K)
+    wu = synth.q4k_blocks(52, 2 * M + 1, M, K)
+    x = synth.activations_f32(52, M, 1, K)
+    h = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q4k_swiglu(dev(wg), dev(wu), dev(x), h, M, K)
+    hg = host(h).astype(np.float64)
+    g, Sg = oracle.gemv(oracle.Q4_K, wg, x, M, K)
+    u, Su = oracle.gemv(oracle.Q4_K, wu, x, M, K)
+    g, Sg, u, Su = g[0], Sg[0], u[0], Su[0]
+    hr = oracle.swiglu(g, u)
+    sg = oracle.swiglu(g, np.ones_like(g))
+    bound = TOL * (1.1 * Sg * np.abs(u) + np.abs(sg) * Su) + (4 + np.abs(g)) * 2.0 ** -23 * np.abs(hr)
+    err = np.abs(hg - hr)
+    assert np.isfinite(hg).all()
+    assert np.all(err <= bound), "swiglu %dx%d: worst %.3g of bound" % (M, K, (err / bound).max())
+    say("  worst err/bound", (err / bound).max())

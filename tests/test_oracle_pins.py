@@ -437,6 +437,24 @@ def test_moe_route_renormalized(orc):
     assert list(ids_r[2]) == list(range(k)) and np.allclose(wts_r[2], 1.0 / k, rtol=1e-15)
 
 
+def test_swiglu_closed_forms(orc):
+    """h = silu(g) * u: silu(0) = 0, silu(1) = 1/(1+e^-1) (the logistic function
+    at 1, 0.7310585786300049), silu(-1) = -1/(1+e) (0.2689414213699951 negated),
+    silu(2) = 2/(1+e^-2) (1.7615941559557646), silu(z) - silu(-z) = z, silu
+    of a large positive z is z and of a large negative z is (-)0; linear in u."""
+    g = np.array([0.0, 1.0, -1.0, 2.0, 40.0, -800.0, 0.5, -0.5, 3.25, -3.25])
+    u = np.array([5.0, 1.0, 1.0, 1.0, 0.25, 7.0, 1.0, 1.0, -2.0, -2.0])
+    h = orc.swiglu(g, u)
+    assert h[0] == 0.0
+    assert abs(h[1] - 0.7310585786300049) <= 2e-16
+    assert abs(h[2] + 0.2689414213699951) <= 2e-16
+    assert abs(h[3] - 1.7615941559557646) <= 4e-16
+    assert h[4] == 10.0 and h[5] == 0.0 and np.isfinite(h).all()
+    assert abs((h[6] - h[7]) - 0.5) <= 1e-15 and abs((h[8] - h[9]) / -2.0 - 3.25) <= 1e-15
+    h3 = orc.swiglu(g, 3.0 * u)
+    assert np.allclose(h3, 3.0 * h, rtol=1e-15, atol=0)
+
+
 def _silu(z):
     return z / (1.0 + np.exp(-z))
 
