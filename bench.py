@@ -392,6 +392,16 @@ def main():
                     del ws
                 del x16, y16
             del w
+        # the same product over Q8_0 weights (the LDS-tile kernel)
+        M, K, N = 14336, 4096, 4096
+        wq8 = torch.from_numpy(synth.q8_0_blocks(PREFILL_WORKLOAD, M, M, K)).cuda()
+        x16 = torch.from_numpy(synth.activations_f16(PREFILL_WORKLOAD, N, N, K)).cuda()
+        y16 = torch.empty((N, M), dtype=torch.float16, device="cuda")
+        s = event_time(torch, stream, lambda: gq.gq_gemm_q8_0(wq8, x16, y16, M, K, N, stream))
+        tf = 2.0 * M * K * N / s / 1e12
+        pre["q8_0_%dx%dxN%d" % (M, K, N)] = {"us": round(s * 1e6, 1), "TFLOP/s": round(tf, 1),
+                                             "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)}
+        del wq8, x16, y16
         extra["prefill_gemm"] = pre
         # achievable ceilings measured beside the kernels: a plain 1 GiB device
         # copy (read + write streaming) and the vendor library's binary16 product

@@ -148,6 +148,14 @@ gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, in
 gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                       int64_t N, void *stream);
 
+/* The same product over Q8_0 weights (M rows of K/32 blocks):
+ *   Y[n][r] = binary16( sum_k X[n][k] * w16[r][k] ),  w16 = binary16(d * q)
+ * accumulated in binary32 (d * q is exact in binary32; one rounding to
+ * binary16).  Requires K % 64 == 0 (the kernel takes two blocks per step;
+ * GQ_ESHAPE otherwise), N <= 2^21. */
+gq_status gq_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                       int64_t N, void *stream);
+
 /* gq_gemm_q4k with the kernel family pinned instead of chosen from the shape:
  * tile_rows = 0 is the automatic choice of gq_gemm_q4k, 64 the small-tile
  * kernels (64 or 128 weight rows per tile, chosen from the shape), 128 and 256

@@ -23,6 +23,10 @@
 namespace gq {
 
 enum { kModeGemm = 0, kModeGateUp = 1, kModeDown = 2 };
+// weight formats: Q4_K super-blocks, or Q8_0 blocks (plain product only; a
+// 64-weight step is two 34-byte blocks, 68 bytes that start 4-byte aligned in
+// every row when K % 64 == 0)
+enum { kFmtQ4K = 0, kFmtQ8 = 1 };
 
 struct GemmParams {
     const uint8_t *w;      // Q4_K weights (gate for the gate/up product); experts stacked
@@ -40,9 +44,10 @@ struct GemmParams {
 };
 
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, int FMT = kFmtQ4K>
 __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
 {
+    static_assert(FMT == kFmtQ4K || MODE == kModeGemm, "Q8_0 only for the plain product");
     constexpr int KS = 64;        // weights per K step
     constexpr int LDR = KS + 8;   // LDS row stride in halves (144 bytes, keeps 16-byte alignment)
     constexpr int NW = MODE == kModeGateUp ? 2 : 1;
@@ -62,7 +67,15 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
     const int wave = tid >> 6;
     const int K = p.K;
     const int nsb = K >> 8;
-    const int64_t row_bytes = (int64_t)nsb * kQ4kBytes;
+    const int64_t row_bytes = FMT == kFmtQ8 ? (int64_t)(K / 32) * 34 : (int64_t)nsb * kQ4kBytes;
+    // Q8_0: this thread's 64/TPR weights of a step start at weight w8 of the
+    // step, inside block w8/32; their quant bytes start at byte q8 of the
+    // step's 68 bytes (dword q8/4, byte shift q8%4, 0 or 2), the block scale
+    // sits in the low or high half of dword d8w
+    constexpr int QB8 = 64 / TPR;
+    const int w8 = (tid % TPR) * QB8;
+    const int q8 = 34 * (w8 >> 5) + 2 + (w8 & 31);
+    const int d8w = (34 * (w8 >> 5)) >> 2, d8hi = (34 * (w8 >> 5)) & 3 ? 16 : 0;
 
     // ---- tile coordinates ----
     const int m0 = blockIdx.x * BM;
@@ -115,8 +128,27 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
     uint4 rh[NW];
     uint32_t rq[NW][QB / 4];
     uint4 rx[XU];
+    uint32_t r8[QB8 / 4 + 1], r8d; // Q8_0: quant dwords (one extra for the shift), scale dword
 
     auto load_step = [&](int kt) {
+        if constexpr (FMT == kFmtQ8) {
+            if (drow_ok) {
+                const uint32_t *st = reinterpret_cast<const uint32_t *>(wrowA + (int64_t)kt * 68);
+#pragma unroll
+                for (int i = 0; i <= QB8 / 4; ++i)
+                    r8[i] = st[min((q8 >> 2) + i, 16)]; // dword 16: the step's last
+                r8d = st[d8w];
+            } else {
+#pragma unroll
+                for (int i = 0; i <= QB8 / 4; ++i)
+                    r8[i] = 0u;
+                r8d = 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < XU; ++u)
+                rx[u] = xrow[u] ? ld16(xrow[u] + kt * KS + 8 * xchunk[u]) : make_uint4(0, 0, 0, 0);
+            return;
+        }
         const int s = kt >> 2, g = kt & 3;
 #pragma unroll
         for (int v = 0; v < NW; ++v) {
@@ -150,6 +182,32 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
     };
 
     auto store_step = [&](int kt, int buf) {
+        if constexpr (FMT == kFmtQ8) {
+            // w = binary16(d * q): exact in binary32, one rounding to binary16.
+            // The signed byte q is taken as (q ^ 0x80) - 128 from an unsigned
+            // byte conversion (exact), not as a sign-extended integer: the
+            // compiler folds the latter into an unsigned conversion of the
+            // sign-extended byte here, which turns negative quants into ~2^32.
+            const float d = half_to_float((r8d >> d8hi) & 0xffffu);
+            uint32_t hw[QB8 / 2];
+#pragma unroll
+            for (int i = 0; i < QB8 / 4; ++i) {
+                const uint32_t D = __builtin_amdgcn_alignbyte(r8[i + 1], r8[i], q8 & 3) ^ 0x80808080u;
+                hw[2 * i] = pack_half2(d * (ubyte_to_float<0>(D) - 128.f),
+                                       d * (ubyte_to_float<1>(D) - 128.f));
+                hw[2 * i + 1] = pack_half2(d * (ubyte_to_float<2>(D) - 128.f),
+                                           d * (ubyte_to_float<3>(D) - 128.f));
+            }
+            _Float16 *dst = &sW[buf][0][drow][w8];
+#pragma unroll
+            for (int i = 0; i < QB8 / 8; ++i)
+                *reinterpret_cast<uint4 *>(dst + 8 * i) =
+                    make_uint4(hw[4 * i], hw[4 * i + 1], hw[4 * i + 2], hw[4 * i + 3]);
+#pragma unroll
+            for (int u = 0; u < XU; ++u)
+                *reinterpret_cast<uint4 *>(&sX[buf][xr[u]][8 * xchunk[u]]) = rx[u];
+            return;
+        }
         const int g = kt & 3;
 #pragma unroll
         for (int v = 0; v < NW; ++v) {
@@ -265,12 +323,33 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
         }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int FMT = kFmtQ4K>
 static hipError_t gemm_go(const GemmParams &p, hipStream_t s)
 {
     dim3 grid((p.M + BM - 1) / BM, (p.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_q4k_kernel<BM, BN, WM, WN, kModeGemm>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_q4k_kernel<BM, BN, WM, WN, kModeGemm, FMT>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                            int64_t N, hipStream_t s)
+{
+    GemmParams p{};
+    p.w = (const uint8_t *)w;
+    p.x = x;
+    p.y = y;
+    p.M = (int)M;
+    p.K = (int)K;
+    p.N = (int)N;
+    if (N <= 64)
+        return gemm_go<128, 32, 4, 1, kFmtQ8>(p, s);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t t64x128 = ((M + 63) / 64) * ((N + 127) / 128);
+    if (t128 >= 448)
+        return gemm_go<128, 128, 2, 2, kFmtQ8>(p, s);
+    if (t64x128 >= 384)
+        return gemm_go<64, 128, 1, 4, kFmtQ8>(p, s);
+    return gemm_go<64, 64, 2, 2, kFmtQ8>(p, s);
 }
 
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,

@@ -326,6 +326,24 @@ gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, 
     return gemm_common("gq_gemm_q4k", w, x, y, M, K, N, 0, stream);
 }
 
+gq_status gq_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                       int64_t N, void *stream)
+{
+    static const char fn[] = "gq_gemm_q8_0";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 64));
+    GQ_TRY(check_dim(fn, "N", N, true));
+    if (N > ((int64_t)1 << 21))
+        return fail(GQ_ESHAPE, "%s: N = %lld exceeds the supported maximum %lld", fn,
+                    (long long)N, (long long)1 << 21);
+    if (M == 0 || N == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "y", y));
+    return launched(fn, gq::launch_gemm_q8_0(w, x, y, M, K, N, (hipStream_t)stream));
+}
+
 gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                             int64_t N, int64_t tile_rows, void *stream)
 {

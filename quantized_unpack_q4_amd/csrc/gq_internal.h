@@ -49,6 +49,9 @@ hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0
 
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s);
+// The same product over Q8_0 weights (K % 64 == 0), on the LDS-tile kernel.
+hipError_t launch_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                            int64_t N, hipStream_t s);
 // Large-tile matrix product (prefill): tiles of bm = 256 or 128 weight rows by
 // 256 activation rows.  gemm_big_fits: the shape fits the kernel's 32-bit
 // activation offsets.  gemm_big_choice: the tile height the automatic

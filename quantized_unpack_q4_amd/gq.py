@@ -24,7 +24,7 @@ MAX_BATCH = 16
 
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
-    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemm_q4k", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
+    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
     "gq_gemm_q4k_splitk_workspace_bytes",
     "gq_moe_gemm_q4k", "gq_moe_route",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.gq_gemm_q4k_splitk.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.gq_gemm_q4k_splitk_workspace_bytes.restype = sz
         L.gq_gemm_q4k_splitk_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.gq_gemm_q8_0.restype = st
+        L.gq_gemm_q8_0.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.gq_gemm_q4k_tiles.restype = st
         L.gq_gemm_q4k_tiles.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.gq_moe_gemm_q4k.restype = st
@@ -193,6 +195,10 @@ class GemvTable:
 
 def gq_gemm_q4k(w, x, y, M, K, N, stream=None):
     _check(lib().gq_gemm_q4k(_ptr(w), _ptr(x), _ptr(y), M, K, N, _stream(stream)))
+
+
+def gq_gemm_q8_0(w, x, y, M, K, N, stream=None):
+    _check(lib().gq_gemm_q8_0(_ptr(w), _ptr(x), _ptr(y), M, K, N, _stream(stream)))
 
 
 def gq_gemm_q4k_tiles(w, x, y, M, K, N, tile_rows, stream=None):

@@ -35,9 +35,11 @@ def within(y_gpu, y_ref, S, tol, what=""):
     Returns the largest |err| / S seen, for the log."""
     y_gpu = np.asarray(y_gpu, np.float64)
     err = np.abs(y_gpu - y_ref)
-    bad = err > tol * S
+    # written as "not within" so that a NaN or infinite result counts as bad
+    bad = ~(err <= tol * S)
     if np.any(bad):
-        i = np.unravel_index(np.argmax(err - tol * S), err.shape)
+        excess = np.where(bad, np.nan_to_num(err - tol * S, nan=np.inf, posinf=np.inf), -np.inf)
+        i = np.unravel_index(np.argmax(excess), err.shape)
         raise AssertionError(
             "%s: %d of %d outputs outside %.1e*S; worst at %s: gpu %.9g ref %.9g S %.6g"
             % (what, int(bad.sum()), bad.size, tol, i, y_gpu[i], y_ref[i], S[i]))

@@ -109,6 +109,17 @@ def test_moe_workspace_and_refusals(L):
     assert f(*([None] * 7), 0, H, I, E, k, None, 0, None) == 0
 
 
+def test_gemm_q8_0_refusals(L):
+    f = L.gq_gemm_q8_0
+    for M, K, N, code in ((16, 96, 8, "GQ_ESHAPE"), (16, 0, 8, "GQ_EINVAL"), (-1, 64, 8, "GQ_EINVAL"),
+                          (16, 64, (1 << 21) + 1, "GQ_ESHAPE")):
+        s, m = status_and_msg(L, f(FAKE, FAKE, FAKE, M, K, N, None))
+        assert s == code and "gq_gemm_q8_0" in m, (M, K, N, s, m)
+    s, m = status_and_msg(L, f(FAKE, MISALIGNED, FAKE, 16, 64, 8, None))
+    assert s == "GQ_EALIGN" and " x " in m + " "
+    assert f(None, None, None, 0, 64, 8, None) == 0
+
+
 def test_gemm_splitk_workspace_and_refusals(L):
     f, wsb = L.gq_gemm_q4k_splitk, L.gq_gemm_q4k_splitk_workspace_bytes
     M, K, N = 4096, 14336, 512

@@ -80,6 +80,27 @@ def test_gemm_parity_ragged_large_tiles():
     say("  max err/S", r1, r2)
 
 
+def test_gemm_parity_pinned_small_tiles_128():
+    """The LDS-tile kernel pinned at a shape with 576 tiles of 128 x 128, so
+    that it runs its 128 x 128 instance, ragged in both dimensions (3000 is
+    not a multiple of 128): all rows over sampled tokens and all tokens over
+    sampled rows, across tile boundaries."""
+    M, K, N = 3000, 256, 3000
+    say("gemm pinned 64 / 128x128", M, K, N)
+    g = np.random.default_rng(95)
+    w = synth.q4k_blocks(94, M, M, K)
+    x16 = synth.activations_f16(94, N, N, K)
+    y = _gemm(dev(w), x16, M, K, 64)
+    edges = np.array([0, 127, 128, 2943, 2944, 2999])
+    toks = np.unique(np.concatenate([edges, g.choice(N, 40, replace=False)]))
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K, toks=toks)
+    r1 = within(y[toks], yr, S, TOL, "128x128 token sample")
+    rows = np.unique(np.concatenate([edges, g.choice(M, 40, replace=False)]))
+    yr2, S2 = oracle.gemm(oracle.Q4_K, w, x16, M, K, rows=rows)
+    r2 = within(y[:, rows], yr2, S2, TOL, "128x128 row sample")
+    say("  max err/S", r1, r2)
+
+
 @pytest.mark.parametrize("tile_rows", [256, 128, 64])
 @pytest.mark.parametrize("M,K,N", [(256, 256, 256), (600, 1024, 520), (512, 2048, 300),
                                    (1000, 512, 1030), (130, 768, 37)])
@@ -202,3 +223,70 @@ def test_gemm_splitk_one_hot_exact():
     _, w16 = oracle.dequant(oracle.Q4_K, w, M, K)
     for i, c in enumerate(cols):
         assert np.array_equal(y[i].astype(np.float16).view(np.uint16), w16[:, c]), c
+
+
+def _gemm_q8(w_d, x16, M, K):
+    torch = torch_cuda()
+    N = x16.shape[0]
+    y = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    gq.gq_gemm_q8_0(w_d, dev(x16), y, M, K, N)
+    return half_bits(y)
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 64, 1), (130, 192, 37), (300, 1088, 270),
+                                   (1000, 1024, 520), (1700, 64, 2048), (3000, 64, 3000)])
+def test_gemm_q8_0_parity(M, K, N):
+    """Q8_0 product at sizes the oracle computes in full, across the tile
+    families (N <= 64, 64 x 64, 64 x 128, 128 x 128), ragged M and N, the
+    smallest K."""
+    say("gemm q8_0", M, K, N)
+    w = synth.q8_0_blocks(97, M, M, K)
+    x16 = synth.activations_f16(97, N, N, K)
+    y = _gemm_q8(dev(w), x16, M, K).view(np.float16).astype(np.float64)
+    yr, S = oracle.gemm(oracle.Q8_0, w, x16, M, K)
+    r = within(y, yr, S, TOL, "gemm q8_0 %dx%dx%d" % (M, K, N))
+    say("  max err/S", r)
+
+
+def test_gemm_q8_0_one_hot_exact_and_special_blocks():
+    """One-hot activation rows read out the binary16 weights binary16(d*q)
+    exactly, on random blocks and on hand-set ones: q = -128, a negative
+    scale, a binary16 subnormal scale, d = 0.  Compared as values: d = 0 with
+    a negative quant is the weight -0, which a sum that starts from +0 reads
+    out as +0 (every other binary16 value compares equal only bit for bit)."""
+    M, K, N = 130, 256, 70
+    w = synth.q8_0_blocks(98, 0, M, K).reshape(M, K // 32, 34)
+    w[0, 0, 0:2] = np.array([1.0], "<f2").view(np.uint8)
+    w[0, 0, 2:] = np.uint8(0x80)                                    # q = -128, d = 1
+    w[1, 3, 0:2] = np.array([-0.5], "<f2").view(np.uint8)           # negative d
+    w[2, 5, 0:2] = np.array([2.0 ** -20], "<f2").view(np.uint8)     # subnormal d
+    w[3, 7, 0:2] = 0                                                # d = 0
+    w = w.reshape(-1)
+    _, w16 = oracle.dequant(oracle.Q8_0, w, M, K)
+    ks = (np.arange(N) * 37 + 3) % K
+    ks[:4] = [0, 3 * 32 + 5, 5 * 32 + 31, 7 * 32]
+    x16 = np.zeros((N, K), np.float16)
+    x16[np.arange(N), ks] = 1.0
+    yb = _gemm_q8(dev(w), x16, M, K)
+    for i, k in enumerate(ks):
+        assert np.array_equal(yb[i].view(np.float16), w16[:, k].view(np.float16)), (i, k)
+    assert yb[0].view(np.float16)[0] == -128.0
+
+
+def test_gemm_q8_0_prefill_sampled():
+    """Q8_0 at a prefill shape, 14336 x 4096 weights and 512 tokens: sampled
+    rows over all tokens and all rows over two tokens."""
+    M, K, N = 14336, 4096, 512
+    say("gemm q8_0 full", M, K, N)
+    g = np.random.default_rng(99)
+    w = synth.q8_0_blocks(3, M, M, K)
+    x16 = synth.activations_f16(3, N, N, K)
+    y = _gemm_q8(dev(w), x16, M, K).view(np.float16).astype(np.float64)
+    rows = np.sort(g.choice(M, 24, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    yr, S = oracle.gemm(oracle.Q8_0, w, x16, M, K, rows=rows)
+    r1 = within(y[:, rows], yr, S, TOL, "rows sample")
+    t2 = np.array([0, N - 1])
+    yr2, S2 = oracle.gemm(oracle.Q8_0, w, x16, M, K, toks=t2)
+    r2 = within(y[t2], yr2, S2, TOL, "token sample")
+    say("  max err/S", r1, r2)
