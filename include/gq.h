@@ -207,6 +207,21 @@ gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_do
                           uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
                           int64_t topk, void *ws, size_t ws_bytes, void *stream);
 
+/* gq_moe_gemm_q4k with each slot's weight applied to the expert's input
+ * instead of its output (the Llama 4 form, page "Frink Inference: the Rust
+ * alternative to llama.cpp", section "Architecture coverage"):
+ *   g = Wg_e (w x), u = Wu_e (w x), h = binary16( silu(g) * u ), d = Wd_e h,
+ *   out[t] = binary16( sum over slots of d ),  w = topk_w[t][s].
+ * The gate and up products are linear in the input, so they are computed on x
+ * and scaled by w in binary32 before the SwiGLU.  Same arguments, workspace
+ * and errors as gq_moe_gemm_q4k. */
+gq_status gq_moe_gemm_q4k_input_weighted(const void *w_gate, const void *w_up,
+                                         const void *w_down, const uint16_t *x,
+                                         const int32_t *topk_ids, const float *topk_w,
+                                         uint16_t *out, int64_t T, int64_t H, int64_t I,
+                                         int64_t E, int64_t topk, void *ws, size_t ws_bytes,
+                                         void *stream);
+
 /* Expert routing on the device (the routing step of the mixture-of-experts
  * layer; the pages' engine routes natively, page "Frink Inference: the Rust
  * alternative to llama.cpp", opening paragraph).  For every token t:

@@ -69,7 +69,7 @@ def lib():
         L.orc_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, ctypes.c_int]
         L.orc_swiglu.argtypes = [vp, vp, i64, vp]
         L.orc_moe_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                  vp, vp, vp, vp, vp, vp, vp, vp]
+                                  vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -216,8 +216,10 @@ def moe_route(logits, topk: int, renormalize: bool = False):
     return ids, wts
 
 
-def moe_ffn(w_gate, w_up, w_down, x16, ids, wts, H: int, I: int, E: int):
-    """Binary64 MoE feed-forward; returns dict of g, u, h, d, out, Sg, Su, Sd."""
+def moe_ffn(w_gate, w_up, w_down, x16, ids, wts, H: int, I: int, E: int,
+            weight_input: bool = False):
+    """Binary64 MoE feed-forward; returns dict of g, u, h, d, out, Sg, Su, Sd.
+    weight_input: each slot's weight scales the expert's input, not its output."""
     x16 = _bits16(x16).reshape(-1, H)
     T = x16.shape[0]
     ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
@@ -235,5 +237,5 @@ def moe_ffn(w_gate, w_up, w_down, x16, ids, wts, H: int, I: int, E: int):
     r["out"] = np.empty((T, H))
     lib().orc_moe_ffn(_p(wg), _p(wu), _p(wd), _p(x16), _p(ids), _p(wts), T, H, I, E, topk,
                       _p(r["g"]), _p(r["u"]), _p(r["h"]), _p(r["d"]), _p(r["out"]),
-                      _p(r["Sg"]), _p(r["Su"]), _p(r["Sd"]))
+                      _p(r["Sg"]), _p(r["Su"]), _p(r["Sd"]), 1 if weight_input else 0)
     return r

@@ -396,16 +396,19 @@ static void expert_matvec(const uint8_t *w, int64_t R, int64_t C, const double *
  *   x16 [T][H] binary16 bits; ids/wts [T][topk] routing (binary32 weights).
  * For each (token t, slot s) with expert e = ids[t][s]:
  *   g = Wg_e x, u = Wu_e x, h = silu(g) * u, d = Wd_e h   (assignment a = t*topk+s)
- * and out[t] = sum over slots of wts[t][s] * d.  Outputs (any may be NULL):
+ * and out[t] = sum over slots of wts[t][s] * d.  With weight_input != 0 the
+ * slot weight scales the expert's input instead: x' = wts[t][s] * x feeds
+ * g and u, and out[t] = sum over slots of d.  Outputs (any may be NULL):
  *   g, u, h [T*topk][I], d [T*topk][H], out [T][H], Sg, Su [T*topk][I], Sd [T*topk][H]. */
 void orc_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
                  const uint16_t *x16, const int32_t *ids, const float *wts, int64_t T, int64_t H,
                  int64_t I, int64_t E, int64_t topk, double *g, double *u, double *h, double *d,
-                 double *out, double *Sg, double *Su, double *Sd)
+                 double *out, double *Sg, double *Su, double *Sd, int weight_input)
 {
     size_t gu_bytes = (size_t)I * (size_t)(H / QK_K) * Q4_K_BYTES;
     size_t dn_bytes = (size_t)H * (size_t)(I / QK_K) * Q4_K_BYTES;
     double *xv = (double *)malloc((size_t)H * sizeof(double));
+    double *xw = (double *)malloc((size_t)H * sizeof(double));
     double *gv = (double *)malloc((size_t)I * sizeof(double));
     double *uv = (double *)malloc((size_t)I * sizeof(double));
     double *hv = (double *)malloc((size_t)I * sizeof(double));
@@ -422,8 +425,14 @@ void orc_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_do
         for (int64_t s = 0; s < topk; s++) {
             int64_t a = t * topk + s;
             int64_t e = ids[a];
-            expert_matvec(w_gate + (size_t)e * gu_bytes, I, H, xv, gv, sg);
-            expert_matvec(w_up + (size_t)e * gu_bytes, I, H, xv, uv, su);
+            const double *xin = xv;
+            if (weight_input) {
+                for (int64_t c = 0; c < H; c++)
+                    xw[c] = (double)wts[a] * xv[c];
+                xin = xw;
+            }
+            expert_matvec(w_gate + (size_t)e * gu_bytes, I, H, xin, gv, sg);
+            expert_matvec(w_up + (size_t)e * gu_bytes, I, H, xin, uv, su);
             for (int64_t i = 0; i < I; i++)
                 hv[i] = silu(gv[i]) * uv[i];
             expert_matvec(w_down + (size_t)e * dn_bytes, H, I, hv, dv, sd);
@@ -445,11 +454,12 @@ void orc_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_do
                 if (Sd)
                     Sd[a * H + c] = sd[c];
                 if (out)
-                    out[t * H + c] += (double)wts[a] * dv[c];
+                    out[t * H + c] += (weight_input ? 1.0 : (double)wts[a]) * dv[c];
             }
         }
     }
     free(xv);
+    free(xw);
     free(gv);
     free(uv);
     free(hv);

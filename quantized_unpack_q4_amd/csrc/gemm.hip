@@ -41,6 +41,8 @@ struct GemmParams {
     int topk;
     int E;
     int64_t expert_bytes;  // bytes of one expert's weight matrix
+    const float *wts;      // gate/up with weight_input: the slot weights, [T*topk]
+    int weight_input;
 };
 
 
@@ -310,8 +312,10 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
                 }
             } else if (MODE == kModeGateUp) {
                 uint16_t *hr = reinterpret_cast<uint16_t *>(p.y) + n * p.M;
-                const float4_t gg = acc[0][i][j];
-                const float4_t uu = acc[NW - 1][i][j];
+                // the slot weight on the expert's input scales g and u alike
+                const float pw = p.weight_input ? p.wts[p.sorted[n]] : 1.f;
+                const float4_t gg = pw * acc[0][i][j];
+                const float4_t uu = pw * acc[NW - 1][i][j];
                 *reinterpret_cast<uint2 *>(hr + m) =
                     make_uint2(pack_half2(silu(gg[0]) * uu[0], silu(gg[1]) * uu[1]),
                                pack_half2(silu(gg[2]) * uu[2], silu(gg[3]) * uu[3]));
@@ -388,6 +392,8 @@ static hipError_t moe_gemms(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.max_tiles = max_tiles;
     p.topk = (int)a.topk;
     p.E = (int)a.E;
+    p.wts = a.wts;
+    p.weight_input = a.weight_input;
 
     // gate/up with the SwiGLU epilogue: h[pos][0..I) in binary16
     p.w = a.w_gate;

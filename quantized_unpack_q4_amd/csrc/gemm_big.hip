@@ -117,6 +117,8 @@ struct BigParams {
     int max_tiles, topk, E;
     int64_t expert_bytes;
     int splits; // kBigSplit: K is cut into this many equal runs of whole super-blocks
+    const float *wts; // gate/up with weight_input: the slot weights, [T*topk]
+    int weight_input;
 };
 
 } // namespace
@@ -363,13 +365,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
             // elements v < 8 are gate rows 8*(v/4) + 4h + v%4 of the wave's 16,
             // elements v + 8 the same rows of up
             uint16_t *hr = reinterpret_cast<uint16_t *>(p.y) + (size_t)(n0 + nl) * M;
+            // the slot weight on the expert's input scales g and u alike
+            const float pw = p.weight_input ? p.wts[p.sorted[n0 + nl]] : 1.f;
 #pragma unroll
             for (int v4 = 0; v4 < 2; ++v4) {
                 const int m = m0 + 16 * wave + 8 * v4 + 4 * h;
                 float o[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    o[c] = silu(a[4 * v4 + c]) * a[8 + 4 * v4 + c];
+                    o[c] = silu(pw * a[4 * v4 + c]) * (pw * a[8 + 4 * v4 + c]);
                 *reinterpret_cast<uint2 *>(hr + m) =
                     make_uint2(pack_half2(o[0], o[1]), pack_half2(o[2], o[3]));
             }
@@ -574,6 +578,8 @@ hipError_t launch_moe_big(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.max_tiles = max_tiles;
     p.topk = (int)a.topk;
     p.E = (int)a.E;
+    p.wts = a.wts;
+    p.weight_input = a.weight_input;
 
     // gate/up with the SwiGLU epilogue: h[pos][0..I) in binary16, 128 rows of
     // I per workgroup

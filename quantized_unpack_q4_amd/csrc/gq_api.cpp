@@ -429,13 +429,14 @@ gq_status gq_moe_workspace_offsets(int64_t T, int64_t H, int64_t I, int64_t E, i
     return moe_layout("gq_moe_workspace_offsets", T, H, I, E, topk, off);
 }
 
-gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_down,
-                          const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
-                          uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
-                          int64_t topk, void *ws, size_t ws_bytes, void *stream)
+static gq_status moe_common(const char *fn, const void *w_gate, const void *w_up,
+                            const void *w_down, const uint16_t *x, const int32_t *topk_ids,
+                            const float *topk_w, uint16_t *out, int64_t T, int64_t H, int64_t I,
+                            int64_t E, int64_t topk, void *ws, size_t ws_bytes, void *stream,
+                            int weight_input)
 {
-    static const char fn[] = "gq_moe_gemm_q4k";
     gq::MoeArgs a;
+    a.weight_input = weight_input;
     GQ_TRY(moe_layout(fn, T, H, I, E, topk, a.off));
     if (T == 0)
         return GQ_OK;
@@ -467,6 +468,26 @@ gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_do
     a.topk = topk;
     a.ws = (uint8_t *)ws;
     return launched(fn, gq::launch_moe(a, (hipStream_t)stream));
+}
+
+gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_down,
+                          const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                          uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
+                          int64_t topk, void *ws, size_t ws_bytes, void *stream)
+{
+    return moe_common("gq_moe_gemm_q4k", w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I,
+                      E, topk, ws, ws_bytes, stream, 0);
+}
+
+gq_status gq_moe_gemm_q4k_input_weighted(const void *w_gate, const void *w_up,
+                                         const void *w_down, const uint16_t *x,
+                                         const int32_t *topk_ids, const float *topk_w,
+                                         uint16_t *out, int64_t T, int64_t H, int64_t I,
+                                         int64_t E, int64_t topk, void *ws, size_t ws_bytes,
+                                         void *stream)
+{
+    return moe_common("gq_moe_gemm_q4k_input_weighted", w_gate, w_up, w_down, x, topk_ids, topk_w,
+                      out, T, H, I, E, topk, ws, ws_bytes, stream, 1);
 }
 
 gq_status gq_gemv_q4k_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,

@@ -80,6 +80,8 @@ struct MoeArgs {
     int64_t T, H, I, E, topk;
     uint8_t *ws;
     size_t off[7];
+    int weight_input; // 1: each slot's weight scales the expert's input (h = silu(p g) (p u),
+                      // output rows summed unweighted); 0: it scales the expert's output
 };
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 

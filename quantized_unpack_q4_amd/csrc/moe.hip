@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restric
                                                           const int32_t *__restrict__ pos_of,
                                                           const float *__restrict__ wts,
                                                           uint16_t *__restrict__ out, int H,
-                                                          int topk, int col_blocks)
+                                                          int topk, int col_blocks, int unit)
 {
     const int t = blockIdx.x / col_blocks;
     const int c = ((blockIdx.x % col_blocks) * 256 + threadIdx.x) * 4;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restric
         const int pos = pos_of[(int64_t)t * topk + s];
         if (pos < 0)
             continue;
-        const float wgt = wts[(int64_t)t * topk + s];
+        const float wgt = unit ? 1.f : wts[(int64_t)t * topk + s];
         const float4 d = ldf4(D + (int64_t)pos * H + c);
         a0 = fmaf(wgt, d.x, a0);
         a1 = fmaf(wgt, d.y, a1);
@@ -243,7 +243,7 @@ hipError_t launch_moe(const MoeArgs &a, hipStream_t s)
     const int col_blocks = (int)((a.H / 4 + 255) / 256);
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)(a.T * col_blocks)), dim3(256), 0, s,
                        reinterpret_cast<const float *>(a.ws + a.off[5]), pos_of, a.wts, a.out,
-                       (int)a.H, (int)a.topk, col_blocks);
+                       (int)a.H, (int)a.topk, col_blocks, a.weight_input);
     return hipGetLastError();
 }
 

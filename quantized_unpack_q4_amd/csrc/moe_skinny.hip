@@ -46,6 +46,8 @@ struct SkinnyParams {
     const int32_t *sorted;  // assignment t*topk + s at each sorted position
     int M, K, topk;
     int64_t expert_bytes;
+    const float *wts; // gate/up with weight_input: the slot weights, [T*topk]
+    int weight_input;
 };
 
 // 16 bytes per lane, global -> LDS; lane l lands at lds_base + 16*l (lds_base
@@ -244,7 +246,9 @@ __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, 
                 continue;
             const int64_t pos = p0 + t;
             if constexpr (MODE == 0) {
-                const float v = silu(acc[0][tg][i]) * acc[1][tg][i];
+                // the slot weight on the expert's input scales g and u alike
+                const float pw = p.weight_input ? p.wts[p.sorted[pos]] : 1.f;
+                const float v = silu(pw * acc[0][tg][i]) * (pw * acc[1][tg][i]);
                 reinterpret_cast<uint16_t *>(p.y)[pos * M + row] = (uint16_t)pack_half2(v, 0.f);
             } else {
                 reinterpret_cast<float *>(p.y)[pos * M + row] = acc[0][tg][i];
@@ -283,6 +287,8 @@ hipError_t launch_moe_skinny(const MoeArgs &a, hipStream_t s)
     p.offsets = reinterpret_cast<const int32_t *>(a.ws + a.off[0]);
     p.sorted = reinterpret_cast<const int32_t *>(a.ws + a.off[1]);
     p.topk = (int)a.topk;
+    p.wts = a.wts;
+    p.weight_input = a.weight_input;
 
     // gate/up with the SwiGLU epilogue: h[pos][0..I) in binary16
     p.w = a.w_gate;

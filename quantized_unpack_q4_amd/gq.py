@@ -26,7 +26,7 @@ EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
     "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
     "gq_gemm_q4k_splitk_workspace_bytes",
-    "gq_moe_gemm_q4k", "gq_moe_route",
+    "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_route",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
 )
@@ -76,9 +76,10 @@ def lib() -> ctypes.CDLL:
         L.gq_gemm_q8_0.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.gq_gemm_q4k_tiles.restype = st
         L.gq_gemm_q4k_tiles.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
-        L.gq_moe_gemm_q4k.restype = st
-        L.gq_moe_gemm_q4k.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                      vp, sz, vp]
+        for name in ("gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted"):
+            f = getattr(L, name)
+            f.restype = st
+            f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
         L.gq_moe_route.restype = st
         L.gq_moe_route.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.gq_moe_workspace_bytes.restype = sz
@@ -233,12 +234,12 @@ def gq_moe_workspace_offsets(T, H, I, E, topk):
 
 
 def gq_moe_gemm_q4k(w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I, E, topk, ws,
-                    ws_bytes=None, stream=None):
+                    ws_bytes=None, stream=None, input_weighted=False):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().gq_moe_gemm_q4k(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x),
-                                 _ptr(topk_ids), _ptr(topk_w), _ptr(out), T, H, I, E, topk,
-                                 _ptr(ws), ws_bytes, _stream(stream)))
+    f = lib().gq_moe_gemm_q4k_input_weighted if input_weighted else lib().gq_moe_gemm_q4k
+    _check(f(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x), _ptr(topk_ids), _ptr(topk_w),
+             _ptr(out), T, H, I, E, topk, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def gq_dequant_q8_0(w, out32, out16, M, K, stream=None):
@@ -308,7 +309,7 @@ def moe_route(logits, topk: int, renormalize=False, stream=None):
 
 
 def moe_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, H: int, I: int, E: int, ws=None,
-            out=None, stream=None):
+            out=None, stream=None, input_weighted=False):
     """Mixture-of-experts feed-forward; returns (out [T][H] float16, workspace)."""
     import torch
     T, topk = topk_ids.shape
@@ -317,7 +318,7 @@ def moe_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, H: int, I: int, E: int,
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x16.device)
     o = out if out is not None else torch.empty((T, H), dtype=torch.float16, device=x16.device)
     gq_moe_gemm_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, o, T, H, I, E, topk, ws,
-                    stream=stream)
+                    stream=stream, input_weighted=input_weighted)
     return o, ws
 
 

@@ -41,8 +41,9 @@ def _setup(seed, T, H, I, E, k):
     return wg, wu, wd, x16, ids, wts64.astype(np.float32)
 
 
-def _run(wg, wu, wd, x16, ids, wts, H, I, E):
-    out, ws = gq.moe_q4k(dev(wg), dev(wu), dev(wd), dev(x16), dev(ids), dev(wts), H, I, E)
+def _run(wg, wu, wd, x16, ids, wts, H, I, E, input_weighted=False):
+    out, ws = gq.moe_q4k(dev(wg), dev(wu), dev(wd), dev(x16), dev(ids), dev(wts), H, I, E,
+                         input_weighted=input_weighted)
     T, k = ids.shape
     off = gq.gq_moe_workspace_offsets(T, H, I, E, k)
     wsh = host(ws)
@@ -69,7 +70,11 @@ def _check_grouping(ids, E, table, sorted_, pos_of):
     assert np.array_equal(pos_of[sorted_], np.arange(A))
 
 
-def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks):
+def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks,
+            weight_input=False):
+    """Stages (ii)-(iv).  weight_input: the slot weight w scales the expert's
+    input, so stage (ii) expects silu(w g) * (w u) with the bounds of g and u
+    scaled by w, and stage (iv) sums the slots' d unweighted."""
     T, k = ids.shape
     gu = I * (H // 256) * 144
     dn = H * (I // 256) * 144
@@ -86,6 +91,9 @@ def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
             g, Sg = oracle.gemm(oracle.Q4_K, wg[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
             u, Su = oracle.gemm(oracle.Q4_K, wu[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
             g, Sg, u, Su = g[0], Sg[0], u[0], Su[0]
+            if weight_input:
+                pw = np.float64(wts[t, s])
+                g, Sg, u, Su = pw * g, pw * Sg, pw * u, pw * Su
             href = _silu(g) * u
             bound = TOL * (np.abs(_dsilu(g) * u) * Sg + np.abs(_silu(g)) * Su) \
                 + np.abs(href) * 2.0 ** -10 + 2.0 ** -24
@@ -96,8 +104,9 @@ def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
             dref, Sd = oracle.gemm(oracle.Q4_K, wd[e * dn:(e + 1) * dn],
                                    h[p:p + 1].view(np.uint16), H, I)
             worst["d"] = max(worst["d"], within(d[p], dref[0], Sd[0], TOL, "d"))
-            acc += np.float64(wts[t, s]) * dref[0]
-            accS += np.float64(wts[t, s]) * Sd[0]
+            wc = 1.0 if weight_input else np.float64(wts[t, s])
+            acc += wc * dref[0]
+            accS += wc * Sd[0]
         # (iv) combine
         worst["out"] = max(worst["out"], within(o[t], acc, accS, TOL, "out t=%d" % t))
     return worst
@@ -196,3 +205,25 @@ def test_moe_many_tokens_per_expert_tiles():
     worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
                     range(T))
     say("moe tiles staged", worst)
+
+
+@pytest.mark.parametrize("T", [100, 300, 700])
+def test_moe_input_weighted(T):
+    """Slot weights applied to the experts' inputs (gq_moe_gemm_q4k_input_weighted)
+    in each regime: 100, 300 and 700 tokens over 8 experts, top-2, are about
+    25, 75 and 175 tokens per expert (weight streaming, 128-row tiles,
+    256 x 256 tiles); grouping whole, values in stages on sampled tokens, and
+    the end-to-end difference from the binary64 oracle of the same form."""
+    H, I, E, k = 512, 256, 8, 2
+    say("moe input weighted T", T)
+    wg, wu, wd, x16, ids, wts = _setup(66, T, H, I, E, k)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E,
+                                           input_weighted=True)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    toks = sorted(set([0, 1, T // 3, T // 2, T - 2, T - 1]))
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks,
+                    weight_input=True)
+    r = oracle.moe_ffn(wg, wu, wd, x16[toks], ids[toks], wts[toks], H, I, E, weight_input=True)
+    bound = r["Sd"].reshape(len(toks), k, -1).sum(axis=1)
+    e2e = float((np.abs(o[toks] - r["out"]) / np.maximum(bound, 1e-300)).max())
+    say("  staged", worst, "end-to-end", e2e)

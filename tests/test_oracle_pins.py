@@ -455,6 +455,33 @@ def test_swiglu_closed_forms(orc):
     assert np.allclose(h3, 3.0 * h, rtol=1e-15, atol=0)
 
 
+def test_moe_input_weighted(orc):
+    """Slot weight on the expert's input: with weight 2 (an exact scaling of
+    binary16 activations) it equals the output-weighted layer run on 2x with
+    weight 1, bit for bit; with weight 1 both forms agree; and the output is
+    the unweighted sum of the slots' d."""
+    T, H, I, E, k = 3, 512, 256, 4, 2
+    wg = synth.q4k_blocks(33, 0, E * I, H)
+    wu = synth.q4k_blocks(33, 1, E * I, H)
+    wd = synth.q4k_blocks(33, 2, E * H, I)
+    x16 = synth.activations_f16(33, 0, T, H)
+    ids = np.array([[0, 3], [2, 1], [1, 0]], np.int32)
+    two = np.full((T, k), 2.0, np.float32)
+    one = np.ones((T, k), np.float32)
+    r_in = orc.moe_ffn(wg, wu, wd, x16, ids, two, H, I, E, weight_input=True)
+    x2 = (x16.astype(np.float32) * 2).astype(np.float16)
+    assert np.array_equal(x2.astype(np.float64), 2 * x16.astype(np.float64))
+    r_out = orc.moe_ffn(wg, wu, wd, x2, ids, one, H, I, E)
+    for key in ("g", "u", "h", "d", "out"):
+        assert np.array_equal(r_in[key], r_out[key]), key
+    w = np.array([[0.7, 0.3], [0.5, 0.25], [1.0, 0.125]], np.float32)
+    r_in = orc.moe_ffn(wg, wu, wd, x16, ids, w, H, I, E, weight_input=True)
+    assert np.allclose(r_in["out"], r_in["d"].reshape(T, k, H).sum(axis=1), rtol=1e-15, atol=1e-300)
+    r_1 = orc.moe_ffn(wg, wu, wd, x16, ids, one, H, I, E, weight_input=True)
+    r_1o = orc.moe_ffn(wg, wu, wd, x16, ids, one, H, I, E)
+    assert np.array_equal(r_1["out"], r_1o["out"])
+
+
 def _silu(z):
     return z / (1.0 + np.exp(-z))
 
