@@ -222,6 +222,26 @@ gq_status gq_moe_gemm_q4k_input_weighted(const void *w_gate, const void *w_up,
                                          int64_t E, int64_t topk, void *ws, size_t ws_bytes,
                                          void *stream);
 
+/* The mixture-of-experts layer over Q8_0 expert stacks: the formula of
+ * gq_moe_gemm_q4k (and, for the second call, of
+ * gq_moe_gemm_q4k_input_weighted) with w_gate, w_up E stacked [I rows][H cols]
+ * and w_down E stacked [H rows][I cols] Q8_0 matrices (rows of 34-byte
+ * blocks), each weight entering as binary16(d * q).  Q8_0 is the format whose
+ * logits the pages report as matching llama.cpp's exactly (page "Frink
+ * Inference: the Rust alternative to llama.cpp", the item on K-quant logits
+ * drifting).  Same arguments, workspace, shape limits (H % 256 == 0,
+ * I % 256 == 0) and errors as gq_moe_gemm_q4k. */
+gq_status gq_moe_gemm_q8_0(const void *w_gate, const void *w_up, const void *w_down,
+                           const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                           uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
+                           int64_t topk, void *ws, size_t ws_bytes, void *stream);
+gq_status gq_moe_gemm_q8_0_input_weighted(const void *w_gate, const void *w_up,
+                                          const void *w_down, const uint16_t *x,
+                                          const int32_t *topk_ids, const float *topk_w,
+                                          uint16_t *out, int64_t T, int64_t H, int64_t I,
+                                          int64_t E, int64_t topk, void *ws, size_t ws_bytes,
+                                          void *stream);
+
 /* Expert routing on the device (the routing step of the mixture-of-experts
  * layer; the pages' engine routes natively, page "Frink Inference: the Rust
  * alternative to llama.cpp", opening paragraph).  For every token t:

@@ -68,7 +68,7 @@ def lib():
         L.orc_gemm.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
         L.orc_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, ctypes.c_int]
         L.orc_swiglu.argtypes = [vp, vp, i64, vp]
-        L.orc_moe_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+        L.orc_moe_ffn.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                   vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
         _lib = L
     return _lib
@@ -217,9 +217,10 @@ def moe_route(logits, topk: int, renormalize: bool = False):
 
 
 def moe_ffn(w_gate, w_up, w_down, x16, ids, wts, H: int, I: int, E: int,
-            weight_input: bool = False):
+            weight_input: bool = False, fmt: int = Q4_K):
     """Binary64 MoE feed-forward; returns dict of g, u, h, d, out, Sg, Su, Sd.
-    weight_input: each slot's weight scales the expert's input, not its output."""
+    weight_input: each slot's weight scales the expert's input, not its output.
+    fmt: format of all three weight stacks (Q4_K or Q8_0)."""
     x16 = _bits16(x16).reshape(-1, H)
     T = x16.shape[0]
     ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
@@ -227,15 +228,15 @@ def moe_ffn(w_gate, w_up, w_down, x16, ids, wts, H: int, I: int, E: int,
     topk = ids.shape[1]
     assert ids.shape == (T, topk) and wts.shape == (T, topk)
     assert 0 <= ids.min() and ids.max() < E
-    gu = I * (H // 256) * 144
-    dn = H * (I // 256) * 144
+    gu = I * row_bytes(fmt, H)
+    dn = H * row_bytes(fmt, I)
     wg, wu, wd = _u8(w_gate), _u8(w_up), _u8(w_down)
     assert wg.size >= E * gu and wu.size >= E * gu and wd.size >= E * dn
     A = T * topk
     r = {k: np.empty((A, I)) for k in ("g", "u", "h", "Sg", "Su")}
     r.update({k: np.empty((A, H)) for k in ("d", "Sd")})
     r["out"] = np.empty((T, H))
-    lib().orc_moe_ffn(_p(wg), _p(wu), _p(wd), _p(x16), _p(ids), _p(wts), T, H, I, E, topk,
+    lib().orc_moe_ffn(fmt, _p(wg), _p(wu), _p(wd), _p(x16), _p(ids), _p(wts), T, H, I, E, topk,
                       _p(r["g"]), _p(r["u"]), _p(r["h"]), _p(r["d"]), _p(r["out"]),
                       _p(r["Sg"]), _p(r["Su"]), _p(r["Sd"]), 1 if weight_input else 0)
     return r

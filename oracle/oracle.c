@@ -372,15 +372,15 @@ void orc_swiglu(const double *g, const double *u, int64_t n, double *h)
         h[i] = silu(g[i]) * u[i];
 }
 
-/* Dense product of one expert's weight matrix (R rows of C columns, Q4_K)
- * with a binary64 vector. */
-static void expert_matvec(const uint8_t *w, int64_t R, int64_t C, const double *v, double *out,
-                          double *mag)
+/* Dense product of one expert's weight matrix (R rows of C columns, format
+ * fmt) with a binary64 vector. */
+static void expert_matvec(int fmt, const uint8_t *w, int64_t R, int64_t C, const double *v,
+                          double *out, double *mag)
 {
     for (int64_t r = 0; r < R; r++) {
         double acc = 0.0, s = 0.0;
         for (int64_t c = 0; c < C; c++) {
-            double p = (double)(float)q4k_weight_exact(w, C, r, c) * v[c];
+            double p = (double)(float)weight_exact(fmt, w, C, r, c) * v[c];
             acc += p;
             s += fabs(p);
         }
@@ -391,8 +391,9 @@ static void expert_matvec(const uint8_t *w, int64_t R, int64_t C, const double *
 }
 
 /* The MoE feed-forward of every token, entirely in binary64.
- *   weights: w_gate, w_up are E stacked [I rows][H cols] Q4_K matrices;
- *            w_down is E stacked [H rows][I cols] Q4_K matrices.
+ *   weights: w_gate, w_up are E stacked [I rows][H cols] matrices;
+ *            w_down is E stacked [H rows][I cols] matrices, all of format
+ *            fmt (0 = Q8_0, 1 = Q4_K).
  *   x16 [T][H] binary16 bits; ids/wts [T][topk] routing (binary32 weights).
  * For each (token t, slot s) with expert e = ids[t][s]:
  *   g = Wg_e x, u = Wu_e x, h = silu(g) * u, d = Wd_e h   (assignment a = t*topk+s)
@@ -400,13 +401,15 @@ static void expert_matvec(const uint8_t *w, int64_t R, int64_t C, const double *
  * slot weight scales the expert's input instead: x' = wts[t][s] * x feeds
  * g and u, and out[t] = sum over slots of d.  Outputs (any may be NULL):
  *   g, u, h [T*topk][I], d [T*topk][H], out [T][H], Sg, Su [T*topk][I], Sd [T*topk][H]. */
-void orc_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+void orc_moe_ffn(int fmt, const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
                  const uint16_t *x16, const int32_t *ids, const float *wts, int64_t T, int64_t H,
                  int64_t I, int64_t E, int64_t topk, double *g, double *u, double *h, double *d,
                  double *out, double *Sg, double *Su, double *Sd, int weight_input)
 {
-    size_t gu_bytes = (size_t)I * (size_t)(H / QK_K) * Q4_K_BYTES;
-    size_t dn_bytes = (size_t)H * (size_t)(I / QK_K) * Q4_K_BYTES;
+    size_t gu_bytes = fmt == 0 ? (size_t)I * (size_t)(H / Q8_0_BLOCK) * Q8_0_BYTES
+                               : (size_t)I * (size_t)(H / QK_K) * Q4_K_BYTES;
+    size_t dn_bytes = fmt == 0 ? (size_t)H * (size_t)(I / Q8_0_BLOCK) * Q8_0_BYTES
+                               : (size_t)H * (size_t)(I / QK_K) * Q4_K_BYTES;
     double *xv = (double *)malloc((size_t)H * sizeof(double));
     double *xw = (double *)malloc((size_t)H * sizeof(double));
     double *gv = (double *)malloc((size_t)I * sizeof(double));
@@ -431,11 +434,11 @@ void orc_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_do
                     xw[c] = (double)wts[a] * xv[c];
                 xin = xw;
             }
-            expert_matvec(w_gate + (size_t)e * gu_bytes, I, H, xin, gv, sg);
-            expert_matvec(w_up + (size_t)e * gu_bytes, I, H, xin, uv, su);
+            expert_matvec(fmt, w_gate + (size_t)e * gu_bytes, I, H, xin, gv, sg);
+            expert_matvec(fmt, w_up + (size_t)e * gu_bytes, I, H, xin, uv, su);
             for (int64_t i = 0; i < I; i++)
                 hv[i] = silu(gv[i]) * uv[i];
-            expert_matvec(w_down + (size_t)e * dn_bytes, H, I, hv, dv, sd);
+            expert_matvec(fmt, w_down + (size_t)e * dn_bytes, H, I, hv, dv, sd);
             for (int64_t i = 0; i < I; i++) {
                 if (g)
                     g[a * I + i] = gv[i];

@@ -49,7 +49,6 @@ struct GemmParams {
 template <int BM, int BN, int WM, int WN, int MODE, int FMT = kFmtQ4K>
 __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
 {
-    static_assert(FMT == kFmtQ4K || MODE == kModeGemm, "Q8_0 only for the plain product");
     constexpr int KS = 64;        // weights per K step
     constexpr int LDR = KS + 8;   // LDS row stride in halves (144 bytes, keeps 16-byte alignment)
     constexpr int NW = MODE == kModeGateUp ? 2 : 1;
@@ -130,21 +129,25 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
     uint4 rh[NW];
     uint32_t rq[NW][QB / 4];
     uint4 rx[XU];
-    uint32_t r8[QB8 / 4 + 1], r8d; // Q8_0: quant dwords (one extra for the shift), scale dword
+    uint32_t r8[NW][QB8 / 4 + 1], r8d[NW]; // Q8_0: quant dwords (one extra for the shift), scale dword
 
     auto load_step = [&](int kt) {
         if constexpr (FMT == kFmtQ8) {
-            if (drow_ok) {
-                const uint32_t *st = reinterpret_cast<const uint32_t *>(wrowA + (int64_t)kt * 68);
 #pragma unroll
-                for (int i = 0; i <= QB8 / 4; ++i)
-                    r8[i] = st[min((q8 >> 2) + i, 16)]; // dword 16: the step's last
-                r8d = st[d8w];
-            } else {
+            for (int v = 0; v < NW; ++v) {
+                if (drow_ok) {
+                    const uint32_t *st =
+                        reinterpret_cast<const uint32_t *>((v == 0 ? wrowA : wrowB) + (int64_t)kt * 68);
 #pragma unroll
-                for (int i = 0; i <= QB8 / 4; ++i)
-                    r8[i] = 0u;
-                r8d = 0u;
+                    for (int i = 0; i <= QB8 / 4; ++i)
+                        r8[v][i] = st[min((q8 >> 2) + i, 16)]; // dword 16: the step's last
+                    r8d[v] = st[d8w];
+                } else {
+#pragma unroll
+                    for (int i = 0; i <= QB8 / 4; ++i)
+                        r8[v][i] = 0u;
+                    r8d[v] = 0u;
+                }
             }
 #pragma unroll
             for (int u = 0; u < XU; ++u)
@@ -190,21 +193,25 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(GemmParams p)
             // byte conversion (exact), not as a sign-extended integer: the
             // compiler folds the latter into an unsigned conversion of the
             // sign-extended byte here, which turns negative quants into ~2^32.
-            const float d = half_to_float((r8d >> d8hi) & 0xffffu);
-            uint32_t hw[QB8 / 2];
 #pragma unroll
-            for (int i = 0; i < QB8 / 4; ++i) {
-                const uint32_t D = __builtin_amdgcn_alignbyte(r8[i + 1], r8[i], q8 & 3) ^ 0x80808080u;
-                hw[2 * i] = pack_half2(d * (ubyte_to_float<0>(D) - 128.f),
-                                       d * (ubyte_to_float<1>(D) - 128.f));
-                hw[2 * i + 1] = pack_half2(d * (ubyte_to_float<2>(D) - 128.f),
-                                           d * (ubyte_to_float<3>(D) - 128.f));
+            for (int v = 0; v < NW; ++v) {
+                const float d = half_to_float((r8d[v] >> d8hi) & 0xffffu);
+                uint32_t hw[QB8 / 2];
+#pragma unroll
+                for (int i = 0; i < QB8 / 4; ++i) {
+                    const uint32_t D =
+                        __builtin_amdgcn_alignbyte(r8[v][i + 1], r8[v][i], q8 & 3) ^ 0x80808080u;
+                    hw[2 * i] = pack_half2(d * (ubyte_to_float<0>(D) - 128.f),
+                                           d * (ubyte_to_float<1>(D) - 128.f));
+                    hw[2 * i + 1] = pack_half2(d * (ubyte_to_float<2>(D) - 128.f),
+                                               d * (ubyte_to_float<3>(D) - 128.f));
+                }
+                _Float16 *dst = &sW[buf][v][drow][w8];
+#pragma unroll
+                for (int i = 0; i < QB8 / 8; ++i)
+                    *reinterpret_cast<uint4 *>(dst + 8 * i) =
+                        make_uint4(hw[4 * i], hw[4 * i + 1], hw[4 * i + 2], hw[4 * i + 3]);
             }
-            _Float16 *dst = &sW[buf][0][drow][w8];
-#pragma unroll
-            for (int i = 0; i < QB8 / 8; ++i)
-                *reinterpret_cast<uint4 *>(dst + 8 * i) =
-                    make_uint4(hw[4 * i], hw[4 * i + 1], hw[4 * i + 2], hw[4 * i + 3]);
 #pragma unroll
             for (int u = 0; u < XU; ++u)
                 *reinterpret_cast<uint4 *>(&sX[buf][xr[u]][8 * xchunk[u]]) = rx[u];
@@ -381,7 +388,7 @@ hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_
 
 // ---- grouped products of the mixture-of-experts layer ----
 
-template <int BN>
+template <int BN, int FMT>
 static hipError_t moe_gemms(const MoeArgs &a, int max_tiles, hipStream_t s)
 {
     const int32_t *offsets = reinterpret_cast<const int32_t *>(a.ws + a.off[0]);
@@ -402,9 +409,9 @@ static hipError_t moe_gemms(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.y = a.ws + a.off[4];
     p.M = (int)a.I;
     p.K = (int)a.H;
-    p.expert_bytes = a.I * (a.H / kQ4kWeights) * kQ4kBytes;
+    p.expert_bytes = FMT == kFmtQ8 ? a.I * (a.H / 32) * 34 : a.I * (a.H / kQ4kWeights) * kQ4kBytes;
     constexpr int WM = BN >= 64 ? 2 : 4, WN = 4 / WM;
-    hipLaunchKernelGGL((gemm_q4k_kernel<128, BN, WM, WN, kModeGateUp>),
+    hipLaunchKernelGGL((gemm_q4k_kernel<128, BN, WM, WN, kModeGateUp, FMT>),
                        dim3((unsigned)(a.I / 128), (unsigned)max_tiles), dim3(256), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
@@ -417,18 +424,25 @@ static hipError_t moe_gemms(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.y = a.ws + a.off[5];
     p.M = (int)a.H;
     p.K = (int)a.I;
-    p.expert_bytes = a.H * (a.I / kQ4kWeights) * kQ4kBytes;
-    hipLaunchKernelGGL((gemm_q4k_kernel<128, BN, WM, WN, kModeDown>),
+    p.expert_bytes = FMT == kFmtQ8 ? a.H * (a.I / 32) * 34 : a.H * (a.I / kQ4kWeights) * kQ4kBytes;
+    hipLaunchKernelGGL((gemm_q4k_kernel<128, BN, WM, WN, kModeDown, FMT>),
                        dim3((unsigned)(a.H / 128), (unsigned)max_tiles), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_moe_gemms(const MoeArgs &a, int bn, int max_tiles, hipStream_t s)
 {
+    if (a.q8_0) {
+        switch (bn) {
+        case 32: return moe_gemms<32, kFmtQ8>(a, max_tiles, s);
+        case 64: return moe_gemms<64, kFmtQ8>(a, max_tiles, s);
+        default: return moe_gemms<128, kFmtQ8>(a, max_tiles, s);
+        }
+    }
     switch (bn) {
-    case 32: return moe_gemms<32>(a, max_tiles, s);
-    case 64: return moe_gemms<64>(a, max_tiles, s);
-    default: return moe_gemms<128>(a, max_tiles, s);
+    case 32: return moe_gemms<32, kFmtQ4K>(a, max_tiles, s);
+    case 64: return moe_gemms<64, kFmtQ4K>(a, max_tiles, s);
+    default: return moe_gemms<128, kFmtQ4K>(a, max_tiles, s);
     }
 }
 

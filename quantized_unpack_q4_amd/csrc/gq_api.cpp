@@ -433,10 +433,11 @@ static gq_status moe_common(const char *fn, const void *w_gate, const void *w_up
                             const void *w_down, const uint16_t *x, const int32_t *topk_ids,
                             const float *topk_w, uint16_t *out, int64_t T, int64_t H, int64_t I,
                             int64_t E, int64_t topk, void *ws, size_t ws_bytes, void *stream,
-                            int weight_input)
+                            int weight_input, int q8_0)
 {
     gq::MoeArgs a;
     a.weight_input = weight_input;
+    a.q8_0 = q8_0;
     GQ_TRY(moe_layout(fn, T, H, I, E, topk, a.off));
     if (T == 0)
         return GQ_OK;
@@ -476,7 +477,7 @@ gq_status gq_moe_gemm_q4k(const void *w_gate, const void *w_up, const void *w_do
                           int64_t topk, void *ws, size_t ws_bytes, void *stream)
 {
     return moe_common("gq_moe_gemm_q4k", w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I,
-                      E, topk, ws, ws_bytes, stream, 0);
+                      E, topk, ws, ws_bytes, stream, 0, 0);
 }
 
 gq_status gq_moe_gemm_q4k_input_weighted(const void *w_gate, const void *w_up,
@@ -487,7 +488,27 @@ gq_status gq_moe_gemm_q4k_input_weighted(const void *w_gate, const void *w_up,
                                          void *stream)
 {
     return moe_common("gq_moe_gemm_q4k_input_weighted", w_gate, w_up, w_down, x, topk_ids, topk_w,
-                      out, T, H, I, E, topk, ws, ws_bytes, stream, 1);
+                      out, T, H, I, E, topk, ws, ws_bytes, stream, 1, 0);
+}
+
+gq_status gq_moe_gemm_q8_0(const void *w_gate, const void *w_up, const void *w_down,
+                           const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                           uint16_t *out, int64_t T, int64_t H, int64_t I, int64_t E,
+                           int64_t topk, void *ws, size_t ws_bytes, void *stream)
+{
+    return moe_common("gq_moe_gemm_q8_0", w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I,
+                      E, topk, ws, ws_bytes, stream, 0, 1);
+}
+
+gq_status gq_moe_gemm_q8_0_input_weighted(const void *w_gate, const void *w_up,
+                                          const void *w_down, const uint16_t *x,
+                                          const int32_t *topk_ids, const float *topk_w,
+                                          uint16_t *out, int64_t T, int64_t H, int64_t I,
+                                          int64_t E, int64_t topk, void *ws, size_t ws_bytes,
+                                          void *stream)
+{
+    return moe_common("gq_moe_gemm_q8_0_input_weighted", w_gate, w_up, w_down, x, topk_ids,
+                      topk_w, out, T, H, I, E, topk, ws, ws_bytes, stream, 1, 1);
 }
 
 gq_status gq_gemv_q4k_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,

@@ -82,6 +82,7 @@ struct MoeArgs {
     size_t off[7];
     int weight_input; // 1: each slot's weight scales the expert's input (h = silu(p g) (p u),
                       // output rows summed unweighted); 0: it scales the expert's output
+    int q8_0;         // 1: the three weight stacks are Q8_0 (128-row tile kernel only); 0: Q4_K
 };
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 

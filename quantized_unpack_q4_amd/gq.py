@@ -26,7 +26,8 @@ EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
     "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
     "gq_gemm_q4k_splitk_workspace_bytes",
-    "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_route",
+    "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
+    "gq_moe_gemm_q8_0_input_weighted", "gq_moe_route",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
 )
@@ -76,7 +77,8 @@ def lib() -> ctypes.CDLL:
         L.gq_gemm_q8_0.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.gq_gemm_q4k_tiles.restype = st
         L.gq_gemm_q4k_tiles.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
-        for name in ("gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted"):
+        for name in ("gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
+                     "gq_moe_gemm_q8_0_input_weighted"):
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
@@ -242,6 +244,15 @@ def gq_moe_gemm_q4k(w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I, E, 
              _ptr(out), T, H, I, E, topk, _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def gq_moe_gemm_q8_0(w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I, E, topk, ws,
+                     ws_bytes=None, stream=None, input_weighted=False):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    f = lib().gq_moe_gemm_q8_0_input_weighted if input_weighted else lib().gq_moe_gemm_q8_0
+    _check(f(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x), _ptr(topk_ids), _ptr(topk_w),
+             _ptr(out), T, H, I, E, topk, _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def gq_dequant_q8_0(w, out32, out16, M, K, stream=None):
     _check(lib().gq_dequant_q8_0(_ptr(w), _ptr(out32), _ptr(out16), M, K, _stream(stream)))
 
@@ -309,16 +320,18 @@ def moe_route(logits, topk: int, renormalize=False, stream=None):
 
 
 def moe_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, H: int, I: int, E: int, ws=None,
-            out=None, stream=None, input_weighted=False):
-    """Mixture-of-experts feed-forward; returns (out [T][H] float16, workspace)."""
+            out=None, stream=None, input_weighted=False, q8_0=False):
+    """Mixture-of-experts feed-forward; returns (out [T][H] float16, workspace).
+    q8_0: the weight stacks are Q8_0 instead of Q4_K."""
     import torch
     T, topk = topk_ids.shape
     need = gq_moe_workspace_bytes(T, H, I, E, topk)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x16.device)
     o = out if out is not None else torch.empty((T, H), dtype=torch.float16, device=x16.device)
-    gq_moe_gemm_q4k(w_gate, w_up, w_down, x16, topk_ids, topk_w, o, T, H, I, E, topk, ws,
-                    stream=stream, input_weighted=input_weighted)
+    f = gq_moe_gemm_q8_0 if q8_0 else gq_moe_gemm_q4k
+    f(w_gate, w_up, w_down, x16, topk_ids, topk_w, o, T, H, I, E, topk, ws, stream=stream,
+      input_weighted=input_weighted)
     return o, ws
 
 

@@ -93,20 +93,22 @@ def test_moe_workspace_and_refusals(L):
     assert gq.gq_moe_workspace_bytes(T, H, 1000, E, k) == 0
     assert gq.gq_moe_workspace_bytes(T, H, I, E, E + 1) == 0
     assert gq.gq_moe_workspace_bytes(T, H, I, 300, 8) == 0
-    f = L.gq_moe_gemm_q4k
     args = [FAKE] * 7
-    st = f(*args, T, H, I, E, k, FAKE, need - 1, None)
-    s, m = status_and_msg(L, st)
-    assert s == "GQ_EWORKSPACE" and str(need) in m
-    st = f(*args, T, H, I, E, k, None, need, None)
-    assert status_and_msg(L, st)[0] == "GQ_EWORKSPACE"
-    st = f(*args, T, H, I, E, 0, FAKE, need, None)
-    assert status_and_msg(L, st)[0] == "GQ_EINVAL"
-    st = f(*args, T, 2000, I, E, k, FAKE, need, None)
-    assert status_and_msg(L, st)[0] == "GQ_ESHAPE"
-    st = f(*args, 1 << 20, H, I, E, k, FAKE, 1 << 62, None)
-    assert status_and_msg(L, st)[0] == "GQ_ESHAPE"
-    assert f(*([None] * 7), 0, H, I, E, k, None, 0, None) == 0
+    for name in ("gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
+                 "gq_moe_gemm_q8_0_input_weighted"):
+        f = getattr(L, name)
+        st = f(*args, T, H, I, E, k, FAKE, need - 1, None)
+        s, m = status_and_msg(L, st)
+        assert s == "GQ_EWORKSPACE" and str(need) in m and name in m
+        st = f(*args, T, H, I, E, k, None, need, None)
+        assert status_and_msg(L, st)[0] == "GQ_EWORKSPACE"
+        st = f(*args, T, H, I, E, 0, FAKE, need, None)
+        assert status_and_msg(L, st)[0] == "GQ_EINVAL"
+        st = f(*args, T, 2000, I, E, k, FAKE, need, None)
+        assert status_and_msg(L, st)[0] == "GQ_ESHAPE"
+        st = f(*args, 1 << 20, H, I, E, k, FAKE, 1 << 62, None)
+        assert status_and_msg(L, st)[0] == "GQ_ESHAPE"
+        assert f(*([None] * 7), 0, H, I, E, k, None, 0, None) == 0
 
 
 def test_gemm_q8_0_refusals(L):

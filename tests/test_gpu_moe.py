@@ -32,18 +32,19 @@ def _dsilu(z):
     return s * (1.0 + z * (1.0 - s))
 
 
-def _setup(seed, T, H, I, E, k):
-    wg = synth.q4k_blocks(seed, 0, E * I, H)
-    wu = synth.q4k_blocks(seed, 1, E * I, H)
-    wd = synth.q4k_blocks(seed, 2, E * H, I)
+def _setup(seed, T, H, I, E, k, fmt=oracle.Q4_K):
+    blocks = synth.q8_0_blocks if fmt == oracle.Q8_0 else synth.q4k_blocks
+    wg = blocks(seed, 0, E * I, H)
+    wu = blocks(seed, 1, E * I, H)
+    wd = blocks(seed, 2, E * H, I)
     x16 = synth.activations_f16(seed, 0, T, H)
     ids, wts64 = oracle.moe_route(synth.router_logits(seed, 0, T, E), k)
     return wg, wu, wd, x16, ids, wts64.astype(np.float32)
 
 
-def _run(wg, wu, wd, x16, ids, wts, H, I, E, input_weighted=False):
+def _run(wg, wu, wd, x16, ids, wts, H, I, E, input_weighted=False, fmt=oracle.Q4_K):
     out, ws = gq.moe_q4k(dev(wg), dev(wu), dev(wd), dev(x16), dev(ids), dev(wts), H, I, E,
-                         input_weighted=input_weighted)
+                         input_weighted=input_weighted, q8_0=fmt == oracle.Q8_0)
     T, k = ids.shape
     off = gq.gq_moe_workspace_offsets(T, H, I, E, k)
     wsh = host(ws)
@@ -71,13 +72,13 @@ def _check_grouping(ids, E, table, sorted_, pos_of):
 
 
 def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks,
-            weight_input=False):
+            weight_input=False, fmt=oracle.Q4_K):
     """Stages (ii)-(iv).  weight_input: the slot weight w scales the expert's
     input, so stage (ii) expects silu(w g) * (w u) with the bounds of g and u
     scaled by w, and stage (iv) sums the slots' d unweighted."""
     T, k = ids.shape
-    gu = I * (H // 256) * 144
-    dn = H * (I // 256) * 144
+    gu = I * oracle.row_bytes(fmt, H)
+    dn = H * oracle.row_bytes(fmt, I)
     worst = {"h": 0.0, "d": 0.0, "out": 0.0}
     for t in toks:
         acc = np.zeros(H)
@@ -88,8 +89,8 @@ def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
             p = pos_of[a]
             assert sorted_[p] == a
             # (ii) h against the oracle's g and u for this token and expert
-            g, Sg = oracle.gemm(oracle.Q4_K, wg[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
-            u, Su = oracle.gemm(oracle.Q4_K, wu[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
+            g, Sg = oracle.gemm(fmt, wg[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
+            u, Su = oracle.gemm(fmt, wu[e * gu:(e + 1) * gu], x16[t:t + 1], I, H)
             g, Sg, u, Su = g[0], Sg[0], u[0], Su[0]
             if weight_input:
                 pw = np.float64(wts[t, s])
@@ -101,7 +102,7 @@ def _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
             assert np.all(err <= bound), ("h", t, s, float((err - bound).max()))
             worst["h"] = max(worst["h"], float((err / bound).max()))
             # (iii) d against Wd_e applied to the GPU's own h
-            dref, Sd = oracle.gemm(oracle.Q4_K, wd[e * dn:(e + 1) * dn],
+            dref, Sd = oracle.gemm(fmt, wd[e * dn:(e + 1) * dn],
                                    h[p:p + 1].view(np.uint16), H, I)
             worst["d"] = max(worst["d"], within(d[p], dref[0], Sd[0], TOL, "d"))
             wc = 1.0 if weight_input else np.float64(wts[t, s])
@@ -227,3 +228,26 @@ def test_moe_input_weighted(T):
     bound = r["Sd"].reshape(len(toks), k, -1).sum(axis=1)
     e2e = float((np.abs(o[toks] - r["out"]) / np.maximum(bound, 1e-300)).max())
     say("  staged", worst, "end-to-end", e2e)
+
+
+@pytest.mark.parametrize("T,weight_input", [(5, False), (100, False), (300, False),
+                                            (700, False), (300, True)])
+def test_moe_q8_0(T, weight_input):
+    """Q8_0 expert stacks (gq_moe_gemm_q8_0 and its input-weighted form): 100,
+    300 and 700 tokens over 8 experts, top-2, take the 32-, 64- and 128-token
+    tiles of the 128-row kernel; 5 tokens over 4 experts checks every token."""
+    E, k = (4, 2) if T == 5 else (8, 2)
+    H, I = 512, 256
+    say("moe q8_0 T", T, "input weighted", weight_input)
+    wg, wu, wd, x16, ids, wts = _setup(67, T, H, I, E, k, fmt=oracle.Q8_0)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E,
+                                           input_weighted=weight_input, fmt=oracle.Q8_0)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    toks = range(T) if T == 5 else sorted(set([0, 1, T // 3, T // 2, T - 2, T - 1]))
+    toks = list(toks)
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks,
+                    weight_input=weight_input, fmt=oracle.Q8_0)
+    r = oracle.moe_ffn(wg, wu, wd, x16[toks], ids[toks], wts[toks], H, I, E,
+                       weight_input=weight_input, fmt=oracle.Q8_0)
+    wsum = np.ones_like(wts[toks]) if weight_input else wts[toks]
+    say("  staged", worst, "end-to-end", _e2e(o[toks], r, wsum))

@@ -529,3 +529,42 @@ def test_moe_combines_experts_with_weights(orc):
             assert np.all(np.abs(r["d"][a] - d) <= 1e-12 * r["Sd"][a])
             acc += np.float32(wts[t, s]).astype(np.float64) * d
         assert np.allclose(r["out"][t], acc, rtol=1e-12, atol=1e-300)
+
+
+def _np_weights_q8_0(w, R, C):
+    blocks = np.ascontiguousarray(w).reshape(-1, 34)
+    d = blocks[:, 0:2].copy().view("<f2").astype(np.float64)
+    q = blocks[:, 2:].view(np.int8).astype(np.float64)
+    return (d * q).astype(np.float32).reshape(R, C).astype(np.float64)
+
+
+@pytest.mark.parametrize("weight_input", [False, True])
+def test_moe_q8_0_against_numpy(orc, weight_input):
+    """Q8_0 expert stacks: every slot's g, u, d against numpy products of the
+    numpy-decoded weights (d * q per 32-weight block, rounded to binary32),
+    and the combine as the weighted (or, input-weighted, unweighted) sum."""
+    T, H, I, E, k = 3, 256, 128, 3, 2
+    wg = synth.q8_0_blocks(34, 0, E * I, H)
+    wu = synth.q8_0_blocks(34, 1, E * I, H)
+    wd = synth.q8_0_blocks(34, 2, E * H, I)
+    x16 = synth.activations_f16(34, 0, T, H)
+    ids = np.array([[0, 2], [1, 0], [2, 1]], np.int32)
+    wts = np.array([[0.6, 0.4], [0.75, 0.25], [0.5, 0.5]], np.float32)
+    r = orc.moe_ffn(wg, wu, wd, x16, ids, wts, H, I, E, weight_input=weight_input, fmt=orc.Q8_0)
+    Wg = _np_weights_q8_0(wg, E * I, H).reshape(E, I, H)
+    Wu = _np_weights_q8_0(wu, E * I, H).reshape(E, I, H)
+    Wd = _np_weights_q8_0(wd, E * H, I).reshape(E, H, I)
+    x = x16.astype(np.float64)
+    for t in range(T):
+        acc = np.zeros(H)
+        for s in range(k):
+            e, a, p = ids[t, s], t * k + s, np.float64(wts[t, s])
+            xin = p * x[t] if weight_input else x[t]
+            g, u = Wg[e] @ xin, Wu[e] @ xin
+            assert np.all(np.abs(r["g"][a] - g) <= 1e-12 * r["Sg"][a])
+            assert np.all(np.abs(r["u"][a] - u) <= 1e-12 * r["Su"][a])
+            d = Wd[e] @ r["h"][a]
+            assert np.all(np.abs(r["d"][a] - d) <= 1e-12 * r["Sd"][a])
+            acc += (1.0 if weight_input else p) * r["d"][a]
+        assert np.allclose(r["out"][t], acc, rtol=1e-12, atol=1e-300)
+    assert np.allclose(r["h"], _silu(r["g"]) * r["u"], rtol=1e-15, atol=0)
