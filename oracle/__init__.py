@@ -13,6 +13,9 @@ they enter the dot product; the fused result equals dequantize-then-dot.
 Parity pins: every function here is pinned by tests marked ``not gpu``
 (hand-built blocks, closed forms, exhaustive binary16 decode against numpy,
 an independently written numpy unpacker, brute force and invariants).  The
+8-bit activation blocks (``quantize_q8k``) and the integer-dot product over
+them (``gemv_q4k_q8k``) follow a reading of a block the pages name but do not
+define, pinned by closed forms, rounding bounds and numpy.  The
 MoE readings (SwiGLU between the expert projections, top-k softmax weights
 used without renormalisation) are readings, not pinned by the pages.
 """
@@ -70,6 +73,8 @@ def lib():
         L.orc_swiglu.argtypes = [vp, vp, i64, vp]
         L.orc_moe_ffn.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                   vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+        L.orc_quantize_q8k.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.orc_gemv_q4k_q8k.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -240,3 +245,31 @@ def moe_ffn(w_gate, w_up, w_down, x16, ids, wts, H: int, I: int, E: int,
                       _p(r["g"]), _p(r["u"]), _p(r["h"]), _p(r["d"]), _p(r["out"]),
                       _p(r["Sg"]), _p(r["Su"]), _p(r["Sd"]), 1 if weight_input else 0)
     return r
+
+
+def quantize_q8k(x, K: int):
+    """Activations as 8-bit blocks of 256: (q int8 [B][K], d float32 [B][K/256],
+    bsum int32 [B][K/32]), every step in binary32."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32).reshape(-1, K))
+    assert K % 256 == 0
+    B = x.shape[0]
+    q = np.empty((B, K), np.int8)
+    d = np.empty((B, K // 256), np.float32)
+    bs = np.empty((B, K // 32), np.int32)
+    lib().orc_quantize_q8k(_p(x), B, K, _p(q), _p(d), _p(bs))
+    return q, d, bs
+
+
+def gemv_q4k_q8k(w, q, d, M: int, K: int, rows=None):
+    """y[b][i] = sum_k w_exact[rows[i]][k] d_b q_b[k] (binary64) and its bound S."""
+    w = _u8(w)
+    _check(Q4_K, w, M, K)
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.int8).reshape(-1, K))
+    B = q.shape[0]
+    d = np.ascontiguousarray(np.asarray(d, dtype=np.float32).reshape(B, K // 256))
+    rows = _idx(rows)
+    nr = M if rows is None else rows.size
+    y = np.empty((B, nr), np.float64)
+    S = np.empty((B, nr), np.float64)
+    lib().orc_gemv_q4k_q8k(_p(w), _p(q), _p(d), M, K, B, _p(rows), nr, _p(y), _p(S))
+    return y, S

@@ -471,3 +471,85 @@ void orc_moe_ffn(int fmt, const uint8_t *w_gate, const uint8_t *w_up, const uint
     free(su);
     free(sd);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Activations as 8-bit blocks (the Q8_K form of the integer-dot path)       */
+/* ------------------------------------------------------------------------ */
+
+/* The pages name llama.cpp's practice of quantizing the activations to Q8_K
+ * before the dot product (page "Frink Inference: the Rust alternative to
+ * llama.cpp", the item on K-quant logits drifting) without defining the
+ * block.  Reading: per 256 consecutive activations of a row, amax = max |x|,
+ * code q = x * (127 / amax) rounded to nearest (ties to even) and clamped to
+ * [-127, 127], scale d = amax / 127; every step in binary32.  A block of zeros
+ * has d = 0 and q = 0.  bsum[j] is the sum of the 32 codes of sub-block j.
+ *   x [B][K] binary32; q [B][K]; d [B][K/256]; bsum [B][K/32]. */
+void orc_quantize_q8k(const float *x, int64_t B, int64_t K, int8_t *q, float *d, int32_t *bsum)
+{
+    int64_t nsb = K / QK_K;
+    for (int64_t b = 0; b < B; b++) {
+        for (int64_t s = 0; s < nsb; s++) {
+            const float *v = x + b * K + s * QK_K;
+            int8_t *qo = q + b * K + s * QK_K;
+            float amax = 0.0f;
+            for (int i = 0; i < QK_K; i++) {
+                float a = fabsf(v[i]);
+                if (a > amax)
+                    amax = a;
+            }
+            float iscale = amax > 0.0f ? 127.0f / amax : 0.0f;
+            d[b * nsb + s] = amax / 127.0f;
+            for (int i = 0; i < QK_K; i++) {
+                float t = v[i] * iscale;
+                float r = rintf(t);
+                if (r > 127.0f)
+                    r = 127.0f;
+                if (r < -127.0f)
+                    r = -127.0f;
+                qo[i] = (int8_t)r;
+            }
+            for (int j = 0; j < QK_K / 32; j++) {
+                int32_t acc = 0;
+                for (int i = 0; i < 32; i++)
+                    acc += qo[32 * j + i];
+                bsum[b * (K / 32) + s * (QK_K / 32) + j] = acc;
+            }
+        }
+    }
+}
+
+/* y[b][i] = sum_k w(r, k) * (d_b[k / 256] * q_b[k]) for r = rows[i] (all rows
+ * if rows is NULL), in binary64, with w the exact Q4_K weight
+ * d * sc * q - dmin * m (not rounded to binary32: the integer-dot form scales
+ * exact integer sums).  S[b][i] = sum_k (|d sc q| + |dmin m|) * |d_b q_b[k]|,
+ * the magnitude against which the kernel's binary32 scaling rounds. */
+void orc_gemv_q4k_q8k(const uint8_t *w, const int8_t *q, const float *d, int64_t M, int64_t K,
+                      int64_t B, const int64_t *rows, int64_t nr, double *y, double *S)
+{
+    int64_t nsb = K / QK_K;
+    (void)M;
+    for (int64_t i = 0; i < nr; i++) {
+        int64_t r = rows ? rows[i] : i;
+        for (int64_t b = 0; b < B; b++) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t s = 0; s < nsb; s++) {
+                const uint8_t *blk = w + (r * nsb + s) * Q4_K_BYTES;
+                double dd = orc_half_to_double(le16(blk));
+                double dm = orc_half_to_double(le16(blk + 2));
+                double xs = (double)d[b * nsb + s];
+                for (int k = 0; k < QK_K; k++) {
+                    int sc, m;
+                    q4k_scale_min(blk + 4, k / 32, &sc, &m);
+                    double a = dd * (double)sc * (double)q4k_quant(blk + 16, k);
+                    double c = dm * (double)m;
+                    double xv = xs * (double)q[b * K + s * QK_K + k];
+                    acc += (a - c) * xv;
+                    mag += (fabs(a) + fabs(c)) * fabs(xv);
+                }
+            }
+            y[b * nr + i] = acc;
+            if (S)
+                S[b * nr + i] = mag;
+        }
+    }
+}

@@ -568,3 +568,93 @@ def test_moe_q8_0_against_numpy(orc, weight_input):
             acc += (1.0 if weight_input else p) * r["d"][a]
         assert np.allclose(r["out"][t], acc, rtol=1e-12, atol=1e-300)
     assert np.allclose(r["h"], _silu(r["g"]) * r["u"], rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# Activations as 8-bit blocks and the integer-dot product
+# ---------------------------------------------------------------------------
+
+def test_quantize_q8k_closed_forms(orc):
+    """A block of integers in [-127, 127] that holds 127 has scale 127/127 = 1
+    and keeps its values as codes (ties 2.5 -> 2, 3.5 -> 4, -2.5 -> -2 go to
+    even); a constant block codes to 127 with scale c/127; a zero block has
+    scale 0 and zero codes; sub-block sums are the sums of the 32 codes."""
+    K = 768
+    x = np.zeros((1, K), np.float32)
+    blk = np.arange(-128, 128, dtype=np.float32)
+    blk[0] = 127.0
+    blk[1:5] = [2.5, 3.5, -2.5, -0.5]
+    x[0, :256] = blk
+    x[0, 256:512] = np.float32(0.3)
+    q, d, bs = orc.quantize_q8k(x, K)
+    assert d[0, 0] == 1.0 and d[0, 2] == 0.0
+    expect = blk.copy()
+    expect[1:5] = [2, 4, -2, 0]
+    assert np.array_equal(q[0, :256].astype(np.float32), expect)
+    assert np.all(q[0, 256:512] == 127)
+    assert d[0, 1] == np.float32(0.3) / np.float32(127)
+    assert np.all(q[0, 512:] == 0)
+    assert np.array_equal(bs[0], q[0].reshape(-1, 32).astype(np.int64).sum(axis=1))
+    assert bs[0, 8] == 127 * 32
+
+
+def test_quantize_q8k_bounds_and_scaling(orc):
+    """Random blocks: codes in [-127, 127] with 127 reached in magnitude, the
+    rounding error |x - d q| within half a step (plus the binary32 rounding
+    of the scale), and power-of-two scaling of x leaves the codes unchanged
+    and scales d exactly."""
+    B, K = 3, 1024
+    x = synth.activations_f32(40, 0, B, K)
+    x[1, 256:512] *= np.float32(1e-30)
+    x[2, 512:768] *= np.float32(1e30)
+    q, d, bs = orc.quantize_q8k(x, K)
+    qb = q.reshape(B, -1, 256).astype(np.int64)
+    assert np.all(np.abs(qb).max(axis=2) == 127)
+    step = np.repeat(d.astype(np.float64), 256, axis=1)
+    err = np.abs(x.astype(np.float64) - step * q)
+    assert np.all(err <= step * (0.5 + 2.0 ** -16))
+    q2, d2, _ = orc.quantize_q8k(x * np.float32(2.0 ** 20), K)
+    assert np.array_equal(q2, q) and np.array_equal(d2, d * np.float32(2.0 ** 20))
+
+
+def test_gemv_q4k_q8k_against_numpy(orc):
+    """The integer-dot product against numpy: exact fp64 weights from the
+    independent table decoder times the decoded activations d * q."""
+    M, K, B = 9, 768, 3
+    w = synth.q4k_blocks(41, 0, M, K)
+    x = synth.activations_f32(41, 0, B, K)
+    q, d, _ = orc.quantize_q8k(x, K)
+    dd, dmin, sc, m, qq = np_decode_q4k(w.reshape(-1, 144))
+    W = (dd[:, None] * np.repeat(sc, 32, axis=1) * qq
+         - dmin[:, None] * np.repeat(m, 32, axis=1)).reshape(M, K)
+    xh = np.repeat(d.astype(np.float64), 256, axis=1) * q
+    ref = xh @ W.T
+    y, S = orc.gemv_q4k_q8k(w, q, d, M, K)
+    assert np.all(np.abs(y - ref) <= 1e-12 * S)
+    rows = np.array([8, 0, 4])
+    yr, Sr = orc.gemv_q4k_q8k(w, q, d, M, K, rows=rows)
+    assert np.array_equal(yr, y[:, rows]) and np.array_equal(Sr, S[:, rows])
+
+
+def test_gemv_q4k_q8k_deviation_from_binary32_path(orc):
+    """The documented cost of quantizing activations: against the binary32
+    product, |y_q8 - y| <= sum_k |w_k| |x_k - d q_k| (plus the binary32
+    rounding of the weights in y), and it vanishes when x is already a block
+    of integers with 127 in it."""
+    M, K, B = 16, 1024, 2
+    w = synth.q4k_blocks(42, 0, M, K)
+    x = synth.activations_f32(42, 0, B, K)
+    q, d, _ = orc.quantize_q8k(x, K)
+    y8, _ = orc.gemv_q4k_q8k(w, q, d, M, K)
+    y, S = orc.gemv(orc.Q4_K, w, x, M, K)
+    W = np.abs(np_weights_q4k(w.reshape(-1, 144)).reshape(M, K).astype(np.float64))
+    dx = np.abs(x.astype(np.float64) - np.repeat(d.astype(np.float64), 256, axis=1) * q)
+    bound = dx @ W.T + 2.0 ** -23 * S
+    assert np.all(np.abs(y8 - y) <= bound)
+    xi = np.clip(np.round(x * 40), -127, 127).astype(np.float32)
+    xi[:, ::256] = 127.0
+    qi, di, _ = orc.quantize_q8k(xi, K)
+    assert np.all(di == 1.0) and np.array_equal(qi.astype(np.float32), xi)
+    y8i, S8 = orc.gemv_q4k_q8k(w, qi, di, M, K)
+    yi, Si = orc.gemv(orc.Q4_K, w, xi, M, K)
+    assert np.all(np.abs(y8i - yi) <= 2.0 ** -23 * Si + 1e-12 * S8)
