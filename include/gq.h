@@ -278,6 +278,36 @@ size_t gq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_
 gq_status gq_moe_workspace_offsets(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
                                    size_t off[7]);
 
+/* Opt-in integer-dot path (llama.cpp's evaluation of K-quant products, which
+ * the pages contrast with keeping activations in binary32: page "Frink
+ * Inference: the Rust alternative to llama.cpp", the item on K-quant logits
+ * drifting).  Results move from the binary32 product by up to
+ * sum_k |w_k| |x_k - d q_k|; the binary32 entry points above remain the
+ * default.
+ *
+ * gq_quantize_q8k: activations as 8-bit blocks of 256 (the pages call the
+ * block Q8_K without defining it; read as below).  For every row b < B and
+ * block s < K/256 of x [B][K] binary32:
+ *   amax = max |x|,  d[b][s] = amax / 127,
+ *   q[b][k] = clamp(round_nearest_even(x[b][k] * (127 / amax)), -127, 127),
+ *   bsum[b][k/32] = sum of the 32 codes of each sub-block,
+ * every step in binary32 (an all-zero block has d = 0, q = 0).
+ * q: [B][K] int8; d: [B][K/256] float; bsum: [B][K/32] int32.  Requires
+ * K % 256 == 0 and B*K <= 2^34; x, q, d, bsum 16-byte aligned.  Non-finite
+ * activations are outside the contract. */
+gq_status gq_quantize_q8k(const float *x, int8_t *q, float *d, int32_t *bsum, int64_t B,
+                          int64_t K, void *stream);
+
+/* gq_gemv_q4k_q8k: y[b][r] = sum_k w(r, k) * d[b][k/256] * q[b][k] over a Q4_K
+ * matrix (M rows of K/256 super-blocks) and activations from
+ * gq_quantize_q8k, 1 <= B <= GQ_GEMV_MAX_BATCH.  Per 32-weight sub-block the
+ * sums of q4 * q and of q are exact integers (8-bit dot products); the
+ * scales d * sc, dmin * m and d[b] are applied in binary32.  Error against
+ * the exact value of the same formula: within 1e-5 * sum_k (|d sc q4| +
+ * |dmin m|) |d[b] q[b][k]|.  y: [B][M] float.  Requires K % 256 == 0. */
+gq_status gq_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d, const int32_t *bsum,
+                          float *y, int64_t M, int64_t K, int64_t B, void *stream);
+
 /* Dequantization probes: write every weight of an M x K matrix as binary32
  * (out32, [M][K]) and/or binary16 (out16, [M][K] bits); either may be NULL.
  * Bit-exact with the rounding rule above. */

@@ -1,0 +1,170 @@
+// gemv_q8k.hip -- the opt-in integer-dot matrix-vector product: activations
+// quantized to 8-bit blocks, Q4_K quants multiplied against them with 8-bit
+// dot products.
+//
+// This is llama.cpp's way of evaluating K-quant products, which the pages set
+// against keeping the activations in binary32 (page "Frink Inference: the Rust
+// alternative to llama.cpp", the item on K-quant logits drifting): the
+// activations lose precision to 8-bit codes, so results move by up to
+// sum_k |w_k| |x_k - d q_k|.  The binary32 products elsewhere in this library
+// are the default; this path is separate and opt-in.
+//
+// The activation block (the pages name it Q8_K and do not define it) is read
+// as: 256 consecutive activations of a row, scale d = max|x| / 127 and codes
+// q = x * (127 / max|x|) rounded to nearest even, clamped to [-127, 127], in
+// binary32; a zero block has d = 0.  With it the 32-weight sub-block j of a
+// Q4_K super-block contributes
+//   d_x * ( d * sc_j * sum_i q4_i q_i  -  dmin * m_j * sum_i q_i )
+// where both sums are exact integers (sum_i q_i is the block's precomputed
+// sub-block sum), taken by v_dot4_i32_i8 on four code pairs at a time.
+#include "gq_device.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+namespace {
+
+constexpr int kWaves = 4; // waves per workgroup, both kernels
+
+// One wave per 256-activation block (blocks in row-major order over [B][K]):
+// lane l takes activations 4l..4l+3.
+__global__ __launch_bounds__(64 * kWaves) void quantize_q8k_kernel(
+    const float *__restrict__ x, int8_t *__restrict__ q, float *__restrict__ d,
+    int32_t *__restrict__ bsum, int64_t nblk)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (blk >= nblk) // the whole wave leaves together
+        return;
+    const float4 v = ldf4(x + blk * 256 + 4 * lane);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const float iscale = amax > 0.f ? 127.f / amax : 0.f;
+    auto code = [&](float xv) {
+        const float t = xv * iscale;
+        return (int)fminf(fmaxf(rintf(t), -127.f), 127.f);
+    };
+    const int c0 = code(v.x), c1 = code(v.y), c2 = code(v.z), c3 = code(v.w);
+    reinterpret_cast<uint32_t *>(q + blk * 256)[lane] =
+        (uint32_t)(c0 & 255) | ((uint32_t)(c1 & 255) << 8) | ((uint32_t)(c2 & 255) << 16) |
+        ((uint32_t)(c3 & 255) << 24);
+    // sub-block j is lanes 8j..8j+7
+    int s = c0 + c1 + c2 + c3;
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 4, 64);
+    if ((lane & 7) == 0)
+        bsum[blk * 8 + (lane >> 3)] = s;
+    if (lane == 0)
+        d[blk] = amax / 127.f;
+}
+
+// One wave per weight row, all B activation rows at once.  A lane takes one
+// (super-block, 32-byte quant group) pair at a time: the group holds the low
+// nibbles of sub-block 2g and the high nibbles of sub-block 2g + 1, 64
+// weights, whose 64 activation codes are four 16-byte loads per batch row.
+template <int B>
+__global__ __launch_bounds__(64 * kWaves) void gemv_q4k_q8k_kernel(
+    const uint8_t *__restrict__ w, const int8_t *__restrict__ q, const float *__restrict__ xd,
+    const int32_t *__restrict__ bsum, float *__restrict__ y, int M, int K)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = (int)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (r >= M) // the whole wave leaves together
+        return;
+    const int nsb = K >> 8;
+    const int ntask = 4 * nsb;
+    const uint8_t *wr = w + (int64_t)r * nsb * kQ4kBytes;
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+        acc[b] = 0.f;
+
+    for (int t = lane; t < ntask; t += 64) {
+        const int s = t >> 2, g = t & 3;
+        const uint8_t *blk = wr + (int64_t)s * kQ4kBytes;
+        const uint4 h = ld16(blk);
+        const uint4 qa = ld16(blk + 16 + 32 * g), qb = ld16(blk + 32 + 32 * g);
+        uint32_t sl, ml, sh, mh;
+        q4k_scale_min(h.y, h.z, h.w, 2 * g, sl, ml);
+        q4k_scale_min(h.y, h.z, h.w, 2 * g + 1, sh, mh);
+        const float d = half_to_float(h.x), dmin = half_to_float(h.x >> 16);
+        const uint32_t W[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int8_t *xq = q + (int64_t)b * K + (int64_t)s * 256 + 64 * g;
+            const uint4 x0 = ld16(xq), x1 = ld16(xq + 16), x2 = ld16(xq + 32), x3 = ld16(xq + 48);
+            const uint32_t X[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                    x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+            int lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                lo = __builtin_amdgcn_sdot4((int)(W[i] & 0x0f0f0f0fu), (int)X[i], lo, false);
+                hi = __builtin_amdgcn_sdot4((int)((W[i] >> 4) & 0x0f0f0f0fu), (int)X[8 + i], hi,
+                                            false);
+            }
+            const int2 bs =
+                *reinterpret_cast<const int2 *>(bsum + (int64_t)b * (K >> 5) + 8 * s + 2 * g);
+            // |isum| < 2^23 and |msum| < 2^19: both convert to binary32 exactly
+            const int isum = (int)sl * lo + (int)sh * hi;
+            const int msum = (int)ml * bs.x + (int)mh * bs.y;
+            acc[b] = fmaf(xd[(int64_t)b * nsb + s], d * (float)isum - dmin * (float)msum, acc[b]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float v = wave_sum(acc[b]);
+        if (lane == 0)
+            y[(int64_t)b * M + r] = v;
+    }
+}
+
+template <int B>
+hipError_t gemv_go(const void *w, const int8_t *q, const float *xd, const int32_t *bsum, float *y,
+                   int64_t M, int64_t K, hipStream_t s)
+{
+    const int64_t blocks = (M + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(gemv_q4k_q8k_kernel<B>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s,
+                       static_cast<const uint8_t *>(w), q, xd, bsum, y, (int)M, (int)K);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_quantize_q8k(const float *x, int8_t *q, float *d, int32_t *bsum, int64_t B,
+                               int64_t K, hipStream_t s)
+{
+    const int64_t nblk = B * (K / 256);
+    const int64_t blocks = (nblk + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(quantize_q8k_kernel, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, x, q,
+                       d, bsum, nblk);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d,
+                               const int32_t *bsum, float *y, int64_t M, int64_t K, int B,
+                               hipStream_t s)
+{
+    switch (B) {
+    case 1: return gemv_go<1>(w, q, d, bsum, y, M, K, s);
+    case 2: return gemv_go<2>(w, q, d, bsum, y, M, K, s);
+    case 3: return gemv_go<3>(w, q, d, bsum, y, M, K, s);
+    case 4: return gemv_go<4>(w, q, d, bsum, y, M, K, s);
+    case 5: return gemv_go<5>(w, q, d, bsum, y, M, K, s);
+    case 6: return gemv_go<6>(w, q, d, bsum, y, M, K, s);
+    case 7: return gemv_go<7>(w, q, d, bsum, y, M, K, s);
+    case 8: return gemv_go<8>(w, q, d, bsum, y, M, K, s);
+    case 9: return gemv_go<9>(w, q, d, bsum, y, M, K, s);
+    case 10: return gemv_go<10>(w, q, d, bsum, y, M, K, s);
+    case 11: return gemv_go<11>(w, q, d, bsum, y, M, K, s);
+    case 12: return gemv_go<12>(w, q, d, bsum, y, M, K, s);
+    case 13: return gemv_go<13>(w, q, d, bsum, y, M, K, s);
+    case 14: return gemv_go<14>(w, q, d, bsum, y, M, K, s);
+    case 15: return gemv_go<15>(w, q, d, bsum, y, M, K, s);
+    default: return gemv_go<16>(w, q, d, bsum, y, M, K, s);
+    }
+}
+
+} // namespace gq

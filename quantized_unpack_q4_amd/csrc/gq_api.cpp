@@ -551,6 +551,43 @@ gq_status gq_moe_route(const float *logits, int32_t *topk_ids, float *topk_w, in
                                              renormalize != 0, (hipStream_t)stream));
 }
 
+gq_status gq_quantize_q8k(const float *x, int8_t *q, float *d, int32_t *bsum, int64_t B,
+                          int64_t K, void *stream)
+{
+    static const char fn[] = "gq_quantize_q8k";
+    GQ_TRY(check_dim(fn, "B", B, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    if (B * K > ((int64_t)1 << 34))
+        return fail(GQ_ESHAPE, "%s: B*K = %lld exceeds 2^34 activations", fn, (long long)(B * K));
+    if (B == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "q", q));
+    GQ_TRY(check_ptr(fn, "d", d));
+    GQ_TRY(check_ptr(fn, "bsum", bsum));
+    return launched(fn, gq::launch_quantize_q8k(x, q, d, bsum, B, K, (hipStream_t)stream));
+}
+
+gq_status gq_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d, const int32_t *bsum,
+                          float *y, int64_t M, int64_t K, int64_t B, void *stream)
+{
+    static const char fn[] = "gq_gemv_q4k_q8k";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    if (B < 0 || B > GQ_GEMV_MAX_BATCH)
+        return fail(GQ_EINVAL, "%s: B = %lld is outside [0, %d]", fn, (long long)B,
+                    GQ_GEMV_MAX_BATCH);
+    if (M == 0 || B == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "q", q));
+    GQ_TRY(check_ptr(fn, "d", d));
+    GQ_TRY(check_ptr(fn, "bsum", bsum));
+    GQ_TRY(check_ptr(fn, "y", y));
+    return launched(fn, gq::launch_gemv_q4k_q8k(w, q, d, bsum, y, M, K, (int)B,
+                                                (hipStream_t)stream));
+}
+
 gq_status gq_dequant_q8_0(const void *w, float *out32, uint16_t *out16, int64_t M, int64_t K,
                           void *stream)
 {

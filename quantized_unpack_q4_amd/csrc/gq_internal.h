@@ -86,6 +86,15 @@ struct MoeArgs {
 };
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 
+// Activations as 8-bit blocks of 256 (x [B][K] -> codes [B][K], scales
+// [B][K/256], sub-block sums [B][K/32]) and the Q4_K integer-dot product over
+// them, 1 <= B <= 16.
+hipError_t launch_quantize_q8k(const float *x, int8_t *q, float *d, int32_t *bsum, int64_t B,
+                               int64_t K, hipStream_t s);
+hipError_t launch_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d,
+                               const int32_t *bsum, float *y, int64_t M, int64_t K, int B,
+                               hipStream_t s);
+
 // Top-k routing of T tokens over E <= 256 experts (one wave per token).
 hipError_t launch_moe_route(const float *logits, int32_t *ids, float *wts, int64_t T, int64_t E,
                             int64_t topk, bool renorm, hipStream_t s);

@@ -27,7 +27,7 @@ EXPORTS = (
     "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
     "gq_gemm_q4k_splitk_workspace_bytes",
     "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
-    "gq_moe_gemm_q8_0_input_weighted", "gq_moe_route",
+    "gq_moe_gemm_q8_0_input_weighted", "gq_moe_route", "gq_quantize_q8k", "gq_gemv_q4k_q8k",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
 )
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
+        L.gq_quantize_q8k.restype = st
+        L.gq_quantize_q8k.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+        L.gq_gemv_q4k_q8k.restype = st
+        L.gq_gemv_q4k_q8k.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.gq_moe_route.restype = st
         L.gq_moe_route.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.gq_moe_workspace_bytes.restype = sz
@@ -253,6 +257,15 @@ def gq_moe_gemm_q8_0(w_gate, w_up, w_down, x, topk_ids, topk_w, out, T, H, I, E,
              _ptr(out), T, H, I, E, topk, _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def gq_quantize_q8k(x, q, d, bsum, B, K, stream=None):
+    _check(lib().gq_quantize_q8k(_ptr(x), _ptr(q), _ptr(d), _ptr(bsum), B, K, _stream(stream)))
+
+
+def gq_gemv_q4k_q8k(w, q, d, bsum, y, M, K, B, stream=None):
+    _check(lib().gq_gemv_q4k_q8k(_ptr(w), _ptr(q), _ptr(d), _ptr(bsum), _ptr(y), M, K, B,
+                                 _stream(stream)))
+
+
 def gq_dequant_q8_0(w, out32, out16, M, K, stream=None):
     _check(lib().gq_dequant_q8_0(_ptr(w), _ptr(out32), _ptr(out16), M, K, _stream(stream)))
 
@@ -347,3 +360,14 @@ def dequant(fmt: str, w, M: int, K: int, want32=True, want16=True, stream=None):
     else:
         raise ValueError("unknown format %r" % fmt)
     return o32, o16
+
+
+def quantize_q8k(x, stream=None):
+    """x [B][K] float32 -> (q int8 [B][K], d float32 [B][K/256], bsum int32 [B][K/32])."""
+    import torch
+    B, K = x.shape
+    q = torch.empty((B, K), dtype=torch.int8, device=x.device)
+    d = torch.empty((B, K // 256), dtype=torch.float32, device=x.device)
+    bs = torch.empty((B, K // 32), dtype=torch.int32, device=x.device)
+    gq_quantize_q8k(x, q, d, bs, B, K, stream)
+    return q, d, bs

@@ -154,6 +154,26 @@ def test_gemv_swiglu_refusals(L):
     assert f(None, None, None, None, 0, 256, None) == 0
 
 
+def test_q8k_refusals(L):
+    f = L.gq_quantize_q8k
+    for B, K, code in ((1, 300, "GQ_ESHAPE"), (1, 0, "GQ_EINVAL"), (-1, 256, "GQ_EINVAL"),
+                       (1 << 26, 1 << 10, "GQ_ESHAPE")):
+        s, m = status_and_msg(L, f(FAKE, FAKE, FAKE, FAKE, B, K, None))
+        assert s == code and "gq_quantize_q8k" in m, (B, K, s, m)
+    s, m = status_and_msg(L, f(FAKE, FAKE, MISALIGNED, FAKE, 2, 256, None))
+    assert s == "GQ_EALIGN" and " d " in m + " "
+    assert f(None, None, None, None, 0, 256, None) == 0
+    g = L.gq_gemv_q4k_q8k
+    for M, K, B, code in ((16, 300, 1, "GQ_ESHAPE"), (16, 256, 17, "GQ_EINVAL"),
+                          (-1, 256, 1, "GQ_EINVAL"), (16, 256, -1, "GQ_EINVAL")):
+        s, m = status_and_msg(L, g(FAKE, FAKE, FAKE, FAKE, FAKE, M, K, B, None))
+        assert s == code and "gq_gemv_q4k_q8k" in m, (M, K, B, s, m)
+    s, m = status_and_msg(L, g(FAKE, FAKE, FAKE, MISALIGNED, FAKE, 16, 256, 1, None))
+    assert s == "GQ_EALIGN" and "bsum" in m
+    assert g(None, None, None, None, None, 0, 256, 1, None) == 0
+    assert g(None, None, None, None, None, 16, 256, 0, None) == 0
+
+
 def test_moe_route_refusals(L):
     f = L.gq_moe_route
     for T, E, k, code in ((4, 257, 8, "GQ_EINVAL"), (4, 64, 65, "GQ_EINVAL"), (4, 64, 0, "GQ_EINVAL"),

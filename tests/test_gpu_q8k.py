@@ -1,0 +1,117 @@
+"""Parity of the opt-in integer-dot path with the oracle.
+
+Quantization of the activations: codes, scales and sub-block sums are
+bit-exact with the oracle's (both take every step in binary32).  Product:
+|y - y_ref| <= 1e-5 * S per output, with y_ref the oracle's binary64 value
+of the same formula on the same codes and S = sum_k (|d sc q4| + |dmin m|) *
+|d_x q_k|, the magnitude the kernel's binary32 scaling rounds against.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_unpack_q4_amd import gq, synth
+from tests._gpu import dev, host, say, torch_cuda, within
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def _special_x(B, K, seed):
+    """N(0,1) rows with special blocks: zeros, a constant, integers with
+    rounding ties, and blocks scaled by 1e-30 and 1e30."""
+    x = synth.activations_f32(seed, 0, B, K)
+    nsb = K // 256
+    for b in range(B):
+        s = (b * 5) % nsb
+        kind = b % 5
+        blk = x[b, 256 * s:256 * (s + 1)]
+        if kind == 0:
+            blk[:] = 0
+        elif kind == 1:
+            blk[:] = np.float32(-0.3)
+        elif kind == 2:
+            blk[:] = np.arange(-128, 128, dtype=np.float32)
+            blk[0] = 127
+            blk[1:5] = [2.5, 3.5, -2.5, -0.5]
+        elif kind == 3:
+            blk *= np.float32(1e-30)
+        else:
+            blk *= np.float32(1e30)
+    return x
+
+
+@pytest.mark.parametrize("B,K", [(1, 256), (3, 4096), (16, 14336), (7, 1280)])
+def test_quantize_q8k_bit_exact(B, K):
+    say("quantize q8k", B, K)
+    x = _special_x(B, K, 70 + B)
+    q, d, bs = gq.quantize_q8k(dev(x))
+    qr, dr, bsr = oracle.quantize_q8k(x, K)
+    assert np.array_equal(host(q), qr)
+    assert np.array_equal(host(d).view(np.uint32), dr.view(np.uint32))
+    assert np.array_equal(host(bs), bsr)
+
+
+def _product(M, K, B, seed, rows_cap=None):
+    torch = torch_cuda()
+    w = synth.q4k_blocks(seed, 0, M, K)
+    x = _special_x(B, K, seed)
+    q, d, bs = gq.quantize_q8k(dev(x))
+    y = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q4k_q8k(dev(w), q, d, bs, y, M, K, B)
+    yg = host(y)
+    assert np.isfinite(yg).all(), "rows not written: %s" % np.argwhere(~np.isfinite(yg))[:5]
+    qh, dh = host(q), host(d)
+    rows = None
+    if rows_cap is not None and M > rows_cap:
+        g = np.random.default_rng(seed)
+        rows = np.sort(g.choice(M, rows_cap, replace=False))
+        rows[0], rows[-1] = 0, M - 1
+    yr, S = oracle.gemv_q4k_q8k(w, qh, dh, M, K, rows=rows)
+    got = yg if rows is None else yg[:, rows]
+    return within(got, yr, S, TOL, "q8k %dx%d B=%d" % (M, K, B))
+
+
+@pytest.mark.parametrize("B", [1, 2, 5, 16])
+def test_gemv_q4k_q8k_ragged(B):
+    """Ragged row counts (partial four-row workgroups), K from one super-block
+    to the maximum, lanes with one or several (super-block, group) tasks."""
+    worst = 0.0
+    for M, K in ((1, 256), (37, 1024), (333, 4096), (61, 14336), (6, 16384)):
+        say("q8k product", M, K, B)
+        worst = max(worst, _product(M, K, B, 71 + M, rows_cap=None))
+    say("  max err/S", worst)
+
+
+@pytest.mark.parametrize("M,K,B", [(14336, 4096, 16), (4096, 14336, 1), (4096, 4096, 4)])
+def test_gemv_q4k_q8k_full_size_sampled(M, K, B):
+    say("q8k full size", M, K, B)
+    say("  max err/S", _product(M, K, B, 72, rows_cap=64))
+
+
+def test_gemv_q4k_q8k_zero_and_one_hot():
+    """Zero activations give exact zeros; a one-hot row (code 127, scale 1)
+    reads out 127 * (d*sc*q - dmin*m) with only the three binary32 roundings
+    of the scaling step (d * isum, dmin * msum, their difference): within
+    2^-21 * S of the oracle's binary64 value."""
+    torch = torch_cuda()
+    M, K = 50, 1024
+    w = synth.q4k_blocks(73, 0, M, K)
+    z = np.zeros((2, K), np.float32)
+    q, d, bs = gq.quantize_q8k(dev(z))
+    y = torch.full((2, M), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q4k_q8k(dev(w), q, d, bs, y, M, K, 2)
+    assert np.all(host(y) == 0)
+    ks = [0, 31, 32, 100, 255, 256, 700, 1023]
+    x = np.zeros((len(ks), K), np.float32)
+    x[np.arange(len(ks)), ks] = 127.0
+    q, d, bs = gq.quantize_q8k(dev(x))
+    y = torch.empty((len(ks), M), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q4k_q8k(dev(w), q, d, bs, y, M, K, len(ks))
+    kb = np.array(ks) // 256
+    assert np.all(host(d)[np.arange(len(ks)), kb] == 1.0)
+    assert np.all(host(q)[np.arange(len(ks)), ks] == 127) and host(q).astype(int).sum() == 127 * len(ks)
+    yr, S = oracle.gemv_q4k_q8k(w, host(q), host(d), M, K)
+    err = np.abs(host(y).astype(np.float64) - yr)
+    assert np.all(err <= 2.0 ** -21 * S), (err / S).max()
