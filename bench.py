@@ -364,6 +364,31 @@ def main():
         extra["gemv_swiglu_%dx%d_b1" % (M, K)] = {
             "fused_us": round(sf * 1e6, 2), "fused_GB/s": round(2 * q4k_bytes(M, K) / sf / 1e9, 1),
             "two_launches_us": round(ss * 1e6, 2)}
+        # the opt-in integer-dot path (8-bit activation codes) on the same
+        # rotated gate matrices at batch 1 and 16, beside the binary32 path
+        q8k = {}
+        for B in (1, 16):
+            xb = torch.from_numpy(synth.activations_f32(1, 3 * M + B, B, K)).cuda()
+            yb = torch.empty((B, M), dtype=torch.float32, device="cuda")
+            xq, xd, xs = gq.quantize_q8k(xb)
+            it["i"] = 0
+
+            def intdot():
+                i = it["i"] % len(gates)
+                it["i"] += 1
+                gq.gq_gemv_q4k_q8k(gates[i], xq, xd, xs, yb, M, K, B, stream)
+
+            def fp32():
+                i = it["i"] % len(gates)
+                it["i"] += 1
+                gq.gq_gemv_q4k(gates[i], xb, yb, M, K, B, stream)
+            si = event_time(torch, stream, intdot, reps=len(gates), warmup=len(gates))
+            sb = event_time(torch, stream, fp32, reps=len(gates), warmup=len(gates))
+            sq = event_time(torch, stream, lambda: gq.gq_quantize_q8k(xb, xq, xd, xs, B, K, stream))
+            q8k["b%d" % B] = {"int_dot_us": round(si * 1e6, 2),
+                              "int_dot_GB/s": round(q4k_bytes(M, K) / si / 1e9, 1),
+                              "binary32_us": round(sb * 1e6, 2), "quantize_us": round(sq * 1e6, 2)}
+        extra["gemv_q4k_q8k_%dx%d" % (M, K)] = q8k
         del stack
         torch.cuda.empty_cache()
         # prefill matrix products
@@ -427,7 +452,7 @@ def main():
         wg = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 0, E * I, H)).cuda()
         wu = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 1, E * I, H)).cuda()
         wd = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 2, E * H, I)).cuda()
-        moe = {}
+        moe, moe_in = {}, {}
         wbytes = 3 * E * q4k_bytes(I, H)
         for T in (256, 2048):
             x16 = torch.from_numpy(synth.activations_f16(MOE_WORKLOAD, 0, T, H)).cuda()
@@ -449,8 +474,28 @@ def main():
             rwt = torch.empty((T, k), dtype=torch.float32, device="cuda")
             s = event_time(torch, stream, lambda: gq.gq_moe_route(lg, rid, rwt, T, E, k, 0, stream))
             moe["T%d" % T]["route_us"] = round(s * 1e6, 2)
+            # the same layer with the weights on the experts' inputs (Llama 4 form)
+            s = event_time(torch, stream, lambda: gq.gq_moe_gemm_q4k(
+                wg, wu, wd, x16, ids_d, wts_d, out, T, H, I, E, k, ws, need, stream,
+                input_weighted=True))
+            moe["T%d" % T]["input_weighted_us"] = round(s * 1e6, 1)
+            moe_in[T] = (x16, ids_d, wts_d, ws, need, out)
         extra["moe_olmoe"] = moe
         del wg, wu, wd
+        # the same layer over Q8_0 expert stacks
+        wg = torch.from_numpy(synth.q8_0_blocks(MOE_WORKLOAD, 0, E * I, H)).cuda()
+        wu = torch.from_numpy(synth.q8_0_blocks(MOE_WORKLOAD, 1, E * I, H)).cuda()
+        wd = torch.from_numpy(synth.q8_0_blocks(MOE_WORKLOAD, 2, E * H, I)).cuda()
+        moe8 = {}
+        wbytes = 3 * E * I * (H // 32) * 34
+        for T, (x16, ids_d, wts_d, ws, need, out) in moe_in.items():
+            s = event_time(torch, stream, lambda: gq.gq_moe_gemm_q8_0(
+                wg, wu, wd, x16, ids_d, wts_d, out, T, H, I, E, k, ws, need, stream))
+            flops = 2.0 * T * k * 3 * H * I
+            moe8["T%d" % T] = {"us": round(s * 1e6, 1), "TFLOP/s": round(flops / s / 1e12, 1),
+                               "weight_GB/s": round(wbytes / s / 1e9, 1)}
+        extra["moe_olmoe_q8_0"] = moe8
+        del wg, wu, wd, moe_in
         # Q8_0 matrix-vector product, 256 x 1024
         wq = torch.from_numpy(synth.q8_0_blocks(0, 0, 256, 1024)).cuda()
         xq = torch.from_numpy(synth.activations_f32(0, 0, 1, 1024)).cuda()
