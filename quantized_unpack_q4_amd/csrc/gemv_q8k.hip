@@ -61,73 +61,98 @@ __global__ __launch_bounds__(64 * kWaves) void quantize_q8k_kernel(
         d[blk] = amax / 127.f;
 }
 
-// One wave per weight row, all B activation rows at once.  A lane takes one
-// (super-block, 32-byte quant group) pair at a time: the group holds the low
-// nibbles of sub-block 2g and the high nibbles of sub-block 2g + 1, 64
-// weights, whose 64 activation codes are four 16-byte loads per batch row.
-template <int B>
+// One wave per R consecutive weight rows, all B activation rows at once.  A
+// lane takes one (super-block, 32-byte quant group) pair at a time: the group
+// holds the low nibbles of sub-block 2g and the high nibbles of sub-block
+// 2g + 1, 64 weights per row, whose 64 activation codes are four 16-byte
+// loads per batch row, loaded once for the R rows.
+template <int B, int R>
 __global__ __launch_bounds__(64 * kWaves) void gemv_q4k_q8k_kernel(
     const uint8_t *__restrict__ w, const int8_t *__restrict__ q, const float *__restrict__ xd,
     const int32_t *__restrict__ bsum, float *__restrict__ y, int M, int K)
 {
     const int lane = threadIdx.x & 63;
-    const int r = (int)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (r >= M) // the whole wave leaves together
+    const int r0 = ((int)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
+    if (r0 >= M) // the whole wave leaves together
         return;
     const int nsb = K >> 8;
     const int ntask = 4 * nsb;
-    const uint8_t *wr = w + (int64_t)r * nsb * kQ4kBytes;
-    float acc[B];
+    const int64_t row_bytes = (int64_t)nsb * kQ4kBytes;
+    // rows past M (last wave of a ragged M) read row M - 1 and are not written
+    const uint8_t *wr[R];
 #pragma unroll
-    for (int b = 0; b < B; ++b)
-        acc[b] = 0.f;
+    for (int j = 0; j < R; ++j)
+        wr[j] = w + (int64_t)min(r0 + j, M - 1) * row_bytes;
+    float acc[R][B];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            acc[j][b] = 0.f;
 
     for (int t = lane; t < ntask; t += 64) {
         const int s = t >> 2, g = t & 3;
-        const uint8_t *blk = wr + (int64_t)s * kQ4kBytes;
-        const uint4 h = ld16(blk);
-        const uint4 qa = ld16(blk + 16 + 32 * g), qb = ld16(blk + 32 + 32 * g);
-        uint32_t sl, ml, sh, mh;
-        q4k_scale_min(h.y, h.z, h.w, 2 * g, sl, ml);
-        q4k_scale_min(h.y, h.z, h.w, 2 * g + 1, sh, mh);
-        const float d = half_to_float(h.x), dmin = half_to_float(h.x >> 16);
-        const uint32_t W[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        uint32_t W[R][8], sl[R], ml[R], sh[R], mh[R];
+        float d[R], dmin[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const uint8_t *blk = wr[j] + (int64_t)s * kQ4kBytes;
+            const uint4 h = ld16(blk);
+            const uint4 qa = ld16(blk + 16 + 32 * g), qb = ld16(blk + 32 + 32 * g);
+            q4k_scale_min(h.y, h.z, h.w, 2 * g, sl[j], ml[j]);
+            q4k_scale_min(h.y, h.z, h.w, 2 * g + 1, sh[j], mh[j]);
+            d[j] = half_to_float(h.x);
+            dmin[j] = half_to_float(h.x >> 16);
+            W[j][0] = qa.x; W[j][1] = qa.y; W[j][2] = qa.z; W[j][3] = qa.w;
+            W[j][4] = qb.x; W[j][5] = qb.y; W[j][6] = qb.z; W[j][7] = qb.w;
+        }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             const int8_t *xq = q + (int64_t)b * K + (int64_t)s * 256 + 64 * g;
             const uint4 x0 = ld16(xq), x1 = ld16(xq + 16), x2 = ld16(xq + 32), x3 = ld16(xq + 48);
             const uint32_t X[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                                     x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-            int lo = 0, hi = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                lo = __builtin_amdgcn_sdot4((int)(W[i] & 0x0f0f0f0fu), (int)X[i], lo, false);
-                hi = __builtin_amdgcn_sdot4((int)((W[i] >> 4) & 0x0f0f0f0fu), (int)X[8 + i], hi,
-                                            false);
-            }
             const int2 bs =
                 *reinterpret_cast<const int2 *>(bsum + (int64_t)b * (K >> 5) + 8 * s + 2 * g);
-            // |isum| < 2^23 and |msum| < 2^19: both convert to binary32 exactly
-            const int isum = (int)sl * lo + (int)sh * hi;
-            const int msum = (int)ml * bs.x + (int)mh * bs.y;
-            acc[b] = fmaf(xd[(int64_t)b * nsb + s], d * (float)isum - dmin * (float)msum, acc[b]);
+            const float dx = xd[(int64_t)b * nsb + s];
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                int lo = 0, hi = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    lo = __builtin_amdgcn_sdot4((int)(W[j][i] & 0x0f0f0f0fu), (int)X[i], lo, false);
+                    hi = __builtin_amdgcn_sdot4((int)((W[j][i] >> 4) & 0x0f0f0f0fu), (int)X[8 + i],
+                                                hi, false);
+                }
+                // |isum| < 2^23 and |msum| < 2^19: both convert to binary32 exactly
+                const int isum = (int)sl[j] * lo + (int)sh[j] * hi;
+                const int msum = (int)ml[j] * bs.x + (int)mh[j] * bs.y;
+                acc[j][b] = fmaf(dx, d[j] * (float)isum - dmin[j] * (float)msum, acc[j][b]);
+            }
         }
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        const float v = wave_sum(acc[b]);
-        if (lane == 0)
-            y[(int64_t)b * M + r] = v;
-    }
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float v = wave_sum(acc[j][b]);
+            if (lane == 0 && r0 + j < M)
+                y[(int64_t)b * M + r0 + j] = v;
+        }
 }
 
+// Rows per wave: the activation codes are loaded once per lane task for R
+// rows, so their cache traffic per weight byte falls as 1/R (measured on
+// 14336 x 4096: batch 16 69 -> 52 us from R = 1 to 4, batch 4 23 -> 21 us;
+// batch 1 is fastest at R = 1).
 template <int B>
 hipError_t gemv_go(const void *w, const int8_t *q, const float *xd, const int32_t *bsum, float *y,
                    int64_t M, int64_t K, hipStream_t s)
 {
-    const int64_t blocks = (M + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(gemv_q4k_q8k_kernel<B>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s,
-                       static_cast<const uint8_t *>(w), q, xd, bsum, y, (int)M, (int)K);
+    constexpr int R = B == 1 ? 1 : B <= 3 ? 2 : 4;
+    const int64_t blocks = (M + R * kWaves - 1) / (R * kWaves);
+    hipLaunchKernelGGL((gemv_q4k_q8k_kernel<B, R>), dim3((unsigned)blocks), dim3(64 * kWaves), 0,
+                       s, static_cast<const uint8_t *>(w), q, xd, bsum, y, (int)M, (int)K);
     return hipGetLastError();
 }
 
