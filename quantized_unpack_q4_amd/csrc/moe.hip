@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restric
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s)
 {
     const int64_t A = a.T * a.topk;
-    // Q8_0 stacks run every regime on the 128-row tile kernel
+    // Q8_0 stacks: weight streaming for few tokens per expert, else the
+    // 128-row tile kernel (the 256 x 256 tiles are Q4_K only)
     const bool big = !a.q8_0 && moe_big_applies(A, a.E, a.H, a.I);
     const int bn = big ? moe_big_token_tile() : moe_token_tile(A, a.E);
     const int max_tiles = (int)((A + bn - 1) / bn + a.E);
@@ -237,7 +238,7 @@ hipError_t launch_moe(const MoeArgs &a, hipStream_t s)
     if (err != hipSuccess)
         return err;
     err = big ? launch_moe_big(a, max_tiles, s)
-              : !a.q8_0 && moe_skinny_applies(A, a.E) ? launch_moe_skinny(a, s)
+              : moe_skinny_applies(A, a.E) ? launch_moe_skinny(a, s)
                                            : launch_moe_gemms(a, bn, max_tiles, s);
     if (err != hipSuccess)
         return err;

@@ -21,6 +21,13 @@
 //   * binary32 accumulation over all of K, then the SwiGLU epilogue
 //     h = binary16(silu(g) * u) (gate/up) or binary32 rows (down), written in
 //     the expert-sorted order the combine step reads.
+// Q8_0 expert stacks take the same schedule: 256 weights of a row are eight
+// 34-byte blocks, 272 bytes starting 16-byte aligned, and each lane owns two
+// whole blocks (its quarter's 64 weights, 68 bytes, four 16-byte and one
+// 4-byte load).  The matrix-core k order inside each 32-weight step is
+// permuted alike for weights and activations, so that step j takes weights
+// 8j .. 8j+7 of every quarter; w16 = binary16(d * q), exact before the one
+// rounding.
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -33,6 +40,11 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
 typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+typedef unsigned int u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef __attribute__((address_space(1))) const u32x4a4 g_u32x4a4;
+typedef __attribute__((address_space(1))) const unsigned int g_u32;
+
+constexpr int kQ8Step = 8 * kQ80Bytes; // 272 bytes: 256 weights of a Q8_0 row
 
 constexpr int SR = 64;  // weight rows per workgroup
 constexpr int ST = 64;  // tokens per chunk (up to 4 groups of 16)
@@ -41,6 +53,7 @@ constexpr int NT = 256; // threads per workgroup
 struct SkinnyParams {
     const uint8_t *w, *w2;  // stacked Q4_K expert matrices (w2: up, gate/up product only)
     const uint16_t *x;      // gate/up: x [T][K]; down: h [A][K] in sorted order
+    // (w, w2: Q8_0 stacks in the Q8 instances)
     void *y;                // gate/up: h [A][M] binary16; down: d [A][M] binary32
     const int32_t *offsets; // expert start positions in sorted order, [E] = total
     const int32_t *sorted;  // assignment t*topk + s at each sorted position
@@ -95,19 +108,64 @@ __device__ __forceinline__ void load_wsb(const uint8_t *row, int sb, int quarter
         w.q[g] = *(g_u32x2 *)(blk + 16 + 32 * g + 8 * quarter);
 }
 
+// Q8_0: this lane's two blocks (2*quarter, 2*quarter + 1) of one 256-weight
+// step, as 17 dwords: D[0] = scale 0 and quants 0, 1; quants 2..31 of block 0
+// end in the low half of D[8], whose high half is scale 1; D[9..16] are the
+// 32 quants of block 1.
+struct WSb8 {
+    uint32_t D[17];
+};
+
+__device__ __forceinline__ void load_wsb8(const uint8_t *row, int sb, int quarter, WSb8 &w)
+{
+    const uint8_t *p = row + (size_t)sb * kQ8Step + 68 * quarter;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4a4 v = *(g_u32x4a4 *)(p + 16 * i);
+        w.D[4 * i] = v.x;
+        w.D[4 * i + 1] = v.y;
+        w.D[4 * i + 2] = v.z;
+        w.D[4 * i + 3] = v.w;
+    }
+    w.D[16] = *(g_u32 *)(p + 64);
+}
+
+// Eight binary16 weights binary16(d * q) from eight signed quant bytes; the
+// byte is converted as (q ^ 0x80) - 128 through an unsigned conversion, and
+// d * u - 128 d is exact in binary32 (at most 19 significant bits).
+__device__ __forceinline__ half8_t deq8(uint32_t q0, uint32_t q1, float d)
+{
+    const uint32_t a = q0 ^ 0x80808080u, b = q1 ^ 0x80808080u;
+    const float o = -128.f * d;
+    const uint4 v = make_uint4(
+        pack_half2(fmaf(d, ubyte_to_float<0>(a), o), fmaf(d, ubyte_to_float<1>(a), o)),
+        pack_half2(fmaf(d, ubyte_to_float<2>(a), o), fmaf(d, ubyte_to_float<3>(a), o)),
+        pack_half2(fmaf(d, ubyte_to_float<0>(b), o), fmaf(d, ubyte_to_float<1>(b), o)),
+        pack_half2(fmaf(d, ubyte_to_float<2>(b), o), fmaf(d, ubyte_to_float<3>(b), o)));
+    return __builtin_bit_cast(half8_t, v);
+}
+
+template <bool Q8> struct WeightSet {
+    typedef WSb type;
+};
+template <> struct WeightSet<true> {
+    typedef WSb8 type;
+};
+
 // One chunk of up to 16*NG tokens of expert e: positions [p0, p0 + nc) of the
 // sorted list.
-template <int MODE, int NG>
+template <int MODE, int NG, bool Q8>
 __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, int nc,
                                           _Float16 *xs0, _Float16 *xs1)
 {
+    typedef typename WeightSet<Q8>::type WS;
     constexpr int NMAT = MODE == 0 ? 2 : 1;
     constexpr int NDMA = NG * 2; // direct-to-LDS copies per wave per super-block
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, quarter = lane >> 4;
     const int K = p.K, M = p.M, nsb = K >> 8;
-    const size_t rowb = (size_t)(K >> 8) * kQ4kBytes;
+    const size_t rowb = (size_t)(K >> 8) * (Q8 ? kQ8Step : kQ4kBytes);
     const int row = (int)blockIdx.x * SR + wave * 16 + col;
 
     const uint8_t *wrow[NMAT];
@@ -139,6 +197,36 @@ __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, 
 #pragma unroll
         for (int g = 0; g < NG; ++g)
             acc[m][g] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Q8_0: step j pairs weights 64*quarter + 8j .. +7 of every row with the
+    // activations of the same k, 16-byte chunk 8*quarter + j of the slice
+    auto compute8 = [&](const _Float16 *buf, const WSb8 (&w)[NMAT]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            half8_t bop[NMAT];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const uint32_t *D = w[m].D;
+                if (j < 4)
+                    bop[m] = deq8(__builtin_amdgcn_alignbyte(D[2 * j + 1], D[2 * j], 2),
+                                  __builtin_amdgcn_alignbyte(D[2 * j + 2], D[2 * j + 1], 2),
+                                  half_to_float(D[0] & 0xffffu));
+                else
+                    bop[m] = deq8(D[2 * j + 1], D[2 * j + 2], half_to_float(D[8] >> 16));
+            }
+            const int c = 8 * quarter + j;
+#pragma unroll
+            for (int tg = 0; tg < NG; ++tg) {
+                const int t = 16 * tg + col;
+                const half8_t a =
+                    *reinterpret_cast<const half8_t *>(buf + 256 * t + 8 * (c ^ (t & 31)));
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+                    acc[m][tg] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[m], acc[m][tg], 0, 0, 0);
+            }
+        }
+    };
 
     auto compute = [&](const _Float16 *buf, const WSb (&w)[NMAT]) {
         float sl[NMAT][8], ol[NMAT][8];
@@ -205,11 +293,24 @@ __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, 
 
     // the previous chunk's readers are done with both buffers
     __syncthreads();
-    WSb wa[NMAT], wb[NMAT];
-    issue_x(0, xs0);
+    auto load_w = [&](int sb, WS(&w)[NMAT]) {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-        load_wsb(wrow[m], 0, quarter, wa[m]);
+        for (int m = 0; m < NMAT; ++m) {
+            if constexpr (Q8)
+                load_wsb8(wrow[m], sb, quarter, w[m]);
+            else
+                load_wsb(wrow[m], sb, quarter, w[m]);
+        }
+    };
+    auto compute_w = [&](const _Float16 *buf, const WS(&w)[NMAT]) {
+        if constexpr (Q8)
+            compute8(buf, w);
+        else
+            compute(buf, w);
+    };
+    WS wa[NMAT], wb[NMAT];
+    issue_x(0, xs0);
+    load_w(0, wa);
     // two super-blocks per iteration so that buffers and register sets stay fixed
     for (int sb = 0; sb < nsb; sb += 2) {
         // retire this wave's copies and weight loads of super-block sb, then
@@ -218,22 +319,18 @@ __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, 
         __builtin_amdgcn_s_barrier();
         if (sb + 1 < nsb) {
             issue_x(sb + 1, xs1);
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-                load_wsb(wrow[m], sb + 1, quarter, wb[m]);
+            load_w(sb + 1, wb);
         }
-        compute(xs0, wa);
+        compute_w(xs0, wa);
         if (sb + 1 >= nsb)
             break;
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
         if (sb + 2 < nsb) {
             issue_x(sb + 2, xs0);
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-                load_wsb(wrow[m], sb + 2, quarter, wa[m]);
+            load_w(sb + 2, wa);
         }
-        compute(xs1, wb);
+        compute_w(xs1, wb);
     }
 
     // element i of group tg: token 16*tg + 4*quarter + i, weight row `row`
@@ -256,7 +353,7 @@ __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, 
         }
 }
 
-template <int MODE>
+template <int MODE, bool Q8>
 __global__ __launch_bounds__(NT, 2) void moe_skinny_kernel(SkinnyParams p)
 {
     __shared__ __attribute__((aligned(16))) _Float16 xs0[ST * 256];
@@ -266,10 +363,10 @@ __global__ __launch_bounds__(NT, 2) void moe_skinny_kernel(SkinnyParams p)
     for (int c0 = begin; c0 < end; c0 += ST) {
         const int nc = end - c0 < ST ? end - c0 : ST;
         switch ((nc + 15) >> 4) {
-        case 1: run_chunk<MODE, 1>(p, e, c0, nc, xs0, xs1); break;
-        case 2: run_chunk<MODE, 2>(p, e, c0, nc, xs0, xs1); break;
-        case 3: run_chunk<MODE, 3>(p, e, c0, nc, xs0, xs1); break;
-        default: run_chunk<MODE, 4>(p, e, c0, nc, xs0, xs1); break;
+        case 1: run_chunk<MODE, 1, Q8>(p, e, c0, nc, xs0, xs1); break;
+        case 2: run_chunk<MODE, 2, Q8>(p, e, c0, nc, xs0, xs1); break;
+        case 3: run_chunk<MODE, 3, Q8>(p, e, c0, nc, xs0, xs1); break;
+        default: run_chunk<MODE, 4, Q8>(p, e, c0, nc, xs0, xs1); break;
         }
     }
 }
@@ -297,9 +394,14 @@ hipError_t launch_moe_skinny(const MoeArgs &a, hipStream_t s)
     p.y = a.ws + a.off[4];
     p.M = (int)a.I;
     p.K = (int)a.H;
-    p.expert_bytes = a.I * (a.H / kQ4kWeights) * kQ4kBytes;
-    hipLaunchKernelGGL(moe_skinny_kernel<0>, dim3((unsigned)(a.I / SR), (unsigned)a.E), dim3(NT),
-                       0, s, p);
+    p.expert_bytes = a.q8_0 ? a.I * (a.H / kQ80Weights) * kQ80Bytes
+                            : a.I * (a.H / kQ4kWeights) * kQ4kBytes;
+    if (a.q8_0)
+        hipLaunchKernelGGL((moe_skinny_kernel<0, true>), dim3((unsigned)(a.I / SR), (unsigned)a.E),
+                           dim3(NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((moe_skinny_kernel<0, false>), dim3((unsigned)(a.I / SR), (unsigned)a.E),
+                           dim3(NT), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -311,9 +413,14 @@ hipError_t launch_moe_skinny(const MoeArgs &a, hipStream_t s)
     p.y = a.ws + a.off[5];
     p.M = (int)a.H;
     p.K = (int)a.I;
-    p.expert_bytes = a.H * (a.I / kQ4kWeights) * kQ4kBytes;
-    hipLaunchKernelGGL(moe_skinny_kernel<1>, dim3((unsigned)(a.H / SR), (unsigned)a.E), dim3(NT),
-                       0, s, p);
+    p.expert_bytes = a.q8_0 ? a.H * (a.I / kQ80Weights) * kQ80Bytes
+                            : a.H * (a.I / kQ4kWeights) * kQ4kBytes;
+    if (a.q8_0)
+        hipLaunchKernelGGL((moe_skinny_kernel<1, true>), dim3((unsigned)(a.H / SR), (unsigned)a.E),
+                           dim3(NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((moe_skinny_kernel<1, false>), dim3((unsigned)(a.H / SR), (unsigned)a.E),
+                           dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

@@ -230,12 +230,13 @@ def test_moe_input_weighted(T):
     say("  staged", worst, "end-to-end", e2e)
 
 
-@pytest.mark.parametrize("T,weight_input", [(5, False), (100, False), (300, False),
+@pytest.mark.parametrize("T,weight_input", [(5, False), (100, False), (100, True), (300, False),
                                             (700, False), (300, True)])
 def test_moe_q8_0(T, weight_input):
-    """Q8_0 expert stacks (gq_moe_gemm_q8_0 and its input-weighted form): 100,
-    300 and 700 tokens over 8 experts, top-2, take the 32-, 64- and 128-token
-    tiles of the 128-row kernel; 5 tokens over 4 experts checks every token."""
+    """Q8_0 expert stacks (gq_moe_gemm_q8_0 and its input-weighted form): 100
+    tokens over 8 experts, top-2 (25 per expert), stream the weights; 300 and
+    700 take the 64- and 128-token tiles of the 128-row kernel; 5 tokens over
+    4 experts checks every token."""
     E, k = (4, 2) if T == 5 else (8, 2)
     H, I = 512, 256
     say("moe q8_0 T", T, "input weighted", weight_input)
