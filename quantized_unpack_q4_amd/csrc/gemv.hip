@@ -283,6 +283,9 @@ static hipError_t gemv_q8_0_go(const void *w, const float *x, float *y, int64_t 
 hipError_t launch_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K,
                             int B, hipStream_t s)
 {
+    // 2..16 activation rows: matrix cores, when rows are whole pairs of blocks
+    if (B >= 2 && K % 64 == 0)
+        return launch_gemv_q8_0_mfma(w, x, y, M, K, B, s);
     switch (B) {
     case 1: return gemv_q8_0_go<1, 2>(w, x, y, M, K, s);
     case 2: return gemv_q8_0_go<2, 2>(w, x, y, M, K, s);

@@ -86,6 +86,10 @@ struct MoeArgs {
 };
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 
+// Q8_0 products for 2..16 activation rows on the matrix cores (K % 64 == 0).
+hipError_t launch_gemv_q8_0_mfma(const void *w, const float *x, float *y, int64_t M, int64_t K,
+                                 int B, hipStream_t s);
+
 // Activations as 8-bit blocks of 256 (x [B][K] -> codes [B][K], scales
 // [B][K/256], sub-block sums [B][K/32]) and the Q4_K integer-dot product over
 // them, 1 <= B <= 16.

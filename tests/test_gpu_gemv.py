@@ -54,6 +54,47 @@ def test_q8_0_one_hot_exact():
         assert np.array_equal(y[b], w32[:, k]), k
 
 
+@pytest.mark.parametrize("M,K,B", [(1, 64, 2), (17, 128, 5), (100, 4096, 16), (61, 14336, 3),
+                                   (333, 1024, 8), (12300, 256, 7)])
+def test_q8_0_matrix_core_ragged(M, K, B):
+    """Batch 2..16 with K % 64 == 0 (the matrix-core kernel): rows that leave a
+    partial 16-row group (12300 rows: a partial 32-row group of the two-tile
+    form), K from one pair of blocks to the maximum, and activation rows
+    scaled from 1e-30 to 1e30 plus an all-zero row."""
+    say("q8_0 mfma gemv", M, K, B)
+    w = synth.q8_0_blocks(83, M, M, K)
+    x = synth.activations_f32(83, M + B, B, K)
+    scales = np.array([1e-30, 1e-8, 1.0, 3e4, 1e12, 1e30, 0.0, 7.0] * 2, np.float32)[:B]
+    x = (x * scales[:, None]).astype(np.float32)
+    y = _gemv("q8_0", dev(w), x, M, K)
+    yr, S = oracle.gemv(oracle.Q8_0, w, x, M, K)
+    r = within(y, yr, S, TOL, "q8_0 mfma %dx%d B=%d" % (M, K, B))
+    if B > 6:
+        assert np.all(y[6] == 0)
+    say("  max err/S", r)
+
+
+@pytest.mark.parametrize("M,K,B", [(14336, 4096, 16), (4096, 14336, 4)])
+def test_q8_0_matrix_core_full_size_sampled(M, K, B):
+    """Decode shapes at batch 4 and 16, 64 sampled rows, and the same bits on a
+    second call."""
+    torch = torch_cuda()
+    say("q8_0 mfma gemv full", M, K, B)
+    w = synth.q8_0_blocks(84, M, M, K)
+    x = synth.activations_f32(84, M, B, K)
+    wd, xd = dev(w), dev(x)
+    y = torch.empty((B, M), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q8_0(wd, xd, y, M, K, B)
+    y1 = host(y).copy()
+    gq.gq_gemv_q8_0(wd, xd, y, M, K, B)
+    assert np.array_equal(y1.view(np.uint32), host(y).view(np.uint32))
+    g = np.random.default_rng(84)
+    rows = np.sort(g.choice(M, 64, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    yr, S = oracle.gemv(oracle.Q8_0, w, x, M, K, rows=rows)
+    say("  max err/S", within(y1[:, rows], yr, S, TOL, "q8_0 mfma full %dx%d" % (M, K)))
+
+
 # -- Q4_K ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,B", [(1, 256, 1), (37, 1024, 1), (5, 512, 2), (131, 2048, 3),
