@@ -74,7 +74,11 @@ typedef enum gq_status {
 /* Q8_0 matrix-vector product, binary32 activations:
  *   y[b][r] = sum_k w[r][k] * x[b][k]  for r < M, b < B, accumulated in binary32.
  * w: M rows of K/32 Q8_0 blocks (M*K/32*34 bytes).  x: [B][K] float.  y: [B][M] float.
- * Requires K % 32 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH. */
+ * Requires K % 32 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH.  With B >= 2 and
+ * K % 64 == 0 the block sums run on the matrix cores with x carried as a
+ * binary16 hi + lo pair scaled per activation row and 32-weight block: x is
+ * kept to 2^-24 of the largest |x| of its block, the products are exact and
+ * the sums binary32.  The result does not depend on B or on the other rows. */
 gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                        void *stream);
 
