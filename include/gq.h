@@ -78,7 +78,8 @@ typedef enum gq_status {
  * K % 64 == 0 the block sums run on the matrix cores with x carried as a
  * binary16 hi + lo pair scaled per activation row and 32-weight block: x is
  * kept to 2^-24 of the largest |x| of its block, the products are exact and
- * the sums binary32.  The result does not depend on B or on the other rows. */
+ * the sums binary32.  Within 2 <= B <= 16 an activation row's result does not
+ * depend on B or on the other rows (B = 1 runs another kernel). */
 gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                        void *stream);
 
