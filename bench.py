@@ -505,6 +505,25 @@ def main():
         s = event_time(torch, stream, lambda: gq.gq_gemv_q8_0(wq, xq, yq, 256, 1024, 1, stream),
                        warm_s=0.0)
         extra["gemv_q8_0_256x1024_b1_us"] = round(s * 1e6, 2)
+        # Q8_0 matrix-vector products at a decode shape, batch 1, 4 and 16,
+        # rotated over 8 copies of the weights (272 MB, past the caches)
+        M, K = 14336, 4096
+        w8 = [torch.from_numpy(synth.q8_0_blocks(0, 1, M, K)).cuda()]
+        w8 += [w8[0].clone() for _ in range(7)]
+        q80 = {}
+        for B in (1, 4, 16):
+            xb = torch.from_numpy(synth.activations_f32(0, 2 + B, B, K)).cuda()
+            yb = torch.empty((B, M), dtype=torch.float32, device="cuda")
+            it = {"i": 0}
+
+            def q8call():
+                gq.gq_gemv_q8_0(w8[it["i"] % 8], xb, yb, M, K, B, stream)
+                it["i"] += 1
+            s = event_time(torch, stream, q8call, reps=48, warmup=16)
+            q80["b%d" % B] = {"us": round(s * 1e6, 2),
+                              "GB/s": round(w8[0].numel() / s / 1e9, 1)}
+        extra["gemv_q8_0_%dx%d" % (M, K)] = q80
+        del w8
 
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
