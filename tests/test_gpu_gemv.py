@@ -30,7 +30,7 @@ def _gemv(fmt, w_d, x, M, K):
 # -- Q8_0 ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,B", [(256, 1024, 1), (1, 32, 1), (7, 96, 3), (33, 160, 16),
-                                   (130, 2048, 2)])
+                                   (130, 2048, 2), (8195, 96, 1)])
 def test_q8_0_parity(M, K, B):
     say("q8_0 gemv", M, K, B)
     w = synth.q8_0_blocks(80, M, M, K)
