@@ -304,6 +304,29 @@ def main():
             "weight_GB/s": round(stack.weight_bytes / s224 / 1e9, 1)}
         del g1
 
+        # one GPU's share of the stack under 8-way tensor parallelism: q, k, v,
+        # gate, up split by output rows (the first M/8 rows), o and down by K
+        # at super-block boundaries (the first K/8 of each row), all 224
+        # shards in one launch
+        itS, shard_bytes = [], 0
+        for name, M, K, t, w in stack.mats:
+            if name in ("o", "down"):
+                ks = K // 8
+                ws = w.view(M, K // 256, 144)[:, :ks // 256, :].contiguous().view(-1)
+                Ms, Ks = M, ks
+            else:
+                Ms, Ks = M // 8, K
+                ws = w[:q4k_bytes(Ms, K)]
+            x = torch.from_numpy(synth.activations_f32(STACK_WORKLOAD, 100 * t + 1, 1, Ks)).cuda()
+            itS.append((ws, x, torch.empty((1, Ms), dtype=torch.float32, device="cuda"), Ms, Ks))
+            shard_bytes += q4k_bytes(Ms, Ks)
+        tabS = gq.GemvTable(itS)
+        s = event_time(torch, stream, lambda: tabS.run(stream), reps=max(10, args.steps))
+        extra["stack_b1_tp8_shard_one_launch"] = {
+            "us_per_step": round(s * 1e6, 1), "weight_bytes": shard_bytes,
+            "weight_GB/s": round(shard_bytes / s / 1e9, 1)}
+        del tabS, itS
+
         for B in (4, 16):
             # the whole stack at batch B in one launch (gq_gemv_q4k_multi_batched)
             log("stack batch", B)
@@ -481,6 +504,27 @@ def main():
             moe["T%d" % T]["input_weighted_us"] = round(s * 1e6, 1)
             moe_in[T] = (x16, ids_d, wts_d, ws, need, out)
         extra["moe_olmoe"] = moe
+        # one GPU's share under 8-way expert parallelism: experts 0..7 and the
+        # rows an all-to-all dispatch would deliver, one row per (token, local
+        # expert) assignment, routed top-1 to the local expert
+        ep = {}
+        for T in (256, 2048):
+            ids, wts = oracle.moe_route(synth.router_logits(MOE_WORKLOAD, 0, T, E), k)
+            tok, slot = np.nonzero(ids < E // 8)
+            x16 = synth.activations_f16(MOE_WORKLOAD, 0, T, H)[tok]
+            R = len(tok)
+            xs_d = torch.from_numpy(np.ascontiguousarray(x16)).cuda()
+            ids_d = torch.from_numpy(ids[tok, slot].astype(np.int32).reshape(R, 1)).cuda()
+            wts_d = torch.from_numpy(wts[tok, slot].astype(np.float32).reshape(R, 1)).cuda()
+            need = gq.gq_moe_workspace_bytes(R, H, I, E // 8, 1)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+            out = torch.empty((R, H), dtype=torch.float16, device="cuda")
+            s = event_time(torch, stream, lambda: gq.gq_moe_gemm_q4k(
+                wg, wu, wd, xs_d, ids_d, wts_d, out, R, H, I, E // 8, 1, ws, need, stream))
+            ep["T%d" % T] = {"rows": int(R), "us": round(s * 1e6, 1),
+                             "TFLOP/s": round(2.0 * R * 3 * H * I / s / 1e12, 1),
+                             "weight_GB/s": round(3 * (E // 8) * q4k_bytes(I, H) / s / 1e9, 1)}
+        extra["moe_olmoe_ep8_shard"] = ep
         del wg, wu, wd
         # the same layer over Q8_0 expert stacks
         wg = torch.from_numpy(synth.q8_0_blocks(MOE_WORKLOAD, 0, E * I, H)).cuda()

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
 
     auto entry = [&](int i) -> GemvEntry { return table ? table[i] : inline0; };
     int di = 0;
-    while (di + 1 < n && entry(di + 1).byte_begin <= lo)
+    while (di + 1 < n && entry(di + 1).work_begin <= lo)
         ++di;
     GemvEntry e = entry(di);
 
@@ -231,14 +231,14 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
         if (di >= n)
             return;
         e = entry(di);
-        if (e.byte_begin >= hi)
+        if (e.work_begin >= hi)
             return;
         nsb = e.K >> 8;
         rowb = (long long)nsb * kQ4kBytes;
-        const long long rel_lo = lo - e.byte_begin, rel_hi = hi - e.byte_begin;
+        const long long rel_lo = lo - e.work_begin, rel_hi = hi - e.work_begin;
         // rows (pairs of rows) are owned whole: unit of `gr` rows
         const int gr = PAIR ? 2 : 1;
-        const long long mrows = (long long)gr * e.M, unit = gr * rowb;
+        const long long mrows = (long long)gr * e.M, unit = gr * gemv_row_work(e.K);
         const int r_lo = rel_lo <= 0 ? 0 : (int)min(mrows, gr * ((rel_lo + unit - 1) / unit));
         r_end = (int)min(mrows, gr * ((rel_hi + unit - 1) / unit));
         if (r_lo >= r_end)
@@ -456,8 +456,8 @@ hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inlin
 hipError_t launch_gemv_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,
                               int64_t M, int64_t K, hipStream_t s)
 {
-    const GemvEntry e{(const uint8_t *)w_gate, x, h, (int)M, (int)K, 0};
-    const long long total = 2LL * M * (K / 256) * kQ4kBytes;
+    const GemvEntry e{(const uint8_t *)w_gate, x, h, (int)M, (int)K, 0, 0};
+    const long long total = 2LL * M * gemv_row_work(K);
     const int grid = gemv_stream_grid(total, gemv_stream_tiles(2 * M, K));
     hipLaunchKernelGGL((gemv_q4k_stream_kernel<kR, 2, 4, true>), dim3((unsigned)grid), dim3(256),
                        0, s, nullptr, e, 1, total, (const uint8_t *)w_up);

@@ -159,13 +159,13 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
     if (M == 0 || B == 0)
         return GQ_OK;
     if (B == 1 && K <= gq::GemvStreamMaxK) {
-        gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0};
-        const long long total = (long long)M * (K / 256) * 144;
+        gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0, 0};
+        const long long total = (long long)M * gq::gemv_row_work(K);
         const int grid = gq::gemv_stream_grid(total, gq::gemv_stream_tiles(M, K));
         return launched(fn, gq::launch_gemv_stream(nullptr, e, 1, total, grid, (hipStream_t)stream));
     }
     if (B >= 2 && gemv_mfma_fits(M, K, B)) {
-        gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0};
+        gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0, 0};
         const long long total = (long long)M * (K / 256) * 144;
         return launched(fn, gq::launch_gemv_mfma(nullptr, e, 1, total, gq::gemv_mfma_blocks(M),
                                                  (int)B, (hipStream_t)stream));
@@ -173,19 +173,20 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
     return launched(fn, gq::launch_gemv_q4k(w, x, y, M, K, (int)B, (hipStream_t)stream));
 }
 
-// Table of a batch-1 multi-product: a 32-byte header, then n entries laid out
-// as gq::GemvEntry.  The same bytes are read on the host (checks, launch
+// Table of a multi-product: a 40-byte header, then n entries laid out as
+// gq::GemvEntry (48 bytes).  The same bytes are read on the host (checks, launch
 // shape) and on the device (the kernel).
 namespace {
 constexpr uint32_t kTableMagic = 0x544D5147u; // "GQMT"
-constexpr uint32_t kTableVersion = 1;
+constexpr uint32_t kTableVersion = 2;
 struct TableHeader {
     uint32_t magic, version;
     int64_t n;
-    int64_t total_bytes;
+    int64_t total_bytes; // weight bytes of all entries
     int64_t total_tiles;
+    int64_t total_work; // gemv_row_work of all entries
 };
-static_assert(sizeof(TableHeader) == 32, "table header layout");
+static_assert(sizeof(TableHeader) == 40, "table header layout");
 } // namespace
 
 size_t gq_gemv_q4k_multi_table_bytes(int64_t n)
@@ -208,7 +209,7 @@ gq_status gq_gemv_q4k_multi_plan(const gq_gemv_desc *descs, int64_t n, void *tab
     if (table_bytes < gq_gemv_q4k_multi_table_bytes(n))
         return fail(GQ_EWORKSPACE, "%s: table_bytes = %zu is below the required %zu", fn,
                     table_bytes, gq_gemv_q4k_multi_table_bytes(n));
-    int64_t total = 0, tiles = 0;
+    int64_t total = 0, tiles = 0, work = 0;
     for (int64_t i = 0; i < n; ++i) {
         const gq_gemv_desc &d = descs[i];
         char name[64];
@@ -226,17 +227,19 @@ gq_status gq_gemv_q4k_multi_plan(const gq_gemv_desc *descs, int64_t n, void *tab
         snprintf(name, sizeof name, "descs[%lld].y", (long long)i);
         GQ_TRY(check_ptr(fn, name, d.y));
         total += d.M * (d.K / 256) * 144;
+        work += d.M * gq::gemv_row_work(d.K);
         tiles += gq::gemv_stream_tiles(d.M, d.K);
     }
-    TableHeader h{kTableMagic, kTableVersion, n, total, tiles};
+    TableHeader h{kTableMagic, kTableVersion, n, total, tiles, work};
     memcpy(table, &h, sizeof h);
     gq::GemvEntry *ent = reinterpret_cast<gq::GemvEntry *>((uint8_t *)table + sizeof h);
-    int64_t begin = 0;
+    int64_t begin = 0, wbegin = 0;
     for (int64_t i = 0; i < n; ++i) {
         const gq_gemv_desc &d = descs[i];
-        gq::GemvEntry e{(const uint8_t *)d.w, d.x, d.y, (int)d.M, (int)d.K, begin};
+        gq::GemvEntry e{(const uint8_t *)d.w, d.x, d.y, (int)d.M, (int)d.K, begin, wbegin};
         memcpy(&ent[i], &e, sizeof e);
         begin += d.M * (d.K / 256) * 144;
+        wbegin += d.M * gq::gemv_row_work(d.K);
     }
     return GQ_OK;
 }
@@ -254,8 +257,8 @@ gq_status gq_gemv_q4k_multi(const void *table, const void *table_dev, void *stre
     const gq::GemvEntry *dev = reinterpret_cast<const gq::GemvEntry *>(
         (const uint8_t *)table_dev + sizeof(TableHeader));
     const gq::GemvEntry none{};
-    const int grid = gq::gemv_stream_grid(h.total_bytes, h.total_tiles);
-    return launched(fn, gq::launch_gemv_stream(dev, none, (int)h.n, h.total_bytes, grid,
+    const int grid = gq::gemv_stream_grid(h.total_work, h.total_tiles);
+    return launched(fn, gq::launch_gemv_stream(dev, none, (int)h.n, h.total_work, grid,
                                                (hipStream_t)stream));
 }
 
@@ -277,8 +280,8 @@ gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, in
         (const uint8_t *)table_dev + sizeof(TableHeader));
     const gq::GemvEntry none{};
     if (B == 1) {
-        const int grid = gq::gemv_stream_grid(h.total_bytes, h.total_tiles);
-        return launched(fn, gq::launch_gemv_stream(dev, none, (int)h.n, h.total_bytes, grid,
+        const int grid = gq::gemv_stream_grid(h.total_work, h.total_tiles);
+        return launched(fn, gq::launch_gemv_stream(dev, none, (int)h.n, h.total_work, grid,
                                                    (hipStream_t)stream));
     }
     const gq::GemvEntry *ent =

@@ -21,14 +21,32 @@ hipError_t launch_gemv_q4k(const void *w, const float *x, float *y, int64_t M, i
 
 // Persistent batch-1 Q4_K matrix-vector products over a table of matrices.
 constexpr int GemvStreamMaxK = 16384;
+// Work of one row of a matrix-vector product in bytes' worth: its weight
+// bytes, but at least kGemvRowFloor, the time a row takes whatever its length
+// (reduction, epilogue, issue).  The tables split work among workgroups in
+// these units, so that a matrix of short rows (a row-parallel shard with
+// K = 512 has 288-byte rows) does not leave one workgroup with thousands of
+// rows; rows longer than the floor count their bytes alone.  Measured on one
+// GPU's 8-way tensor-parallel share of the decode stack (491 MB, o and down
+// split along K): 299 -> 142 us at batch 1, the whole stack unchanged.  The
+// batch 2-16 kernel splits by bytes (its 128-row blocks amortize the per-row
+// cost; the floor made that share 16% slower).
+constexpr long long kGemvRowFloor = 1152;
+__host__ __device__ inline long long gemv_row_work(long long K)
+{
+    const long long b = (K / 256) * 144;
+    return b > kGemvRowFloor ? b : kGemvRowFloor;
+}
+
 struct GemvEntry {
     const uint8_t *w; // Q4_K weights, M rows of K/256 super-blocks
     const float *x;   // [K]
     float *y;         // [M]
     int M, K;
-    long long byte_begin; // sum of the weight bytes of the entries before this one
+    long long byte_begin; // weight bytes of the entries before this one (batch 2-16 split)
+    long long work_begin; // gemv_row_work of the entries before this one (batch-1 split)
 };
-static_assert(sizeof(GemvEntry) == 40, "table entry layout");
+static_assert(sizeof(GemvEntry) == 48, "table entry layout");
 long long gemv_stream_tiles(int64_t M, int64_t K);
 int gemv_stream_grid(long long total_bytes, long long tiles);
 // table_dev == nullptr: a single matrix given by inline0 (n must be 1)

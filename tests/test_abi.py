@@ -207,7 +207,7 @@ def test_multi_plan_checks_and_layout(L):
     assert gq.gq_gemv_q4k_multi_table_bytes(0) == 0
     n = 3
     nbytes = gq.gq_gemv_q4k_multi_table_bytes(n)
-    assert nbytes == 32 + 40 * n
+    assert nbytes == 40 + 48 * n
     D = (gq.GemvDesc * n)()
     base = 0x100000
     shapes = [(24, 4096), (1, 256), (100, 14336)]
@@ -217,15 +217,24 @@ def test_multi_plan_checks_and_layout(L):
     table = (ctypes.c_uint8 * nbytes)()
     assert L.gq_gemv_q4k_multi_plan(D, n, table, nbytes) == 0
     raw = bytes(table)
-    magic, version, nn, total, tiles = struct.unpack_from("<IIqqq", raw, 0)
-    assert magic == 0x544D5147 and version == 1 and nn == n
+    magic, version, nn, total, tiles, total_work = struct.unpack_from("<IIqqqq", raw, 0)
+    assert magic == 0x544D5147 and version == 2 and nn == n
     sizes = [M * (K // 256) * 144 for M, K in shapes]
     assert total == sum(sizes)
-    begin = 0
+    # batch-1 work split: a row counts max(its bytes, F) for one floor F; the
+    # one-row 256-wide entry (144 bytes) shows F, rows of K >= 4096 keep their
+    # bytes
+    ents = [struct.unpack_from("<QQQiiqq", raw, 40 + 48 * i) for i in range(n)]
+    floor = ents[2][6] - ents[1][6]
+    assert 144 <= floor <= 2304
+    works = [M * max(K // 256 * 144, floor) for M, K in shapes]
+    assert total_work == sum(works) and works[0] == sizes[0] and works[2] == sizes[2]
+    begin = wbegin = 0
     for i, (M, K) in enumerate(shapes):
-        w, x, y, m, k, bb = struct.unpack_from("<QQQiiq", raw, 32 + 40 * i)
-        assert (w, m, k, bb) == (D[i].w, M, K, begin)
+        w, x, y, m, k, bb, wb = ents[i]
+        assert (w, m, k, bb, wb) == (D[i].w, M, K, begin, wbegin)
         begin += sizes[i]
+        wbegin += works[i]
     # refusals name the descriptor
     D[1].K = 300
     st = L.gq_gemv_q4k_multi_plan(D, n, table, nbytes)
