@@ -174,7 +174,8 @@ def event_time(torch, stream, fn, reps=20, warmup=3, warm_s=0.05):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_q4k_stream_decode_stack.md")
 TRAFFIC_SOURCES = ("quantized_unpack_q4_amd/csrc/gemv_stream.hip",
-                   "quantized_unpack_q4_amd/csrc/gq_device.h")
+                   "quantized_unpack_q4_amd/csrc/gq_device.h",
+                   "quantized_unpack_q4_amd/csrc/gq_internal.h")
 
 
 def measured_traffic():
