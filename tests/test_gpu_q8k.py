@@ -73,10 +73,11 @@ def _product(M, K, B, seed, rows_cap=None):
     return within(got, yr, S, TOL, "q8k %dx%d B=%d" % (M, K, B))
 
 
-@pytest.mark.parametrize("B", [1, 2, 5, 16])
+@pytest.mark.parametrize("B", [1, 2, 5, 6, 16])
 def test_gemv_q4k_q8k_ragged(B):
-    """Ragged row counts (partial four-row workgroups), K from one super-block
-    to the maximum, lanes with one or several (super-block, group) tasks."""
+    """Ragged row counts (partial workgroups of either kernel: vector for
+    batch 1-5, int8 matrix cores from 6), K from one super-block to the
+    maximum, lanes or waves with one or several super-blocks."""
     worst = 0.0
     for M, K in ((1, 256), (37, 1024), (333, 4096), (61, 14336), (6, 16384)):
         say("q8k product", M, K, B)
