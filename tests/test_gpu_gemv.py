@@ -30,7 +30,7 @@ def _gemv(fmt, w_d, x, M, K):
 # -- Q8_0 ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,B", [(256, 1024, 1), (1, 32, 1), (7, 96, 3), (33, 160, 16),
-                                   (130, 2048, 2), (8195, 96, 1)])
+                                   (130, 2048, 2), (8195, 96, 1), (8195, 128, 1), (77, 14336, 1)])
 def test_q8_0_parity(M, K, B):
     say("q8_0 gemv", M, K, B)
     w = synth.q8_0_blocks(80, M, M, K)
@@ -93,6 +93,22 @@ def test_q8_0_matrix_core_full_size_sampled(M, K, B):
     rows[0], rows[-1] = 0, M - 1
     yr, S = oracle.gemv(oracle.Q8_0, w, x, M, K, rows=rows)
     say("  max err/S", within(y1[:, rows], yr, S, TOL, "q8_0 mfma full %dx%d" % (M, K)))
+
+
+def test_q8_0_batch1_one_hot_exact():
+    """Batch 1: a one-hot activation reads out the binary32 weight d * q
+    exactly, on a tall matrix (four rows per wave) and a short one (two)."""
+    torch = torch_cuda()
+    for M, K in ((9000, 128), (19, 320)):
+        w = synth.q8_0_blocks(85, M, M, K)
+        w32, _ = oracle.dequant(oracle.Q8_0, w, M, K)
+        wd = dev(w)
+        y = torch.empty((1, M), dtype=torch.float32, device="cuda")
+        for k in (0, 1, 31, 32, 33, 63, 64, K - 1):
+            x = np.zeros((1, K), np.float32)
+            x[0, k] = 1.0
+            gq.gq_gemv_q8_0(wd, dev(x), y, M, K, 1)
+            assert np.array_equal(host(y)[0], w32[:, k]), (M, K, k)
 
 
 # -- Q4_K ------------------------------------------------------------------------
