@@ -306,8 +306,9 @@ gq_status gq_quantize_q8k(const float *x, int8_t *q, float *d, int32_t *bsum, in
 /* gq_gemv_q4k_q8k: y[b][r] = sum_k w(r, k) * d[b][k/256] * q[b][k] over a Q4_K
  * matrix (M rows of K/256 super-blocks) and activations from
  * gq_quantize_q8k, 1 <= B <= GQ_GEMV_MAX_BATCH.  Per 32-weight sub-block the
- * sums of q4 * q and of q are exact integers (8-bit dot products); the
- * scales d * sc, dmin * m and d[b] are applied in binary32.  Error against
+ * sums of q4 * q and of q are exact integers (8-bit dot products at batch
+ * 1-5, the int8 matrix cores at batch 6-16, where the sub-block scales also
+ * apply in int32); the remaining scales are applied in binary32.  Error against
  * the exact value of the same formula: within 1e-5 * sum_k (|d sc q4| +
  * |dmin m|) |d[b] q[b][k]|.  y: [B][M] float.  Requires K % 256 == 0. */
 gq_status gq_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d, const int32_t *bsum,
