@@ -234,7 +234,13 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB five times (the "
                          "reference kernel for scaling hardware byte counters)")
+    ap.add_argument("--stack-batch", type=int, default=1, metavar="B",
+                    help="activation rows of the timed decode-stack step (1 by default; 2-16 "
+                         "time the batched one-launch form, for profiling it)")
     args = ap.parse_args()
+    if not 1 <= args.stack_batch <= 16:
+        print("--stack-batch must be in 1..16", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU: the library runs the hot path on a single MI355X "
               "and has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -253,13 +259,14 @@ def main():
     stream = torch.cuda.Stream()
 
     # the step: all 224 batch-1 products of the stack in one launch
+    SB = args.stack_batch
     items = []
     for _, M, K, t, w in stack.mats:
-        x = torch.from_numpy(synth.activations_f32(STACK_WORKLOAD, 100 * t + 1, 1, K)).cuda()
-        y = torch.empty((1, M), dtype=torch.float32, device="cuda")
+        x = torch.from_numpy(synth.activations_f32(STACK_WORKLOAD, 100 * t + SB, SB, K)).cuda()
+        y = torch.empty((SB, M), dtype=torch.float32, device="cuda")
         items.append((w, x, y, M, K))
-    table = gq.GemvTable(items)
-    alg_bytes = sum(gemv_bytes(M, K, 1) for _, M, K, _, _ in stack.mats)
+    table = gq.GemvTable(items, batch=SB) if SB > 1 else gq.GemvTable(items)
+    alg_bytes = sum(gemv_bytes(M, K, SB) for _, M, K, _, _ in stack.mats)
 
     log("timing %d steps after %d warm-up steps" % (args.steps, args.warmup))
     with torch.cuda.stream(stream):
@@ -283,7 +290,7 @@ def main():
     avg_dur = sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / args.steps
     achieved = alg_bytes / avg_dur / 1e9
 
-    extra = {"stack_b1_one_launch": {"ms_per_step": round(sec * 1e3, 4),
+    extra = {"stack_b%d_one_launch" % SB: {"ms_per_step": round(sec * 1e3, 4),
                                      "kernel_ms_events": round(avg_dur * 1e3, 4)}}
     if args.copy_probe > 0:
         n = args.copy_probe << 20
@@ -586,13 +593,14 @@ def main():
         "dtype": "q4_k weights, f32 activations and accumulation",
         "data": "synthetic (seeded Q4_K blocks and N(0,1) activations)",
         "config": {"workload": "llama3-8b-shaped Q4_K decode stack, 32 layers x 7 GEMVs, "
-                               "batch 1, one launch per step",
+                               "batch %d, one launch per step" % SB,
                    "weight_bytes_per_step": stack_bytes_total(),
-                   "global_batch": 1, "parallelism": "single GPU"},
+                   "global_batch": SB, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "gemv_q4k_stream_kernel (224 products per launch)",
+                     "traffic": measured_traffic() if SB == 1 else None,
+                     "kernel": ("gemv_q4k_stream_kernel" if SB == 1 else "gemv_q4k_mfma_kernel")
+                     + " (224 products per launch)",
                      "avg_launch_us": round(avg_dur * 1e6, 3),
                      "alg_bytes_per_launch": int(alg_bytes)},
         "cpu_baseline": cpu,
