@@ -115,6 +115,19 @@ def test_multi_decode_layer_full_size():
     say("multi layer max err/S", r)
 
 
+def test_multi_tensor_parallel_share():
+    """Two layers of one GPU's 8-way tensor-parallel share (q/k/v/gate/up by
+    rows, o and down by K): thousands of 288-byte rows (K = 512) among long
+    ones, where the work split counts a row as at least a fixed cost; every
+    row written once, sampled rows against the oracle."""
+    shapes = [(512, 4096), (128, 4096), (128, 4096), (4096, 512), (1792, 4096), (1792, 4096),
+              (4096, 1792)] * 2
+    t, h = _table(shapes, 25)
+    t.run()
+    r = _check(t, h, shapes, rows_cap=64, what="tp share")
+    say("multi tp share max err/S", r)
+
+
 def test_single_matrix_batch1_large_k_and_ragged():
     """The single-matrix entry point at batch 1 (same streaming kernel)."""
     torch = torch_cuda()
