@@ -252,3 +252,25 @@ def test_moe_q8_0(T, weight_input):
                        weight_input=weight_input, fmt=oracle.Q8_0)
     wsum = np.ones_like(wts[toks]) if weight_input else wts[toks]
     say("  staged", worst, "end-to-end", _e2e(o[toks], r, wsum))
+
+
+@pytest.mark.parametrize("rows", [261, 2054])
+def test_moe_expert_parallel_share(rows):
+    """One GPU's expert-parallel share as the benchmark runs it: 8 experts,
+    one dispatched row per (token, local expert) pair, top-1 routing with the
+    slot's weight (261 rows stream the weights, 2054 take the large tiles);
+    grouping whole, stages on sampled rows."""
+    H, I, E, k = 2048, 1024, 8, 1
+    say("moe ep share rows", rows)
+    g = np.random.default_rng(rows)
+    wg = synth.q4k_blocks(68, 0, E * I, H)
+    wu = synth.q4k_blocks(68, 1, E * I, H)
+    wd = synth.q4k_blocks(68, 2, E * H, I)
+    x16 = synth.activations_f16(68, 0, rows, H)
+    ids = g.integers(0, E, (rows, 1)).astype(np.int32)
+    wts = g.uniform(0.02, 0.4, (rows, 1)).astype(np.float32)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    toks = sorted(set([0, 1, rows // 3, rows // 2, rows - 2, rows - 1]))
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks)
+    say("  staged", worst)
