@@ -30,7 +30,8 @@ def _gemv(fmt, w_d, x, M, K):
 # -- Q8_0 ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,B", [(256, 1024, 1), (1, 32, 1), (7, 96, 3), (33, 160, 16),
-                                   (130, 2048, 2), (8195, 96, 1), (8195, 128, 1), (77, 14336, 1)])
+                                   (130, 2048, 2), (8195, 96, 1), (8195, 128, 1), (77, 14336, 1),
+                                   (8200, 256, 1), (3, 16384, 1)])
 def test_q8_0_parity(M, K, B):
     say("q8_0 gemv", M, K, B)
     w = synth.q8_0_blocks(80, M, M, K)
@@ -97,9 +98,9 @@ def test_q8_0_matrix_core_full_size_sampled(M, K, B):
 
 def test_q8_0_batch1_one_hot_exact():
     """Batch 1: a one-hot activation reads out the binary32 weight d * q
-    exactly, on a tall matrix (four rows per wave) and a short one (two)."""
+    exactly, on a tall matrix (four rows per wave) and short ones (two)."""
     torch = torch_cuda()
-    for M, K in ((9000, 128), (19, 320)):
+    for M, K in ((9000, 128), (19, 320), (40, 512), (17, 4096)):
         w = synth.q8_0_blocks(85, M, M, K)
         w32, _ = oracle.dequant(oracle.Q8_0, w, M, K)
         wd = dev(w)
