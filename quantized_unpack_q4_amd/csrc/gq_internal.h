@@ -48,7 +48,7 @@ struct GemvEntry {
 };
 static_assert(sizeof(GemvEntry) == 48, "table entry layout");
 long long gemv_stream_tiles(int64_t M, int64_t K);
-int gemv_stream_grid(long long total_bytes, long long tiles);
+int gemv_stream_grid(long long total_work, long long tiles);
 // table_dev == nullptr: a single matrix given by inline0 (n must be 1)
 hipError_t launch_gemv_stream(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
                               long long total_bytes, int grid, hipStream_t s);
