@@ -7,14 +7,16 @@
 // "Building a Rust Inference Engine That Matches Llama.cpp", section "Where
 // the wins came from").
 //
-// Q4_K arithmetic.  Within a 32-weight sub-block j every weight is
-// d*sc_j*q - dmin*m_j, so the sub-block's share of the dot product is
-//     (d*sc_j) * sum(q*x)  -  (dmin*m_j) * sum(x).
-// The kernel accumulates the integer-weighted sums sum(q*x) and sum(x) in
-// binary32 and applies the two scales once per sub-block.  High nibbles are
-// used as 16*q (masking without a shift) and the factor 1/16 goes into d*sc.
-// For a one-hot x the result is exactly the binary32 weight: d*sc*q is exact
-// and the single fused multiply-add with -dmin*m rounds once.
+// Q4_K arithmetic (the general kernel: batch 1 with K above the streaming
+// kernel's limit, and matrices too large for the matrix-core kernel's 32-bit
+// offsets).  Each weight is dequantized once to its binary32 value,
+// w = d*sc_j*q - dmin*m_j with one rounding (d*sc_j*q is exact, so a fused
+// multiply-add gives it), and multiplied by each of the B activation rows in
+// binary32; the dequantization is shared by the batch rows.  Unlike the
+// factored form sum(q*x)*d*sc - sum(x)*dmin*m, whose rounding error follows
+// the two terms, the error here follows sum |w*x| however w's terms cancel.
+// High nibbles are used as 16*q (masking without a shift) and the factor 1/16
+// goes into d*sc (exact).
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -63,55 +65,7 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
             }
         }
         const float *xs = x + (size_t)s * 256 + 64 * g;
-        float plo[R][B], phi[R][B], sxl[B], sxh[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            sxl[b] = 0.f;
-            sxh[b] = 0.f;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                plo[r][b] = 0.f;
-                phi[r][b] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float ql[R][4], qh[R][4];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t D = i == 0 ? qa[r].x : i == 1 ? qa[r].y : i == 2 ? qa[r].z
-                                 : i == 3 ? qa[r].w : i == 4 ? qb[r].x : i == 5 ? qb[r].y
-                                 : i == 6 ? qb[r].z : qb[r].w;
-                const uint32_t lo = D & 0x0f0f0f0fu;
-                const uint32_t hi = D & 0xf0f0f0f0u;
-                ql[r][0] = ubyte_to_float<0>(lo);
-                ql[r][1] = ubyte_to_float<1>(lo);
-                ql[r][2] = ubyte_to_float<2>(lo);
-                ql[r][3] = ubyte_to_float<3>(lo);
-                qh[r][0] = ubyte_to_float<0>(hi);
-                qh[r][1] = ubyte_to_float<1>(hi);
-                qh[r][2] = ubyte_to_float<2>(hi);
-                qh[r][3] = ubyte_to_float<3>(hi);
-            }
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float4 xl = ldf4(xs + (size_t)b * K + 4 * i);
-                const float4 xh = ldf4(xs + (size_t)b * K + 32 + 4 * i);
-                sxl[b] += (xl.x + xl.y) + (xl.z + xl.w);
-                sxh[b] += (xh.x + xh.y) + (xh.z + xh.w);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    plo[r][b] = fmaf(ql[r][0], xl.x, plo[r][b]);
-                    plo[r][b] = fmaf(ql[r][1], xl.y, plo[r][b]);
-                    plo[r][b] = fmaf(ql[r][2], xl.z, plo[r][b]);
-                    plo[r][b] = fmaf(ql[r][3], xl.w, plo[r][b]);
-                    phi[r][b] = fmaf(qh[r][0], xh.x, phi[r][b]);
-                    phi[r][b] = fmaf(qh[r][1], xh.y, phi[r][b]);
-                    phi[r][b] = fmaf(qh[r][2], xh.z, phi[r][b]);
-                    phi[r][b] = fmaf(qh[r][3], xh.w, phi[r][b]);
-                }
-            }
-        }
+        float dsl[R], dsh[R], dml[R], dmh[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             uint32_t scl, ml, sch, mh;
@@ -119,18 +73,47 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
             q4k_scale_min(hd[r].y, hd[r].z, hd[r].w, 2 * g + 1, sch, mh);
             const float d = half_to_float(hd[r].x);
             const float dmin = half_to_float(hd[r].x >> 16);
-            const float dsl = d * (float)scl;
-            const float dsh = d * (float)sch * 0.0625f;
-            const float dml = dmin * (float)ml;
-            const float dmh = dmin * (float)mh;
+            dsl[r] = d * (float)scl;
+            dsh[r] = d * (float)sch * 0.0625f;
+            dml[r] = dmin * (float)ml;
+            dmh[r] = dmin * (float)mh;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float wl[R][4], wh[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t D = i == 0 ? qa[r].x : i == 1 ? qa[r].y : i == 2 ? qa[r].z
+                                 : i == 3 ? qa[r].w : i == 4 ? qb[r].x : i == 5 ? qb[r].y
+                                 : i == 6 ? qb[r].z : qb[r].w;
+                const uint32_t lo = D & 0x0f0f0f0fu;
+                const uint32_t hi = D & 0xf0f0f0f0u;
+                wl[r][0] = fmaf(dsl[r], ubyte_to_float<0>(lo), -dml[r]);
+                wl[r][1] = fmaf(dsl[r], ubyte_to_float<1>(lo), -dml[r]);
+                wl[r][2] = fmaf(dsl[r], ubyte_to_float<2>(lo), -dml[r]);
+                wl[r][3] = fmaf(dsl[r], ubyte_to_float<3>(lo), -dml[r]);
+                wh[r][0] = fmaf(dsh[r], ubyte_to_float<0>(hi), -dmh[r]);
+                wh[r][1] = fmaf(dsh[r], ubyte_to_float<1>(hi), -dmh[r]);
+                wh[r][2] = fmaf(dsh[r], ubyte_to_float<2>(hi), -dmh[r]);
+                wh[r][3] = fmaf(dsh[r], ubyte_to_float<3>(hi), -dmh[r]);
+            }
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                float a = acc[r][b];
-                a = fmaf(dsl, plo[r][b], a);
-                a = fmaf(dsh, phi[r][b], a);
-                a = fmaf(-dml, sxl[b], a);
-                a = fmaf(-dmh, sxh[b], a);
-                acc[r][b] = a;
+                const float4 xl = ldf4(xs + (size_t)b * K + 4 * i);
+                const float4 xh = ldf4(xs + (size_t)b * K + 32 + 4 * i);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float a = acc[r][b];
+                    a = fmaf(wl[r][0], xl.x, a);
+                    a = fmaf(wl[r][1], xl.y, a);
+                    a = fmaf(wl[r][2], xl.z, a);
+                    a = fmaf(wl[r][3], xl.w, a);
+                    a = fmaf(wh[r][0], xh.x, a);
+                    a = fmaf(wh[r][1], xh.y, a);
+                    a = fmaf(wh[r][2], xh.z, a);
+                    a = fmaf(wh[r][3], xh.w, a);
+                    acc[r][b] = a;
+                }
             }
         }
     }

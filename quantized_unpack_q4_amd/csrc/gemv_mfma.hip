@@ -12,12 +12,21 @@
 //     weights) per instruction: the 4-bit quant enters as the binary16
 //     subnormal q*2^-24 (exact; high nibbles as 16q*2^-24) and the activation
 //     as two binary16 halves hi + lo of x * 2^e, where 2^e (per activation row
-//     and super-block) brings the largest |x| of the slice to [2^14, 2^15); the
-//     products are exact and the sums binary32, so the activation keeps about
-//     22 significant bits;
-//   * (d*sc_j) * D_j is applied in binary32 per sub-block, 2^-e per super-block;
+//     and sub-block) brings the largest |x| of the 32 values to
+//     [2^14, 2^15); the products are exact and the sums binary32, every
+//     value at least 2^-17 of that maximum keeps 22 significant bits and
+//     every value at least 2^-20 of it a relative error below 2^-19;
+//   * (d*sc_j) * D_j and 2^-e are applied in binary32 per sub-block;
 //   * sum_j (dmin*m_j) * sum_k x_k is a 16 x 16 x 8 product per super-block on
 //     v_mfma_f32_16x16x4f32 from the binary32 sub-block sums of x.
+// A sub-block of an activation row whose non-zero |x| span more than 2^20, or
+// that holds more than 1/16 of the row's sum of |x| over the super-block, is
+// left out of the split (its staged values and sum are zero) and computed
+// exactly instead: each weight dequantized to its binary32 value times the
+// binary32 activation (staged in LDS for such sub-blocks), summed over the
+// four lanes that hold the sub-block
+// (the same rule and reasons as the batch-1 kernel: dropped small values, and
+// a dominant activation meeting a near-cancelling d*sc*q - dmin*m).
 //
 // Work split.  A block is 128 consecutive rows of one matrix (4 waves x 2
 // tiles x 16 rows) over the whole K.  The 256 threads first stage the
@@ -46,9 +55,16 @@ struct Smem {
     // activation row b sit in slot b ^ swz(j, q)
     uint4 xh[2][8][4][16];
     uint4 xl[2][8][4][16];
-    float sx[2][8][16]; // [buffer][j][b] binary32 sum of x over sub-block j
-    float inv[2][16];   // [buffer][b] 2^-e
+    float sx[2][8][16];  // [buffer][j][b] binary32 sum of x over sub-block j (0: computed exactly)
+    float inv[2][8][16]; // [buffer][j][b] 2^-e of sub-block j
+    uint64_t exact[2][4]; // [buffer][wave]: bit 16i + 2j: row 4*wave + i, sub-block j exact
+    float xf[2][8][16][32]; // [buffer][j][b][k]: binary32 x of the sub-blocks computed exactly
 };
+
+// a sub-block whose non-zero |x| span more than this is computed exactly
+constexpr float kSplitSpan = 1048576.f; // 2^20
+// ... and one holding more than this fraction of its super-block's sum of |x|
+constexpr float kDominant = 0.0625f;
 
 // Slot swizzle: the 16 staging threads of one activation row write 16
 // different (j, q) pairs at once; xor-ing the row index with a function of
@@ -202,29 +218,42 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                         float4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 16 * i, s * 1024, 0));
             }
         };
-        // binary16 hi/lo parts, sub-block sums and scale of the staged slice
+        // binary16 hi/lo parts, sub-block sums and scales of the staged slice
         auto store_x = [&](int buf) {
+            float m = 0.f, mn = INFINITY, l1 = 0.f, sum = 0.f;
+            if (stager) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a[4] = {fabsf(xr[i].x), fabsf(xr[i].y), fabsf(xr[i].z), fabsf(xr[i].w)};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        m = fmaxf(m, a[c]);
+                        mn = a[c] > 0.f ? fminf(mn, a[c]) : mn;
+                        l1 += a[c];
+                    }
+                    sum += (xr[i].x + xr[i].y) + (xr[i].z + xr[i].w);
+                }
+            }
+            // the partner lane holds the other half of sub-block sj
+            m = fmaxf(m, dpp_f(m, 0));
+            mn = fminf(mn, dpp_f(mn, 0));
+            sum += dpp_f(sum, 0);
+            // sum of |x| over the 16 lanes of this activation row (the super-block)
+            l1 += dpp_f(l1, 0);
+            l1 += dpp_f(l1, 1);
+            l1 += dpp_f(l1, 2);
+            l1 += dpp_f(l1, 3);
+            const bool exact = stager && m > 0.f && (m > kSplitSpan * mn || m > kDominant * l1);
+            const uint64_t eb = __ballot(exact && (sc_ & 1) == 0);
+            if (lane == 0)
+                sm.exact[buf][wave] = eb;
             if (!stager)
                 return;
-            float m = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                m = fmaxf(m, fmaxf(fmaxf(fabsf(xr[i].x), fabsf(xr[i].y)),
-                                   fmaxf(fabsf(xr[i].z), fabsf(xr[i].w))));
-            m = fmaxf(m, dpp_f(m, 0));
-            m = fmaxf(m, dpp_f(m, 1));
-            m = fmaxf(m, dpp_f(m, 2));
-            m = fmaxf(m, dpp_f(m, 3)); // max over the 16 lanes of this row
             // 2^e with the largest |x| in [2^14, 2^15): exponent field 268 - ex,
-            // kept in [1, 253] (zero or tiny slices get 2^126)
+            // kept in [1, 253] (zero or tiny sub-blocks get 2^126)
             const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 255u);
             const int fe = min(max(268 - ex, 1), 253);
-            const float s = __builtin_bit_cast(float, (uint32_t)fe << 23);
-            float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sum += (xr[i].x + xr[i].y) + (xr[i].z + xr[i].w);
-            sum += dpp_f(sum, 0); // the partner lane holds the other half of sub-block sj
+            const float s = exact ? 0.f : __builtin_bit_cast(float, (uint32_t)fe << 23);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 // quarter sq0 + h: elements k = 8h .. 8h+7 of this lane's 16
@@ -238,10 +267,15 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                 sm.xh[buf][sj][q][sb ^ swz(sj, q)] = hv;
                 sm.xl[buf][sj][q][sb ^ swz(sj, q)] = lv;
             }
-            if ((sc_ & 1) == 0)
-                sm.sx[buf][sj][sb] = sum;
-            if (sc_ == 0)
-                sm.inv[buf][sb] = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
+            if (exact) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<float4_t *>(&sm.xf[buf][sj][sb][16 * (sc_ & 1) + 4 * i]) = xr[i];
+            }
+            if ((sc_ & 1) == 0) {
+                sm.sx[buf][sj][sb] = exact ? 0.f : sum;
+                sm.inv[buf][sj][sb] = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
+            }
         };
 
         float4_t acc[2], macc[2];
@@ -286,6 +320,8 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                     const uint4 xl = sm.xl[buf][j][quarter][col ^ swz(j, quarter)];
                     const half8_t ah = __builtin_bit_cast(half8_t, xh);
                     const half8_t al = __builtin_bit_cast(half8_t, xl);
+                    // 2^-e of sub-block j for batch rows 4*quarter .. +3
+                    const float4_t iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][j][4 * quarter]);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const uint32_t D0 = wt[t].q[g].x, D1 = wt[t].q[g].y;
@@ -295,17 +331,69 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                         const half8_t bq = __builtin_bit_cast(half8_t, qv);
                         float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                         D = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, D, 0, 0, 0);
-                        ch[t] = sl[t][j] * D + ch[t];
+                        ch[t] = (sl[t][j] * D) * iv + ch[t];
                     }
                 }
                 // bound the live ranges: one group's operands at a time
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const float4_t iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][4 * quarter]);
+            // sub-blocks computed exactly (rare; the condition is the same for
+            // the whole workgroup)
+            uint64_t ex4[4];
+#pragma unroll
+            for (int wv = 0; wv < 4; ++wv) {
+                const uint64_t v = sm.exact[buf][wv];
+                ex4[wv] = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                          __builtin_amdgcn_readfirstlane((uint32_t)v);
+            }
+            if ((ex4[0] | ex4[1] | ex4[2] | ex4[3]) != 0) {
+#pragma unroll 1
+                for (int wv = 0; wv < 4; ++wv) {
+                    uint64_t bits = ex4[wv];
+                    while (bits) {
+                        const int bit = __builtin_ctzll(bits);
+                        bits &= bits - 1;
+                        const int b = 4 * wv + (bit >> 4), j = (bit & 15) >> 1;
+                        // this lane's 8 activations of the sub-block: k = 32j + 8*quarter + i
+                        const float4_t xa = *reinterpret_cast<const float4_t *>(&sm.xf[buf][j][b][8 * quarter]);
+                        const float4_t xb = *reinterpret_cast<const float4_t *>(&sm.xf[buf][j][b][8 * quarter + 4]);
+                        const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const uint4 h = wt[t].h;
+                            uint32_t sc, m;
+                            q4k_scale_min(h.y, h.z, h.w, j, sc, m);
+                            const float dsc = half_to_float(h.x) * (float)sc;
+                            const float dmm = half_to_float(h.x >> 16) * (float)m;
+                            const uint32_t D0 = (j >> 1) == 0 ? wt[t].q[0].x : (j >> 1) == 1 ? wt[t].q[1].x
+                                              : (j >> 1) == 2 ? wt[t].q[2].x : wt[t].q[3].x;
+                            const uint32_t D1 = (j >> 1) == 0 ? wt[t].q[0].y : (j >> 1) == 1 ? wt[t].q[1].y
+                                              : (j >> 1) == 2 ? wt[t].q[2].y : wt[t].q[3].y;
+                            const int sh = 4 * (j & 1);
+                            float part = 0.f;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                const uint32_t q = ((i < 4 ? D0 : D1) >> (8 * (i & 3) + sh)) & 15u;
+                                part = fmaf(fmaf(dsc, (float)q, -dmm), xv[i], part);
+                            }
+                            // the four quarters of weight row col
+                            part += __shfl_xor(part, 16, 64);
+                            part += __shfl_xor(part, 32, 64);
+                            if (quarter == (b >> 2)) {
+                                const int i = b & 3;
+                                ch[t][0] += i == 0 ? part : 0.f;
+                                ch[t][1] += i == 1 ? part : 0.f;
+                                ch[t][2] += i == 2 ? part : 0.f;
+                                ch[t][3] += i == 3 ? part : 0.f;
+                            }
+                        }
+                    }
+                }
+            }
             const float sx0 = sm.sx[buf][quarter][col], sx1 = sm.sx[buf][4 + quarter][col];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                acc[t] = iv * ch[t] + acc[t];
+                acc[t] = ch[t] + acc[t];
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx0, mb[t][0], macc[t], 0, 0, 0);
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx1, mb[t][1], macc[t], 0, 0, 0);
             }
@@ -357,14 +445,7 @@ long long gemv_mfma_blocks(int64_t M) { return (M + RB - 1) / RB; }
 hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
                             long long total_bytes, long long blocks, int B, hipStream_t s)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-            return hipErrorInvalidDevice;
-        cus = prop.multiProcessorCount;
-    }
+    const int cus = device_cus();
     const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
     hipLaunchKernelGGL(gemv_q4k_mfma_kernel, dim3((unsigned)grid), dim3(NT), 0, s, table_dev,
                        inline0, n, total_bytes, B);

@@ -12,8 +12,13 @@
 // pair: the quant is an exact binary16 integer, the activation enters as two
 // binary16 halves hi + lo of x * 2^e, where 2^e (per activation row and
 // block) brings the block's largest |x| to [2^14, 2^15).  The products are
-// exact and the sums binary32, so the activation keeps about 22 significant
-// bits; d and 2^-e are applied in binary32 per block.
+// exact and the sums binary32, so every value at least 2^-17 of its block's
+// largest |x| keeps 22 significant bits and every value at least 2^-20 of it
+// a relative error below 2^-19; d and 2^-e are applied in binary32 per block.
+// A block of an activation row whose non-zero |x| span more than 2^20 (the
+// split would lose its small values) is left out of the split and
+// computed exactly instead: d*q (exact) times the binary32 activation, summed
+// in binary32 over the four lanes that hold the block.
 //
 // Work split.  A workgroup of 16 waves owns T 16-row tiles of weight rows (T
 // = 2 when that still gives at least 384 workgroups, else 1; the tiles share
@@ -74,13 +79,23 @@ __device__ __forceinline__ void split8(float4 u, float4 v, int e, half8_t &hi, h
 
 // Exponent e with max|x| * 2^e in [2^14, 2^15) over the 32 values of one
 // block of this lane's activation row (its 8 and those of the 3 other lanes
-// of the row: lanes b, b+16, b+32, b+48); 0 for an all-zero block.
-__device__ __forceinline__ int block_exp(float4 u, float4 v)
+// of the row: lanes b, b+16, b+32, b+48); 0 for an all-zero block.  exact: the
+// block's non-zero |x| span more than 2^20.
+__device__ __forceinline__ int block_exp(float4 u, float4 v, bool &exact)
 {
-    float m = fmaxf(fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))),
-                    fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const float a[8] = {fabsf(u.x), fabsf(u.y), fabsf(u.z), fabsf(u.w),
+                        fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w)};
+    float m = 0.f, mn = INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        m = fmaxf(m, a[i]);
+        mn = a[i] > 0.f ? fminf(mn, a[i]) : mn;
+    }
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
+    mn = fminf(mn, __shfl_xor(mn, 16, 64));
+    mn = fminf(mn, __shfl_xor(mn, 32, 64));
+    exact = m > 1048576.f * mn; // 2^20
     if (m == 0.f)
         return 0;
     int E;
@@ -143,26 +158,60 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_q8_0_mfma_kernel(
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const float4 u = blk ? p.x2 : p.x0, v = blk ? p.x3 : p.x1;
-            const int e = block_exp(u, v);
+            bool exact;
+            const int e = block_exp(u, v, exact);
             half8_t xh, xl;
             split8(u, v, e, xh, xl);
+            if (exact) {
+                xh = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                xl = xh;
+            }
             int eb[4]; // exponents of batch rows 4q + i
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 eb[i] = __shfl(e, 4 * q + i, 64);
+            float dq[T];
+            half8_t wqv[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const half8_t wq =
-                    blk ? quants8(p.wb0[t], p.wb1[t])
-                        : quants8(__builtin_amdgcn_alignbyte(p.wa1[t], p.wa0[t], 2),
-                                  __builtin_amdgcn_alignbyte(p.wa2[t], p.wa1[t], 2));
-                const float d = half_to_float(blk ? (p.d1w[t] >> 16) : (p.d0w[t] & 0xffffu));
+                wqv[t] = blk ? quants8(p.wb0[t], p.wb1[t])
+                             : quants8(__builtin_amdgcn_alignbyte(p.wa1[t], p.wa0[t], 2),
+                                       __builtin_amdgcn_alignbyte(p.wa2[t], p.wa1[t], 2));
+                dq[t] = half_to_float(blk ? (p.d1w[t] >> 16) : (p.d0w[t] & 0xffffu));
                 float4_t c = float4_t{0.f, 0.f, 0.f, 0.f};
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wq, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wq, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wqv[t], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wqv[t], c, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[t][i] = fmaf(d, ldexpf(c[i], -eb[i]), acc[t][i]);
+                    acc[t][i] = fmaf(dq[t], ldexpf(c[i], -eb[i]), acc[t][i]);
+            }
+            // batch rows whose block is computed exactly (bit b: row b)
+            uint64_t rows_exact = __ballot(exact && q == 0 && col < B);
+            while (rows_exact) {
+                const int b = __builtin_ctzll(rows_exact);
+                rows_exact &= rows_exact - 1;
+                // row b's 8 activations of this lane's quarter, from lane b + 16q
+                const int src = b + 16 * q;
+                const float xv[8] = {__shfl(u.x, src, 64), __shfl(u.y, src, 64),
+                                     __shfl(u.z, src, 64), __shfl(u.w, src, 64),
+                                     __shfl(v.x, src, 64), __shfl(v.y, src, 64),
+                                     __shfl(v.z, src, 64), __shfl(v.w, src, 64)};
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        part = fmaf(dq[t] * (float)wqv[t][i], xv[i], part);
+                    part += __shfl_xor(part, 16, 64);
+                    part += __shfl_xor(part, 32, 64);
+                    if (q == (b >> 2)) {
+                        const int i = b & 3;
+                        acc[t][0] += i == 0 ? part : 0.f;
+                        acc[t][1] += i == 1 ? part : 0.f;
+                        acc[t][2] += i == 2 ? part : 0.f;
+                        acc[t][3] += i == 3 ? part : 0.f;
+                    }
+                }
             }
         }
     };

@@ -22,15 +22,31 @@
 // Arithmetic per lane.  Two lanes share a 256-weight super-block: lane p
 // (0 or 1) owns quant groups p and p + 2, i.e. sub-blocks 2p, 2p+1, 2p+4 and
 // 2p+5, whose scales come from the same three scale bytes per pair (j, j+4).
-// Activations are scaled by a power of two (max|x| into [2^14, 2^15)), split
-// as x = hi + lo with hi, lo binary16 (about 22 significant bits together)
-// and staged in LDS once per matrix; the scale is undone exactly.  Quants are
-// used as binary16 subnormals (the nibble bits themselves, q * 2^-24, or
-// 16q * 2^-24 for high nibbles), so one v_dot2_f32_f16 multiplies two quants
-// by two activation halves exactly and accumulates in binary32.  Per
-// sub-block j the contribution is (d*sc_j) * sum(q*x) - (dmin*m_j) * sum(x);
-// sum(x) per sub-block is staged with x.  With a one-hot x the result is the
-// binary32 weight exactly (d*sc*q exact, one rounding with -dmin*m).
+// Quants are used as binary16 subnormals (the nibble bits themselves,
+// q * 2^-24, or 16q * 2^-24 for high nibbles), so one v_dot2_f32_f16
+// multiplies two quants by two activation halves exactly and accumulates in
+// binary32.  Per sub-block j the contribution is
+// (d*sc_j) * sum(q*x) - (dmin*m_j) * sum(x).  With a one-hot x the result is
+// the binary32 weight exactly (d*sc*q exact, one rounding with -dmin*m).
+//
+// Activations.  Each 32-value sub-block j of x is staged in LDS once per
+// matrix as binary16 pairs hi + lo of x * 2^s_j, where 2^s_j brings the
+// sub-block's largest |x| into [2^14, 2^15); every value at least 2^-17 of
+// that maximum then keeps 22 significant bits (lo stays a normal binary16),
+// and every value at least 2^-20 of it a relative error below 2^-19.  The
+// sub-block's result is brought to the vector's own scale (its largest |x| in
+// [2^14, 2^15)) by an exact power of two, and the row's sum is scaled back
+// once at the end, so no intermediate overflows or underflows whatever the
+// vector's magnitude.  Two kinds of sub-block skip the split and are computed
+// exactly in binary32 instead, each weight dequantized to its binary32 value
+// (d*sc*q - dmin*m, one rounding) times the binary32 activation staged in LDS:
+// a sub-block whose non-zero |x| span more than 2^20 (the split would lose
+// the small ones), and a sub-block holding more than 1/16 of the sum of |x|
+// over its super-block (a single dominant activation would otherwise meet a
+// near-cancelling d*sc*q - dmin*m through the factored form, whose error
+// scales with the two terms rather than with their difference).  Neither
+// occurs in practice in standard-normal vectors; both keep spikes, one-hot
+// and sparse vectors and wide ranges within the bound.
 //
 // Pipelining: each wave issues the global loads of its next step before
 // computing the current one; the loads are unconditional (out-of-range rows
@@ -89,7 +105,16 @@ __device__ __forceinline__ float lane_value(float v, int lane)
 
 constexpr int kStreamMaxK = GemvStreamMaxK;
 constexpr int kRecs = kStreamMaxK / 4;                      // 16-byte x records
-constexpr int kLdsWords = (kRecs + kRecs / 16) * 4 + kStreamMaxK / 32;
+constexpr int kLdsWords = (kRecs + kRecs / 16) * 4 + 2 * (kStreamMaxK / 32);
+// binary32 activations (in the vector's scale) of up to kExactSlots sub-blocks
+// computed exactly, so that the exact path reads LDS; further ones (vectors
+// with a wide range everywhere) read global memory.  kLdsWords + the slots
+// stay within 80 KB, two workgroups per CU.
+constexpr int kExactSlots = 56;
+// a sub-block whose non-zero |x| span more than this is computed exactly
+constexpr float kSplitSpan = 1048576.f; // 2^20
+// ... and one holding more than this fraction of its super-block's sum of |x|
+constexpr float kDominant = 0.0625f;
 constexpr int kR = 3;          // row groups per wave step (a group is 2 or 4 rows)
 constexpr int kTileRowsMin = 24; // rows per workgroup tile with 32 lanes per row
 
@@ -121,8 +146,10 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
     constexpr int kThreads = 64 * W;
     constexpr int kSubPerThread = (kStreamMaxK / 32 + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+    __shared__ __attribute__((aligned(16))) float xex[kExactSlots][32];
+    __shared__ int s_nexact;
     uint32_t *xrec = lds;
-    float *ssum = reinterpret_cast<float *>(lds + (kRecs + kRecs / 16) * 4);
+    float2 *srec = reinterpret_cast<float2 *>(lds + (kRecs + kRecs / 16) * 4);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = lane & 1;
@@ -138,71 +165,112 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
     int nsb = e.K >> 8, r_end = 0, rpg = 2, sps = 16, rsub = 0, sbl = 0;
     long long rowb = (long long)nsb * kQ4kBytes;
 
-    // Power-of-two scale that brings max|x| into [2^14, 2^15): keeps the
-    // binary16 hi/lo split accurate for any finite x of moderate magnitude.
+    // Activation staging (see the header): records of hi/lo binary16 pairs,
+    // and per sub-block j the pair srec[j] = (sum of x over j, factor f_j) in
+    // the vector's scale; f_j = 2^(e_j - e) takes sub-block j's products to
+    // the vector's scale (times 2^-4 for odd j: high nibbles enter as 16q),
+    // 0 for an all-zero sub-block, -1 for one computed exactly.
     __shared__ float s_amax[W];
-    float inv_scale = 1.f;
+    int vexp = 0; // the vector's scale is 2^(15 - vexp): max|x| < 2^vexp
     auto stage = [&]() {
         // thread t owns sub-blocks t, t + kThreads, ... (32 activations each,
         // at most 512 sub-blocks): every activation is loaded once, all loads
-        // in flight together, and kept in registers for the scale, split and sums
+        // in flight together, and kept in registers for the scale, split and
+        // sums.  The 8 sub-blocks of a super-block belong to 8 consecutive
+        // lanes of one wave.
         const int nsub = e.K >> 5;
         float4 v[kSubPerThread][8];
         float amax = 0.f;
 #pragma unroll
         for (int u = 0; u < kSubPerThread; ++u) {
             const int j = tid + kThreads * u;
-            if (j < nsub) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    v[u][i] = gloadf4(e.x + 32 * j + 4 * i);
-                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][i].x), fabsf(v[u][i].y)),
-                                             fmaxf(fabsf(v[u][i].z), fabsf(v[u][i].w))));
-                }
-            }
+            for (int i = 0; i < 8; ++i)
+                v[u][i] = j < nsub ? gloadf4(e.x + 32 * j + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][i].x), fabsf(v[u][i].y)),
+                                         fmaxf(fabsf(v[u][i].z), fabsf(v[u][i].w))));
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
             amax = fmaxf(amax, __shfl_xor(amax, off, 64));
         if (lane == 0)
             s_amax[wave] = amax;
+        if (tid == 0)
+            s_nexact = 0;
         __syncthreads();
         amax = s_amax[0];
 #pragma unroll
         for (int i = 1; i < W; ++i)
             amax = fmaxf(amax, s_amax[i]);
-        int ex = 0;
+        vexp = 0;
         if (amax > 0.f)
-            (void)frexpf(amax, &ex); // amax < 2^ex
-        const float scale = ldexpf(1.f, 15 - ex);
-        inv_scale = ldexpf(1.f, ex - 15);
-        // record i holds x[4i..4i+3]*scale as (hi(x0,x2), hi(x1,x3), lo(x0,x2),
-        // lo(x1,x3)); 16 bytes of padding after every 16 records.  ssum[j] is
-        // the plain binary32 sum of x over sub-block j.
+            (void)frexpf(amax, &vexp); // amax < 2^vexp
+        // record i holds x[4i..4i+3]*2^s_j as (hi(x0,x2), hi(x1,x3), lo(x0,x2),
+        // lo(x1,x3)); 16 bytes of padding after every 16 records
 #pragma unroll
         for (int u = 0; u < kSubPerThread; ++u) {
             const int j = tid + kThreads * u;
-            if (j < nsub) {
-                float sum = 0.f;
+            float smax = 0.f, smin = INFINITY, l1 = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float4 w = v[u][i];
-                    sum += (w.x + w.y) + (w.z + w.w);
-                    w.x *= scale;
-                    w.y *= scale;
-                    w.z *= scale;
-                    w.w *= scale;
-                    const h2_t h02 = {(_Float16)w.x, (_Float16)w.z};
-                    const h2_t h13 = {(_Float16)w.y, (_Float16)w.w};
-                    const h2_t l02 = {(_Float16)(w.x - (float)h02.x), (_Float16)(w.z - (float)h02.y)};
-                    const h2_t l13 = {(_Float16)(w.y - (float)h13.x), (_Float16)(w.w - (float)h13.y)};
-                    const int ri = 8 * j + i;
-                    *reinterpret_cast<uint4 *>(xrec + 4 * (ri + (ri >> 4))) = make_uint4(
-                        __builtin_bit_cast(uint32_t, h02), __builtin_bit_cast(uint32_t, h13),
-                        __builtin_bit_cast(uint32_t, l02), __builtin_bit_cast(uint32_t, l13));
+            for (int i = 0; i < 8; ++i) {
+                const float a[4] = {fabsf(v[u][i].x), fabsf(v[u][i].y), fabsf(v[u][i].z),
+                                    fabsf(v[u][i].w)};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    smax = fmaxf(smax, a[c]);
+                    smin = a[c] > 0.f ? fminf(smin, a[c]) : smin;
+                    l1 += a[c];
                 }
-                ssum[j] = sum;
             }
+            // sum of |x| over the super-block (8 consecutive lanes)
+            float sl1 = l1 + __shfl_xor(l1, 1, 64);
+            sl1 += __shfl_xor(sl1, 2, 64);
+            sl1 += __shfl_xor(sl1, 4, 64);
+            if (j >= nsub)
+                continue;
+            const bool exact = smax > 0.f && (smax > kSplitSpan * smin || smax > kDominant * sl1);
+            int ej = 0;
+            if (smax > 0.f)
+                (void)frexpf(smax, &ej);
+            const int sh = 15 - ej;
+            const bool split = smax > 0.f && !exact;
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float4 w = v[u][i];
+                w.x = split ? ldexpf(w.x, sh) : 0.f;
+                w.y = split ? ldexpf(w.y, sh) : 0.f;
+                w.z = split ? ldexpf(w.z, sh) : 0.f;
+                w.w = split ? ldexpf(w.w, sh) : 0.f;
+                sum += (w.x + w.y) + (w.z + w.w);
+                const h2_t h02 = {(_Float16)w.x, (_Float16)w.z};
+                const h2_t h13 = {(_Float16)w.y, (_Float16)w.w};
+                const h2_t l02 = {(_Float16)(w.x - (float)h02.x), (_Float16)(w.z - (float)h02.y)};
+                const h2_t l13 = {(_Float16)(w.y - (float)h13.x), (_Float16)(w.w - (float)h13.y)};
+                const int ri = 8 * j + i;
+                *reinterpret_cast<uint4 *>(xrec + 4 * (ri + (ri >> 4))) = make_uint4(
+                    __builtin_bit_cast(uint32_t, h02), __builtin_bit_cast(uint32_t, h13),
+                    __builtin_bit_cast(uint32_t, l02), __builtin_bit_cast(uint32_t, l13));
+            }
+            // exact: slot for its binary32 values, factor -(1 + slot)
+            int slot = kExactSlots;
+            if (exact) {
+                slot = min(atomicAdd(&s_nexact, 1), kExactSlots);
+                if (slot < kExactSlots) {
+                    const int xs = 15 - vexp;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        *reinterpret_cast<float4 *>(&xex[slot][4 * i]) =
+                            make_float4(ldexpf(v[u][i].x, xs), ldexpf(v[u][i].y, xs),
+                                        ldexpf(v[u][i].z, xs), ldexpf(v[u][i].w, xs));
+                }
+            }
+            // 2^(e_j - vexp) <= 1, and 2^-4 more for the high-nibble sub-blocks
+            const float f = ldexpf(1.f, ej - vexp - 4 * (j & 1));
+            srec[j] = split ? make_float2(sum * ldexpf(1.f, ej - vexp), f)
+                            : make_float2(0.f, exact ? -1.f - (float)slot : 0.f);
         }
     };
 
@@ -327,9 +395,14 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
                     P5[r] = dot2(eh13, xd.w, P5[r]);
                 }
             }
-            const float2 s01 = *reinterpret_cast<const float2 *>(ssum + 8 * s + 2 * p);
-            const float2 s45 = *reinterpret_cast<const float2 *>(ssum + 8 * s + 2 * p + 4);
+            // (sum, factor) of sub-blocks 2p, 2p+1 and 2p+4, 2p+5
+            const float4 g01 = *reinterpret_cast<const float4 *>(srec + 8 * s + 2 * p);
+            const float4 g45 = *reinterpret_cast<const float4 *>(srec + 8 * s + 2 * p + 4);
             const int o0 = 16 * p, o1 = 16 * p + 8; // bit offsets of scale bytes 2p, 2p+1
+            // sub-blocks computed exactly (factor -1); rare, so a divergent branch
+            const bool any_exact = fminf(fminf(g01.y, g01.w), fminf(g45.y, g45.w)) < 0.f;
+            const int xsh = 15 - vexp;
+            const float *xs = e.x + 256 * s;
 #pragma unroll
             for (int r = 0; r < kR; ++r) {
                 const uint32_t h0 = cur[r].ok ? cur[r].hd.x : 0u;
@@ -349,24 +422,75 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
                 const uint32_t m5 = __builtin_amdgcn_ubfe(h3, o1 + 4, 4) |
                                     (__builtin_amdgcn_ubfe(h2, o1 + 6, 2) << 4);
                 // quants entered as q*2^-24 (low) and q*2^-20 (high): fold 2^24 into d
-                const float d24 = half_to_float(h0) * 16777216.f;
+                const float d = half_to_float(h0);
+                const float d24 = d * 16777216.f;
                 const float dmin = half_to_float(h0 >> 16);
-                float t1 = (float)sc0 * P0[r];
-                t1 = fmaf((float)sc1 * 0.0625f, P1[r], t1);
-                t1 = fmaf((float)sc4, P4[r], t1);
-                t1 = fmaf((float)sc5 * 0.0625f, P5[r], t1);
-                float t2 = (float)m0 * s01.x;
-                t2 = fmaf((float)m1, s01.y, t2);
-                t2 = fmaf((float)m4, s45.x, t2);
-                t2 = fmaf((float)m5, s45.y, t2);
-                acc[r] = fmaf(-dmin, t2, fmaf(d24, t1 * inv_scale, acc[r]));
+                float t1 = ((float)sc0 * g01.y) * P0[r];
+                t1 = fmaf((float)sc1 * g01.w, P1[r], t1);
+                t1 = fmaf((float)sc4 * g45.y, P4[r], t1);
+                t1 = fmaf((float)sc5 * g45.w, P5[r], t1);
+                float t2 = (float)m0 * g01.x;
+                t2 = fmaf((float)m1, g01.z, t2);
+                t2 = fmaf((float)m4, g45.x, t2);
+                t2 = fmaf((float)m5, g45.z, t2);
+                acc[r] = fmaf(-dmin, t2, fmaf(d24, t1, acc[r]));
+            }
+            if (any_exact) {
+                // the sub-blocks marked exact (their split records are zero):
+                // each weight as its binary32 value times x in the vector's
+                // scale, x loaded once for the kR row groups
+#pragma unroll 1
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float fj = jj == 0 ? g01.y : jj == 1 ? g01.w : jj == 2 ? g45.y : g45.w;
+                    if (!(fj < 0.f))
+                        continue;
+                    const int j = 2 * p + (jj & 1) + 4 * (jj >> 1), shift = 4 * (jj & 1);
+                    float dsc[kR], dmm[kR], s0[kR], s1[kR];
+#pragma unroll
+                    for (int r = 0; r < kR; ++r) {
+                        const uint32_t h0 = cur[r].ok ? cur[r].hd.x : 0u;
+                        uint32_t sc, m;
+                        q4k_scale_min(cur[r].hd.y, cur[r].hd.z, cur[r].hd.w, j, sc, m);
+                        dsc[r] = half_to_float(h0) * (float)sc;
+                        dmm[r] = half_to_float(h0 >> 16) * (float)m;
+                        s0[r] = 0.f;
+                        s1[r] = 0.f;
+                    }
+                    // slot of the binary32 values, or kExactSlots: global memory
+                    const int slot = (int)(-fj) - 1;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        float4 xv;
+                        if (slot < kExactSlots) {
+                            xv = *reinterpret_cast<const float4 *>(&xex[slot][4 * i]);
+                        } else {
+                            xv = gloadf4(xs + 32 * j + 4 * i);
+                            xv = make_float4(ldexpf(xv.x, xsh), ldexpf(xv.y, xsh),
+                                             ldexpf(xv.z, xsh), ldexpf(xv.w, xsh));
+                        }
+                        const float x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
+#pragma unroll
+                        for (int r = 0; r < kR; ++r) {
+                            const uint32_t D = (jj < 2 ? word8(cur[r].a0, cur[r].a1, i)
+                                                       : word8(cur[r].b0, cur[r].b1, i)) >> shift;
+                            s0[r] = fmaf(fmaf(dsc[r], (float)(D & 15u), -dmm[r]), x0, s0[r]);
+                            s1[r] = fmaf(fmaf(dsc[r], (float)((D >> 8) & 15u), -dmm[r]), x1, s1[r]);
+                            s0[r] = fmaf(fmaf(dsc[r], (float)((D >> 16) & 15u), -dmm[r]), x2, s0[r]);
+                            s1[r] = fmaf(fmaf(dsc[r], (float)((D >> 24) & 15u), -dmm[r]), x3, s1[r]);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < kR; ++r)
+                        acc[r] += s0[r] + s1[r];
+                }
             }
             if (c == nchunk - 1) {
                 const int row0 = r_lo + t * tile_rows + wave * wave_rows;
+                const int xsh_out = 15 - vexp;
 #pragma unroll
                 for (int r = 0; r < kR; ++r) {
                     // every lane of a 16-lane row ends with that row's sum
-                    const float v = rowsum16(acc[r]);
+                    const float v = ldexpf(rowsum16(acc[r]), -xsh_out);
                     const float q0 = lane_value(v, 0), q1 = lane_value(v, 16);
                     const float q2 = lane_value(v, 32), q3 = lane_value(v, 48);
                     if (PAIR) {
@@ -412,8 +536,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
     }
 }
 
-static int device_cus()
+int device_cus()
 {
+    // one entry per device, written once with the same value by any thread
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)

@@ -19,6 +19,9 @@ hipError_t launch_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, 
 hipError_t launch_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int B,
                            hipStream_t s);
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+
 // Persistent batch-1 Q4_K matrix-vector products over a table of matrices.
 constexpr int GemvStreamMaxK = 16384;
 // Work of one row of a matrix-vector product in bytes' worth: its weight
