@@ -12,21 +12,22 @@
 //     weights) per instruction: the 4-bit quant enters as the binary16
 //     subnormal q*2^-24 (exact; high nibbles as 16q*2^-24) and the activation
 //     as two binary16 halves hi + lo of x * 2^e, where 2^e (per activation row
-//     and sub-block) brings the largest |x| of the 32 values to
-//     [2^14, 2^15); the products are exact and the sums binary32, every
-//     value at least 2^-17 of that maximum keeps 22 significant bits and
-//     every value at least 2^-20 of it a relative error below 2^-19;
-//   * (d*sc_j) * D_j and 2^-e are applied in binary32 per sub-block;
+//     and super-block) brings the largest |x| of the slice to [2^14, 2^15);
+//     the products are exact and the sums binary32, every value at least
+//     2^-17 of that maximum keeps 22 significant bits and every value at
+//     least 2^-20 of it a relative error below 2^-19;
+//   * (d*sc_j) * D_j is applied in binary32 per sub-block, 2^-e per super-block;
 //   * sum_j (dmin*m_j) * sum_k x_k is a 16 x 16 x 8 product per super-block on
 //     v_mfma_f32_16x16x4f32 from the binary32 sub-block sums of x.
-// A sub-block of an activation row whose non-zero |x| span more than 2^20, or
-// that holds more than 1/16 of the row's sum of |x| over the super-block, is
-// left out of the split (its staged values and sum are zero) and computed
-// exactly instead: each weight dequantized to its binary32 value times the
-// binary32 activation (staged in LDS for such sub-blocks), summed over the
-// four lanes that hold the sub-block
-// (the same rule and reasons as the batch-1 kernel: dropped small values, and
-// a dominant activation meeting a near-cancelling d*sc*q - dmin*m).
+// A sub-block of an activation row holding a non-zero |x| below 2^-20 of the
+// super-block's largest, or more than 1/16 of the row's sum of |x| over the
+// super-block, is left out of the split (its staged values and sum are zero)
+// and computed exactly instead: each weight dequantized to its binary32 value
+// times the binary32 activation (staged in LDS for such sub-blocks), summed
+// over the four lanes that hold the sub-block.  The reasons are those of the
+// batch-1 kernel: the split would lose the small values, and a dominant
+// activation would meet a near-cancelling d*sc*q - dmin*m through the
+// factored form, whose error follows the two terms, not their difference.
 //
 // Work split.  A block is 128 consecutive rows of one matrix (4 waves x 2
 // tiles x 16 rows) over the whole K.  The 256 threads first stage the
@@ -55,13 +56,14 @@ struct Smem {
     // activation row b sit in slot b ^ swz(j, q)
     uint4 xh[2][8][4][16];
     uint4 xl[2][8][4][16];
-    float sx[2][8][16];  // [buffer][j][b] binary32 sum of x over sub-block j (0: computed exactly)
-    float inv[2][8][16]; // [buffer][j][b] 2^-e of sub-block j
+    float sx[2][8][16]; // [buffer][j][b] binary32 sum of x over sub-block j (0: computed exactly)
+    float inv[2][16];   // [buffer][b] 2^-e
     uint64_t exact[2][4]; // [buffer][wave]: bit 16i + 2j: row 4*wave + i, sub-block j exact
     float xf[2][8][16][32]; // [buffer][j][b][k]: binary32 x of the sub-blocks computed exactly
 };
 
-// a sub-block whose non-zero |x| span more than this is computed exactly
+// a sub-block holding a non-zero |x| below 1/kSplitSpan of its super-block's
+// largest is computed exactly
 constexpr float kSplitSpan = 1048576.f; // 2^20
 // ... and one holding more than this fraction of its super-block's sum of |x|
 constexpr float kDominant = 0.0625f;
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                         float4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 16 * i, s * 1024, 0));
             }
         };
-        // binary16 hi/lo parts, sub-block sums and scales of the staged slice
+        // binary16 hi/lo parts, sub-block sums and scale of the staged slice
         auto store_x = [&](int buf) {
             float m = 0.f, mn = INFINITY, l1 = 0.f, sum = 0.f;
             if (stager) {
@@ -235,22 +237,26 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                 }
             }
             // the partner lane holds the other half of sub-block sj
-            m = fmaxf(m, dpp_f(m, 0));
+            float mj = fmaxf(m, dpp_f(m, 0));
             mn = fminf(mn, dpp_f(mn, 0));
             sum += dpp_f(sum, 0);
-            // sum of |x| over the 16 lanes of this activation row (the super-block)
+            // max and sum of |x| over the 16 lanes of this activation row
+            m = mj;
+            m = fmaxf(m, dpp_f(m, 1));
+            m = fmaxf(m, dpp_f(m, 2));
+            m = fmaxf(m, dpp_f(m, 3));
             l1 += dpp_f(l1, 0);
             l1 += dpp_f(l1, 1);
             l1 += dpp_f(l1, 2);
             l1 += dpp_f(l1, 3);
-            const bool exact = stager && m > 0.f && (m > kSplitSpan * mn || m > kDominant * l1);
+            const bool exact = stager && mj > 0.f && (kSplitSpan * mn < m || mj > kDominant * l1);
             const uint64_t eb = __ballot(exact && (sc_ & 1) == 0);
             if (lane == 0)
                 sm.exact[buf][wave] = eb;
             if (!stager)
                 return;
             // 2^e with the largest |x| in [2^14, 2^15): exponent field 268 - ex,
-            // kept in [1, 253] (zero or tiny sub-blocks get 2^126)
+            // kept in [1, 253] (zero or tiny slices get 2^126)
             const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 255u);
             const int fe = min(max(268 - ex, 1), 253);
             const float s = exact ? 0.f : __builtin_bit_cast(float, (uint32_t)fe << 23);
@@ -272,10 +278,10 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<float4_t *>(&sm.xf[buf][sj][sb][16 * (sc_ & 1) + 4 * i]) = xr[i];
             }
-            if ((sc_ & 1) == 0) {
+            if ((sc_ & 1) == 0)
                 sm.sx[buf][sj][sb] = exact ? 0.f : sum;
-                sm.inv[buf][sj][sb] = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
-            }
+            if (sc_ == 0)
+                sm.inv[buf][sb] = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
         };
 
         float4_t acc[2], macc[2];
@@ -320,8 +326,6 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                     const uint4 xl = sm.xl[buf][j][quarter][col ^ swz(j, quarter)];
                     const half8_t ah = __builtin_bit_cast(half8_t, xh);
                     const half8_t al = __builtin_bit_cast(half8_t, xl);
-                    // 2^-e of sub-block j for batch rows 4*quarter .. +3
-                    const float4_t iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][j][4 * quarter]);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const uint32_t D0 = wt[t].q[g].x, D1 = wt[t].q[g].y;
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                         const half8_t bq = __builtin_bit_cast(half8_t, qv);
                         float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                         D = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, D, 0, 0, 0);
-                        ch[t] = (sl[t][j] * D) * iv + ch[t];
+                        ch[t] = sl[t][j] * D + ch[t];
                     }
                 }
                 // bound the live ranges: one group's operands at a time
@@ -381,19 +385,20 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                             part += __shfl_xor(part, 32, 64);
                             if (quarter == (b >> 2)) {
                                 const int i = b & 3;
-                                ch[t][0] += i == 0 ? part : 0.f;
-                                ch[t][1] += i == 1 ? part : 0.f;
-                                ch[t][2] += i == 2 ? part : 0.f;
-                                ch[t][3] += i == 3 ? part : 0.f;
+                                acc[t][0] += i == 0 ? part : 0.f;
+                                acc[t][1] += i == 1 ? part : 0.f;
+                                acc[t][2] += i == 2 ? part : 0.f;
+                                acc[t][3] += i == 3 ? part : 0.f;
                             }
                         }
                     }
                 }
             }
+            const float4_t iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][4 * quarter]);
             const float sx0 = sm.sx[buf][quarter][col], sx1 = sm.sx[buf][4 + quarter][col];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                acc[t] = ch[t] + acc[t];
+                acc[t] = iv * ch[t] + acc[t];
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx0, mb[t][0], macc[t], 0, 0, 0);
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx1, mb[t][1], macc[t], 0, 0, 0);
             }
