@@ -199,6 +199,30 @@ def gemm(fmt: int, w, x16, M: int, K: int, rows=None, toks=None):
     return y, S
 
 
+def gemm_matmul(fmt: int, w, x16, M: int, K: int, rows=None, toks=None):
+    """The same result as ``gemm``, for large samples: each weight is decoded
+    by the C decoder (``dequant``, binary32), every product and sum is taken in
+    binary64 by numpy's matrix product (a library primitive in place of the
+    plain loop; only the summation order differs, by ~1e-15 * S), and
+    S = |X| |W|^T likewise.  Returns (Y [ntoks][nrows], S)."""
+    w = _u8(w)
+    _check(fmt, w, M, K)
+    x16 = _bits16(x16).reshape(-1, K)
+    rows = None if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    toks = None if toks is None else np.asarray(toks, dtype=np.int64).reshape(-1)
+    rb = row_bytes(fmt, K)
+    if rows is None:
+        wsel, nr = w[:M * rb], M
+    else:
+        wsel = w[:M * rb].reshape(M, rb)[rows].reshape(-1)
+        nr = rows.size
+    w32, _ = dequant(fmt, wsel, nr, K)
+    xs = x16 if toks is None else x16[toks]
+    xd = xs.view(np.float16).astype(np.float64)
+    wd = w32.astype(np.float64)
+    return xd @ wd.T, np.abs(xd) @ np.abs(wd).T
+
+
 def swiglu(g, u):
     """h = silu(g) * u elementwise in binary64 (silu(z) = z / (1 + e^-z))."""
     g = np.ascontiguousarray(np.asarray(g, dtype=np.float64))

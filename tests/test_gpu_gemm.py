@@ -39,24 +39,51 @@ def test_gemm_parity_small(M, K, N):
     say("  max err/S", r)
 
 
+def _with_fixed(g, fixed, size, n):
+    """The fixed indices plus random others, n in all (sorted, distinct)."""
+    fixed = np.unique(np.asarray(fixed, dtype=np.int64))
+    others = np.setdiff1d(np.arange(size), fixed)
+    extra = g.choice(others, max(0, n - fixed.size), replace=False)
+    return np.sort(np.concatenate([fixed, extra]))
+
+
+def sample_rows(g, M, n=512):
+    """n rows: the first and last rows and both sides of the first 256-row
+    tile boundaries, the rest at random."""
+    edges = [r for t in range(256, M, 256)[:16] for r in (t - 1, t)]
+    return _with_fixed(g, [0, M - 1] + edges, M, n)
+
+
+def sample_tokens(g, N, n=16):
+    """n tokens: the first and last and both sides of the first three
+    256-token tile boundaries, the rest at random."""
+    edges = [t for b in range(256, N, 256)[:3] for t in (b - 1, b)]
+    return _with_fixed(g, [0, N - 1] + edges, N, n)
+
+
+def check_prefill_sample(y, w, x16, M, K, N, g, fmt=oracle.Q4_K):
+    """512 rows over all tokens and all rows over 16 tokens against the
+    oracle (its matrix-product form)."""
+    rows = sample_rows(g, M)
+    yr, S = oracle.gemm_matmul(fmt, w, x16, M, K, rows=rows)
+    r1 = within(y[:, rows], yr, S, TOL, "%d rows x all %d tokens" % (rows.size, N))
+    toks = sample_tokens(g, N)
+    yr2, S2 = oracle.gemm_matmul(fmt, w, x16, M, K, toks=toks)
+    r2 = within(y[toks], yr2, S2, TOL, "all rows x %d tokens" % toks.size)
+    return r1, r2
+
+
 @pytest.mark.parametrize("M,K,N", [(14336, 4096, 512), (4096, 14336, 512),
                                    (14336, 4096, 4096), (4096, 14336, 4096)])
 def test_gemm_parity_prefill_sampled(M, K, N):
-    """Prefill shapes at full size: sampled rows over all tokens, and all rows
-    over sampled tokens."""
+    """Prefill shapes at full size: 512 rows over all tokens, and all rows
+    over 16 tokens (tile edges included)."""
     say("gemm full", M, K, N)
     g = np.random.default_rng(91)
     w = synth.q4k_blocks(3, M, M, K)
     x16 = synth.activations_f16(3, N, N, K)
     y = _gemm(dev(w), x16, M, K)
-    rows = np.sort(g.choice(M, 24, replace=False))
-    rows[0], rows[-1] = 0, M - 1
-    toks = np.sort(g.choice(N, min(N, 256), replace=False))
-    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K, rows=rows, toks=toks)
-    r1 = within(y[np.ix_(toks, rows)], yr, S, TOL, "rows sample")
-    t2 = np.array([0, N - 1])
-    yr2, S2 = oracle.gemm(oracle.Q4_K, w, x16, M, K, toks=t2)
-    r2 = within(y[t2], yr2, S2, TOL, "token sample")
+    r1, r2 = check_prefill_sample(y, w, x16, M, K, N, g)
     say("  max err/S", r1, r2)
 
 
@@ -192,20 +219,14 @@ def test_gemm_splitk_parity(M, K, N, splits):
 @pytest.mark.parametrize("M,K", [(4096, 14336), (14336, 4096)])
 def test_gemm_splitk_prefill_sampled(M, K):
     """The 512-token prefill shapes at full size with the automatic split
-    count: sampled rows over all tokens, all rows over sampled tokens."""
+    count: 512 rows over all tokens, all rows over 16 tokens."""
     N = 512
     say("gemm splitk full", M, K, N)
     g = np.random.default_rng(97)
     w = synth.q4k_blocks(3, M, M, K)
     x16 = synth.activations_f16(3, N, N, K)
     y = _gemm_splitk(dev(w), x16, M, K, 0)
-    rows = np.sort(g.choice(M, 24, replace=False))
-    rows[0], rows[-1] = 0, M - 1
-    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K, rows=rows)
-    r1 = within(y[:, rows], yr, S, TOL, "rows sample")
-    t2 = np.array([0, 255, 256, N - 1])
-    yr2, S2 = oracle.gemm(oracle.Q4_K, w, x16, M, K, toks=t2)
-    r2 = within(y[t2], yr2, S2, TOL, "token sample")
+    r1, r2 = check_prefill_sample(y, w, x16, M, K, N, g)
     say("  max err/S", r1, r2)
 
 
@@ -274,19 +295,13 @@ def test_gemm_q8_0_one_hot_exact_and_special_blocks():
 
 
 def test_gemm_q8_0_prefill_sampled():
-    """Q8_0 at a prefill shape, 14336 x 4096 weights and 512 tokens: sampled
-    rows over all tokens and all rows over two tokens."""
+    """Q8_0 at a prefill shape, 14336 x 4096 weights and 512 tokens: 512 rows
+    over all tokens and all rows over 16 tokens."""
     M, K, N = 14336, 4096, 512
     say("gemm q8_0 full", M, K, N)
     g = np.random.default_rng(99)
     w = synth.q8_0_blocks(3, M, M, K)
     x16 = synth.activations_f16(3, N, N, K)
     y = _gemm_q8(dev(w), x16, M, K).view(np.float16).astype(np.float64)
-    rows = np.sort(g.choice(M, 24, replace=False))
-    rows[0], rows[-1] = 0, M - 1
-    yr, S = oracle.gemm(oracle.Q8_0, w, x16, M, K, rows=rows)
-    r1 = within(y[:, rows], yr, S, TOL, "rows sample")
-    t2 = np.array([0, N - 1])
-    yr2, S2 = oracle.gemm(oracle.Q8_0, w, x16, M, K, toks=t2)
-    r2 = within(y[t2], yr2, S2, TOL, "token sample")
+    r1, r2 = check_prefill_sample(y, w, x16, M, K, N, g, fmt=oracle.Q8_0)
     say("  max err/S", r1, r2)

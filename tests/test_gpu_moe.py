@@ -154,17 +154,73 @@ def test_moe_empty_expert_and_dropped_ids():
     assert ratio <= 2 * TOL
 
 
+def _staged_by_expert(wg, wu, wd, x16, ids, wts, H, I, E, o, sorted_, pos_of, h, d, toks,
+                      fmt=oracle.Q4_K):
+    """Stages (ii)-(iv) of _staged for many tokens, the oracle's products taken
+    per expert over all of that expert's sampled assignments (its
+    matrix-product form)."""
+    T, k = ids.shape
+    gu = I * oracle.row_bytes(fmt, H)
+    dn = H * oracle.row_bytes(fmt, I)
+    toks = np.asarray(sorted(set(int(t) for t in toks)))
+    assign = np.array([t * k + s for t in toks for s in range(k)])
+    dref = np.zeros((T * k, H))
+    Sd = np.zeros((T * k, H))
+    worst = {"h": 0.0, "d": 0.0, "out": 0.0}
+    experts = ids.reshape(-1)
+    for e in np.unique(experts[assign]):
+        a_e = assign[experts[assign] == e]
+        t_e = a_e // k
+        p_e = pos_of[a_e]
+        assert np.array_equal(sorted_[p_e], a_e)
+        g, Sg = oracle.gemm_matmul(fmt, wg[e * gu:(e + 1) * gu], x16, I, H, toks=t_e)
+        u, Su = oracle.gemm_matmul(fmt, wu[e * gu:(e + 1) * gu], x16, I, H, toks=t_e)
+        href = _silu(g) * u
+        bound = TOL * (np.abs(_dsilu(g) * u) * Sg + np.abs(_silu(g)) * Su) \
+            + np.abs(href) * 2.0 ** -10 + 2.0 ** -24
+        err = np.abs(h[p_e].astype(np.float64) - href)
+        assert np.all(err <= bound), ("h", int(e), float((err - bound).max()))
+        worst["h"] = max(worst["h"], float((err / bound).max()))
+        dr, S = oracle.gemm_matmul(fmt, wd[e * dn:(e + 1) * dn], h[p_e].view(np.uint16), H, I)
+        worst["d"] = max(worst["d"], within(d[p_e], dr, S, TOL, "d e=%d" % e))
+        dref[a_e], Sd[a_e] = dr, S
+    for t in toks:
+        w_t = wts[t].astype(np.float64)
+        acc = (w_t[:, None] * dref[t * k:(t + 1) * k]).sum(0)
+        accS = (w_t[:, None] * Sd[t * k:(t + 1) * k]).sum(0)
+        worst["out"] = max(worst["out"], within(o[t], acc, accS, TOL, "out t=%d" % t))
+    return worst
+
+
+def tokens_in_last_tiles(ids, E, n, g):
+    """At least n tokens: for every expert, the token of its last assignment in
+    the stable expert order (it sits in that expert's last, usually partial,
+    token tile), then random tokens."""
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    last = {}
+    for a in range(T * k):
+        last[int(flat[a])] = a // k
+    picked = set(last.values()) | {0, T - 1}
+    rest = [t for t in g.permutation(T) if t not in picked]
+    picked |= set(int(t) for t in rest[:max(0, n - len(picked))])
+    return sorted(picked)
+
+
 @pytest.mark.parametrize("T", [256, 2048])
 def test_moe_olmoe_shape_sampled(T):
     """OLMoE-1B-7B-shaped layer (64 experts, top-8, hidden 2048, expert 1024) at
-    full size; grouping checked whole, values on sampled tokens."""
+    full size; grouping checked whole, values on at least 64 tokens including
+    every expert's last token (its ragged remainder tile)."""
     H, I, E, k = 2048, 1024, 64, 8
     say("moe olmoe T", T)
     wg, wu, wd, x16, ids, wts = _setup(4, T, H, I, E, k)
     o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E)
     _check_grouping(ids, E, table, sorted_, pos_of)
-    toks = [0, T // 2, T - 1]
-    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d, toks)
+    toks = tokens_in_last_tiles(ids, E, 96, np.random.default_rng(7))
+    assert len(toks) >= 64
+    say("  checking", len(toks), "tokens")
+    worst = _staged_by_expert(wg, wu, wd, x16, ids, wts, H, I, E, o, sorted_, pos_of, h, d, toks)
     say("  staged worst ratios", worst)
 
 

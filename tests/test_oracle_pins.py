@@ -658,3 +658,21 @@ def test_gemv_q4k_q8k_deviation_from_binary32_path(orc):
     y8i, S8 = orc.gemv_q4k_q8k(w, qi, di, M, K)
     yi, Si = orc.gemv(orc.Q4_K, w, xi, M, K)
     assert np.all(np.abs(y8i - yi) <= 2.0 ** -23 * Si + 1e-12 * S8)
+
+
+def test_gemm_matmul_equals_gemm(orc):
+    """The matrix-product form of the oracle's GEMM (used for large parity
+    samples) agrees with the plain loop: same decoded weights, binary64 sums,
+    only the summation order differs; rows and tokens subsets index alike."""
+    from quantized_unpack_q4_amd import synth
+    for fmt, M, K, N in ((orc.Q4_K, 37, 512, 11), (orc.Q8_0, 29, 320, 7)):
+        blocks = synth.q4k_blocks if fmt == orc.Q4_K else synth.q8_0_blocks
+        w = blocks(61, 0, M, K)
+        x16 = synth.activations_f16(61, 1, N, K)
+        y, S = orc.gemm(fmt, w, x16, M, K)
+        y2, S2 = orc.gemm_matmul(fmt, w, x16, M, K)
+        assert np.all(np.abs(y - y2) <= 1e-13 * S)
+        assert np.allclose(S, S2, rtol=1e-13, atol=0)
+        rows, toks = np.array([0, 5, M - 1]), np.array([N - 1, 2])
+        y3, S3 = orc.gemm_matmul(fmt, w, x16, M, K, rows=rows, toks=toks)
+        assert np.all(np.abs(y3 - y[np.ix_(toks, rows)]) <= 1e-13 * S[np.ix_(toks, rows)])
