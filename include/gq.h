@@ -193,6 +193,25 @@ gq_status gq_gemm_q4k_splitk(const void *w, const uint16_t *x, uint16_t *y, int6
  * choice); 0 if the arguments are invalid. */
 size_t gq_gemm_q4k_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t splits);
 
+/* gq_gemm_q4k_splitk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the binary32 partials live in a static
+ * array inside the library, one per GPU, of
+ * gq_gemm_q4k_splitk_static_max_bytes() = 64 MiB, held until the process
+ * ends.  The call allocates nothing.  Same arguments, results (bit for bit)
+ * and refusals as gq_gemm_q4k_splitk; in addition GQ_EWORKSPACE when
+ * splits*N*M*4 bytes exceed the scratch (e.g. 4096 x 14336 x 512 fits with
+ * its automatic 8 splits, 4096 tokens do not), and GQ_EHIP when the scratch's
+ * device address cannot be looked up.  Every call on one GPU shares that
+ * GPU's scratch, which keeps the last call's partials: calls that overlap
+ * in time on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller. */
+gq_status gq_gemm_q4k_splitk_static(const void *w, const uint16_t *x, uint16_t *y, int64_t M,
+                                    int64_t K, int64_t N, int64_t splits, void *stream);
+
+/* Size in bytes of gq_gemm_q4k_splitk_static's scratch. */
+size_t gq_gemm_q4k_splitk_static_max_bytes(void);
+
 /* Mixture-of-experts feed-forward over Q4_K experts (the grouped form):
  *   for every token t and slot s < topk, with e = topk_ids[t][s]:
  *     g = Wg_e x_t, u = Wu_e x_t            (binary16 matrix cores, binary32 sums)

@@ -48,6 +48,8 @@
 // Workgroups of the dense product are numbered so that each XCD (blockIdx
 // mod 8) receives a contiguous run of tiles in activation-panel-major order:
 // the workgroups an XCD runs at once share one activation panel in its L2.
+#include <mutex>
+
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -557,6 +559,37 @@ hipError_t launch_gemm_splitk(const void *w, const uint16_t *x, uint16_t *y, int
     hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
                        dim3(256), 0, s, ws, y, count, splits);
     return hipGetLastError();
+}
+
+// Split-K partials for callers that cannot allocate device memory: one array
+// per device (each GPU the library runs on holds its own copy until the
+// process ends).  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in): it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) float scratch[kSplitkScratchBytes / sizeof(float)];
+
+hipError_t splitk_scratch(float **out)
+{
+    static std::mutex mu;
+    static float *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!ptr)
+            return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float *>(ptr);
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 int moe_big_token_tile() { return BN; }

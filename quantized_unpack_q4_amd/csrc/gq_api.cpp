@@ -412,6 +412,31 @@ gq_status gq_gemm_q4k_splitk(const void *w, const uint16_t *x, uint16_t *y, int6
                                                (hipStream_t)stream));
 }
 
+gq_status gq_gemm_q4k_splitk_static(const void *w, const uint16_t *x, uint16_t *y, int64_t M,
+                                    int64_t K, int64_t N, int64_t splits, void *stream)
+{
+    static const char fn[] = "gq_gemm_q4k_splitk_static";
+    int s = 0;
+    GQ_TRY(splitk_count(fn, M, K, N, splits, &s));
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "y", y));
+    const size_t need = (size_t)s * (size_t)N * (size_t)M * sizeof(float);
+    if (need > gq::kSplitkScratchBytes)
+        return fail(GQ_EWORKSPACE,
+                    "%s: %d runs of binary32 partials need %zu bytes, above the static scratch "
+                    "of %zu bytes (fewer splits, or gq_gemm_q4k_splitk with a workspace)",
+                    fn, s, need, gq::kSplitkScratchBytes);
+    float *ws = nullptr;
+    const hipError_t e = gq::splitk_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(GQ_EHIP, "%s: device address of the static scratch: %s", fn,
+                    hipGetErrorString(e));
+    return launched(fn, gq::launch_gemm_splitk(w, x, y, M, K, N, s, ws, (hipStream_t)stream));
+}
+
+size_t gq_gemm_q4k_splitk_static_max_bytes(void) { return gq::kSplitkScratchBytes; }
+
 size_t gq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk)
 {
     size_t off[7];

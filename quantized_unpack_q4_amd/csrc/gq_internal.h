@@ -90,6 +90,10 @@ hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_
 int gemm_splitk_choice(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_splitk(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                               int64_t N, int splits, float *ws, hipStream_t s);
+// The library's static split-K scratch (no allocation): its size, and its
+// device address on the current device (looked up once per device).
+constexpr size_t kSplitkScratchBytes = (size_t)64 << 20;
+hipError_t splitk_scratch(float **out);
 
 // Mixture-of-experts pieces; ws_off are the region offsets of gq_moe_workspace_offsets.
 struct MoeArgs {

@@ -25,7 +25,8 @@ MAX_BATCH = 16
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
     "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_splitk",
-    "gq_gemm_q4k_splitk_workspace_bytes",
+    "gq_gemm_q4k_splitk_workspace_bytes", "gq_gemm_q4k_splitk_static",
+    "gq_gemm_q4k_splitk_static_max_bytes",
     "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
     "gq_moe_gemm_q8_0_input_weighted", "gq_moe_route", "gq_quantize_q8k", "gq_gemv_q4k_q8k",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.gq_gemv_q4k_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.gq_gemm_q4k_splitk.restype = st
         L.gq_gemm_q4k_splitk.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        L.gq_gemm_q4k_splitk_static.restype = st
+        L.gq_gemm_q4k_splitk_static.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
+        L.gq_gemm_q4k_splitk_static_max_bytes.restype = sz
+        L.gq_gemm_q4k_splitk_static_max_bytes.argtypes = []
         L.gq_gemm_q4k_splitk_workspace_bytes.restype = sz
         L.gq_gemm_q4k_splitk_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.gq_gemm_q8_0.restype = st
@@ -227,6 +232,15 @@ def gq_gemm_q4k_splitk(w, x, y, M, K, N, splits, ws, ws_bytes=None, stream=None)
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gq_gemm_q4k_splitk(_ptr(w), _ptr(x), _ptr(y), M, K, N, splits, _ptr(ws),
                                     ws_bytes, _stream(stream)))
+
+
+def gq_gemm_q4k_splitk_static(w, x, y, M, K, N, splits=0, stream=None):
+    _check(lib().gq_gemm_q4k_splitk_static(_ptr(w), _ptr(x), _ptr(y), M, K, N, splits,
+                                           _stream(stream)))
+
+
+def gq_gemm_q4k_splitk_static_max_bytes() -> int:
+    return lib().gq_gemm_q4k_splitk_static_max_bytes()
 
 
 def gq_moe_workspace_bytes(T, H, I, E, topk) -> int:
