@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Q4_K fused-dequant GEMV weight GB/s (decode); dequant-GEMM TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP16_PEAK_TFLOPS = 2500.0    # MI355X dense binary16 matrix cores
+WARM_FLOOR_S = 0.5           # least sustained warm-up before the timed steps
 LAYER = (("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
          ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336))
 N_LAYERS = 32
@@ -52,12 +53,17 @@ class Stack:
     """The 224 weight matrices of the decode stack, resident in HBM."""
 
     def __init__(self, torch, synth):
+        import hashlib
         self.mats = []
+        h = hashlib.sha256()
         for layer in range(N_LAYERS):
             for i, (name, M, K) in enumerate(LAYER):
                 t = layer * len(LAYER) + i
-                w = torch.from_numpy(synth.q4k_blocks(STACK_WORKLOAD, t, M, K)).cuda()
+                wh = synth.q4k_blocks(STACK_WORKLOAD, t, M, K)
+                h.update(wh.data)
+                w = torch.from_numpy(wh).cuda()
                 self.mats.append((name, M, K, t, w))
+        self.sha256 = h.hexdigest()
         self.weight_bytes = sum(q4k_bytes(M, K) for _, M, K, _, _ in self.mats)
 
 
@@ -197,28 +203,168 @@ def measured_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(synth, budget_s=12.0):
-    """The binary64 oracle on whole matrices of the stack (layer 0 onwards, in
-    order) until about budget_s seconds of oracle time are spent; one thread.
-    Input generation is not timed."""
+def cpu_threads():
+    """Host threads for the all-cores oracle runs: the CPUs this process may
+    use, at most 16 (one GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_runs(fn, nrows, threads, reps=3):
+    """Median, min and max seconds of fn(rows) over `reps` runs, the rows
+    [0, nrows) cut into `threads` contiguous ranges, each range one call on
+    its own host thread (the oracle's C code releases the interpreter lock);
+    the oracle's arithmetic is unchanged."""
+    import threading
+
+    import numpy as np
+    chunks = [c for c in np.array_split(np.arange(nrows), threads) if c.size]
+    ts = []
+    for _ in range(reps):
+        ths = [threading.Thread(target=fn, args=(c,)) for c in chunks]
+        a = time.perf_counter()
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
+        ts.append(time.perf_counter() - a)
+    ts.sort()
+    return ts[len(ts) // 2], ts[0], ts[-1]
+
+
+def cpu_baseline(synth):
+    """The binary64 oracle, as it stands, on the host cores: every workload on
+    one thread and on all cores (rows split over threads), median of 3 runs.
+    Large workloads run a fixed sample and are extrapolated linearly (rows for
+    products; tokens for the MoE layer; matrices for the decode stack), and
+    say so.  Input generation is not timed."""
+    import numpy as np
+
     import oracle
     oracle.lib()
-    done_bytes, mats, secs = 0, 0, 0.0
-    for t in range(N_LAYERS * len(LAYER)):
-        name, M, K = LAYER[t % len(LAYER)]
-        w = synth.q4k_blocks(STACK_WORKLOAD, t, M, K)
-        x = synth.activations_f32(STACK_WORKLOAD, 100 * t + 1, 1, K)
-        a = time.perf_counter()
-        oracle.gemv(oracle.Q4_K, w, x, M, K)
-        secs += time.perf_counter() - a
-        done_bytes += q4k_bytes(M, K)
-        mats += 1
-        if secs >= budget_s:
-            break
-    return {"value": round(done_bytes / secs / 1e9, 6), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "first %d of the 224 stack matrices (layer order q,k,v,o,gate,up,down), "
-                      "batch 1, all rows, %.1f s single-threaded binary64" % (mats, secs)}
+    nthr = cpu_threads()
+    out = {}
+
+    def both(name, fn, nrows, scale, unit_work, unit, sample, extrapolated, nrows_all=None,
+             scale_all=None):
+        r1 = _oracle_runs(fn, nrows, 1)
+        rn = _oracle_runs(fn, nrows_all or nrows, nthr)
+        sa = scale_all or scale
+        out[name] = {
+            "sample": sample, "extrapolated": extrapolated,
+            "single_thread_s": round(r1[0] * scale, 4),
+            "single_thread_s_min_max": [round(r1[1] * scale, 4), round(r1[2] * scale, 4)],
+            "all_cores_s": round(rn[0] * sa, 4),
+            "all_cores_s_min_max": [round(rn[1] * sa, 4), round(rn[2] * sa, 4)],
+            "unit": unit,
+            "single_thread_rate": round(unit_work / (r1[0] * scale), 6),
+            "all_cores_rate": round(unit_work / (rn[0] * sa), 6)}
+
+    # C0: Q8_0 256 x 1024, batch 1, whole
+    w = synth.q8_0_blocks(0, 0, 256, 1024)
+    x = synth.activations_f32(0, 0, 1, 1024)
+    both("q8_0_gemv_256x1024_b1", lambda r: oracle.gemv(oracle.Q8_0, w, x, 256, 1024, rows=r),
+         256, 1.0, synth.q8_0_bytes(256, 1024) / 1e9, "GB/s of weights", "whole", False)
+    # C1: Q4_K 4096 x 4096 (whole) and 14336 x 4096 (first quarter of the rows)
+    for M, K, nr in ((4096, 4096, 4096), (14336, 4096, 3584)):
+        w = synth.q4k_blocks(1, M, M, K)
+        x = synth.activations_f32(1, M, 1, K)
+        both("q4k_gemv_%dx%d_b1" % (M, K),
+             lambda r, w=w, x=x, M=M, K=K: oracle.gemv(oracle.Q4_K, w, x, M, K, rows=r),
+             nr, M / nr, q4k_bytes(M, K) / 1e9, "GB/s of weights",
+             "whole" if nr == M else "first %d of %d rows, times %d" % (nr, M, M // nr),
+             nr != M)
+    # C2: the decode stack, batch 1: the first eighth of the rows of layer 0's
+    # seven products, scaled to all rows and 32 layers
+    layer0 = []
+    for t, (name, M, K) in enumerate(LAYER):
+        layer0.append((synth.q4k_blocks(STACK_WORKLOAD, t, M, K),
+                       synth.activations_f32(STACK_WORKLOAD, 100 * t + 1, 1, K), M, K))
+    offs = np.cumsum([0] + [m[2] // 8 for m in layer0])
+
+    def stack_rows(rows):
+        for i, (w, x, M, K) in enumerate(layer0):
+            sel = rows[(rows >= offs[i]) & (rows < offs[i + 1])] - offs[i]
+            if sel.size:
+                oracle.gemv(oracle.Q4_K, w, x, M, K, rows=sel)
+    both("decode_stack_b1", stack_rows, int(offs[-1]), 8.0 * N_LAYERS,
+         stack_bytes_total() / 1e9, "GB/s of weights",
+         "first eighth of the rows of layer 0's q, k, v, o, gate, up, down, times 8 x 32", True)
+    del layer0
+    # C3: prefill 14336 x 4096 at 512 and 4096 tokens: a row sample over all
+    # tokens, scaled to all rows
+    M, K = 14336, 4096
+    w = synth.q4k_blocks(PREFILL_WORKLOAD, M, M, K)
+    for N, nr in ((512, 8), (4096, 2)):
+        x16 = synth.activations_f16(PREFILL_WORKLOAD, N, N, K)
+        both("prefill_%dx%dxN%d" % (M, K, N),
+             lambda r, x16=x16: oracle.gemm(oracle.Q4_K, w, x16, M, K, rows=r),
+             nr, M / nr, 2.0 * M * K * N / 1e9, "GFLOP/s",
+             "first %d rows (one thread) / first %d rows (one per thread) over all %d "
+             "tokens, scaled to %d rows" % (nr, nthr, N, M), True,
+             nrows_all=nthr, scale_all=M / nthr)
+    del w
+    # C4: the MoE layer (64 experts, top-8, 2048 / 1024) at 256 tokens: one
+    # token on one thread, one token per thread on all cores, scaled to 256
+    H, I, E, k, T = 2048, 1024, 64, 8, 256
+    wg = synth.q4k_blocks(MOE_WORKLOAD, 0, E * I, H)
+    wu = synth.q4k_blocks(MOE_WORKLOAD, 1, E * I, H)
+    wd = synth.q4k_blocks(MOE_WORKLOAD, 2, E * H, I)
+    x16 = synth.activations_f16(MOE_WORKLOAD, 0, T, H)
+    ids, wts = oracle.moe_route(synth.router_logits(MOE_WORKLOAD, 0, T, E), k)
+    wts = wts.astype(np.float32)
+
+    def moe_tokens(r):
+        oracle.moe_ffn(wg, wu, wd, x16[r], ids[r], wts[r], H, I, E)
+    both("moe_olmoe_T256", moe_tokens, 1, float(T), 2.0 * T * k * 3 * H * I / 1e9, "GFLOP/s",
+         "token 0 (one thread) / tokens 0..%d (one per thread), times 256 / %d"
+         % (nthr - 1, nthr), True, nrows_all=nthr, scale_all=T / nthr)
+    head = out["decode_stack_b1"]
+    return {"value": head["all_cores_rate"], "unit": "GB/s", "cores": nthr, "kind": "oracle",
+            "sample": "decode stack at batch 1: the first eighth of the rows of layer 0's "
+                      "seven products, extrapolated to all rows of 32 layers; median of 3 "
+                      "runs, rows split over %d threads" % nthr,
+            "single_thread_value": head["single_thread_rate"],
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "threads": nthr,
+            "configs": out}
+
+
+def make_receipt(torch, stack_sha256):
+    """Where and from what this line was measured."""
+    import hashlib
+
+    from quantized_unpack_q4_amd import build as gqbuild
+    info = {}
+    try:
+        info = json.load(open(gqbuild.BUILD_INFO))
+    except (OSError, ValueError):
+        pass
+    lib_h = hashlib.sha256()
+    with open(gqbuild.LIB, "rb") as fh:
+        lib_h.update(fh.read())
+    props = torch.cuda.get_device_properties(0)
+    return {"git_rev": info.get("git_rev"), "git_dirty": info.get("git_dirty"),
+            "hipcc": info.get("hipcc"), "source_sha256": info.get("source_sha256"),
+            "libgq_sha256": lib_h.hexdigest(),
+            "gpu": torch.cuda.get_device_name(0),
+            "gpu_arch": getattr(props, "gcnArchName", None),
+            "gpu_cus": props.multi_processor_count,
+            "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "decode_stack_weights_sha256": stack_sha256}
 
 
 def main():
@@ -256,6 +402,7 @@ def main():
 
     log("generating the decode stack ...")
     stack = Stack(torch, synth)
+    stack_sha256 = stack.sha256
     stream = torch.cuda.Stream()
 
     # the step: all 224 batch-1 products of the stack in one launch
@@ -268,11 +415,20 @@ def main():
     table = gq.GemvTable(items, batch=SB) if SB > 1 else gq.GemvTable(items)
     alg_bytes = sum(gemv_bytes(M, K, SB) for _, M, K, _, _ in stack.mats)
 
-    log("timing %d steps after %d warm-up steps" % (args.steps, args.warmup))
+    # W warm-up steps, continued until at least WARM_FLOOR_S of sustained
+    # load: the clocks of an idle GPU take ~0.1 s to come up, and a few
+    # steps (5 are ~4 ms) would time the ramp, not the kernel
+    log("timing %d steps after %d warm-up steps (and >= %.1f s of warm-up)"
+        % (args.steps, args.warmup, WARM_FLOOR_S))
+    warm_steps, tw = 0, time.perf_counter()
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
+        while warm_steps < args.warmup or time.perf_counter() - tw < WARM_FLOOR_S:
             table.run(stream)
+            warm_steps += 1
+            if warm_steps % 32 == 0:
+                torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - tw
     # one event pair around each launch, on the stream the kernel runs on: the
     # kernel's average duration without the gaps between launches
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -287,11 +443,15 @@ def main():
     sec = (time.perf_counter() - t0) / args.steps
     value = stack.weight_bytes / sec / 1e9
     # the step is one launch of the streaming kernel: its average duration
-    avg_dur = sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / args.steps
+    durs = sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
+    avg_dur = sum(durs) / args.steps
     achieved = alg_bytes / avg_dur / 1e9
 
-    extra = {"stack_b%d_one_launch" % SB: {"ms_per_step": round(sec * 1e3, 4),
-                                     "kernel_ms_events": round(avg_dur * 1e3, 4)}}
+    extra = {"stack_b%d_one_launch" % SB: {
+        "ms_per_step": round(sec * 1e3, 4), "kernel_ms_events": round(avg_dur * 1e3, 4),
+        "kernel_ms_median": round(durs[len(durs) // 2] * 1e3, 4),
+        "kernel_ms_min": round(durs[0] * 1e3, 4), "kernel_ms_max": round(durs[-1] * 1e3, 4),
+        "warmup_steps_run": warm_steps, "warmup_s": round(warm_s, 3)}}
     if args.copy_probe > 0:
         n = args.copy_probe << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -477,8 +637,8 @@ def main():
             del a16, b16
         ceil.update(probe_ceilings(torch, stream, pre, value, stack_bytes_total()))
         extra["measured_ceilings"] = ceil
-        # mixture of experts, OLMoE-1B-7B shape
-        import oracle  # routing only: the oracle's binary64 softmax/top-k on the host
+        # mixture of experts, OLMoE-1B-7B shape; routing by the device router
+        # (gq_moe_route), outside the timed layer
         H, I, E, k = 2048, 1024, 64, 8
         wg = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 0, E * I, H)).cuda()
         wu = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 1, E * I, H)).cuda()
@@ -487,9 +647,9 @@ def main():
         wbytes = 3 * E * q4k_bytes(I, H)
         for T in (256, 2048):
             x16 = torch.from_numpy(synth.activations_f16(MOE_WORKLOAD, 0, T, H)).cuda()
-            ids, wts = oracle.moe_route(synth.router_logits(MOE_WORKLOAD, 0, T, E), k)
-            ids_d = torch.from_numpy(ids).cuda()
-            wts_d = torch.from_numpy(wts.astype(np.float32)).cuda()
+            lg = torch.from_numpy(synth.router_logits(MOE_WORKLOAD, 0, T, E)).cuda()
+            ids_d, wts_d = gq.moe_route(lg, k, stream=stream)
+            torch.cuda.synchronize()
             need = gq.gq_moe_workspace_bytes(T, H, I, E, k)
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
             out = torch.empty((T, H), dtype=torch.float16, device="cuda")
@@ -498,9 +658,7 @@ def main():
             flops = 2.0 * T * k * 3 * H * I
             moe["T%d" % T] = {"us": round(s * 1e6, 1), "TFLOP/s": round(flops / s / 1e12, 1),
                               "weight_GB/s": round(wbytes / s / 1e9, 1)}
-            # the routing step on the device (gq_moe_route), timed apart: the
-            # layer above takes the host's binary64 routing as its input
-            lg = torch.from_numpy(synth.router_logits(MOE_WORKLOAD, 0, T, E)).cuda()
+            # the routing step itself (gq_moe_route), timed apart
             rid = torch.empty((T, k), dtype=torch.int32, device="cuda")
             rwt = torch.empty((T, k), dtype=torch.float32, device="cuda")
             s = event_time(torch, stream, lambda: gq.gq_moe_route(lg, rid, rwt, T, E, k, 0, stream))
@@ -517,7 +675,10 @@ def main():
         # expert) assignment, routed top-1 to the local expert
         ep = {}
         for T in (256, 2048):
-            ids, wts = oracle.moe_route(synth.router_logits(MOE_WORKLOAD, 0, T, E), k)
+            lg = torch.from_numpy(synth.router_logits(MOE_WORKLOAD, 0, T, E)).cuda()
+            ids_t, wts_t = gq.moe_route(lg, k, stream=stream)
+            torch.cuda.synchronize()
+            ids, wts = ids_t.cpu().numpy(), wts_t.cpu().numpy()
             tok, slot = np.nonzero(ids < E // 8)
             x16 = synth.activations_f16(MOE_WORKLOAD, 0, T, H)[tok]
             R = len(tok)
@@ -578,6 +739,7 @@ def main():
         del w8
 
     cpu = None if args.no_cpu else cpu_baseline(synth)
+    receipt = make_receipt(torch, stack_sha256)
 
     line = {
         "metric": METRIC,
@@ -590,7 +752,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_k weights, f32 activations and accumulation",
+        "dtype": ("q4_k weights x f32 activations (carried as a binary16 hi+lo pair, "
+                  "~22 significant bits, into v_dot2_f32_f16), f32 accumulation"
+                  if SB == 1 else
+                  "q4_k weights x f32 activations (binary16 hi+lo pair into f16 MFMA), "
+                  "f32 accumulation"),
         "data": "synthetic (seeded Q4_K blocks and N(0,1) activations)",
         "config": {"workload": "llama3-8b-shaped Q4_K decode stack, 32 layers x 7 GEMVs, "
                                "batch %d, one launch per step" % SB,
@@ -604,6 +770,7 @@ def main():
                      "avg_launch_us": round(avg_dur * 1e6, 3),
                      "alg_bytes_per_launch": int(alg_bytes)},
         "cpu_baseline": cpu,
+        "receipt": receipt,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

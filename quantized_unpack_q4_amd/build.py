@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -68,12 +69,51 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
+BUILD_INFO = os.path.join(PKG, "build_info.json")
+
+
+def _run_text(cmd) -> str:
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=30)
+        return r.stdout.strip() if r.returncode == 0 else ""
+    except (OSError, subprocess.SubprocessError):
+        return ""
+
+
+def write_build_info() -> dict:
+    """What was built from what: the git revision (with a flag for uncommitted
+    changes under the package, include/ and oracle/), the compiler version
+    and a SHA-256 over the HIP/C++ sources; written next to the library so
+    that benchmark receipts can quote it where no git checkout exists."""
+    import hashlib
+    import json
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for f in sorted(os.listdir(d)):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    info = {
+        "git_rev": _run_text(["git", "rev-parse", "HEAD"]) or None,
+        "git_dirty": bool(_run_text(["git", "status", "--porcelain", "--",
+                                     "quantized_unpack_q4_amd", "include", "oracle"])),
+        "hipcc": (_run_text([hipcc(), "--version"]).splitlines() or [""])[0] or None,
+        "offload_arch": ARCH,
+        "source_sha256": h.hexdigest(),
+        "built_unix": int(time.time()),
+    }
+    with open(BUILD_INFO, "w") as fh:
+        json.dump(info, fh, indent=1)
+    return info
+
+
 def build(jobs: int = 8, verbose: bool = False) -> str:
     srcs = SOURCES + PROBE_SOURCES
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = dict(zip(srcs, ex.map(_compile, srcs)))
     _link([objs[s] for s in SOURCES], LIB)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
+    write_build_info()
     if verbose:
         print("built", LIB, "and", PROBE_LIB)
     return LIB
