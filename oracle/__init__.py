@@ -75,6 +75,7 @@ def lib():
                                   vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
         L.orc_quantize_q8k.argtypes = [vp, i64, i64, vp, vp, vp]
         L.orc_gemv_q4k_q8k.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, vp]
+        L.orc_q4k_terms.argtypes = [vp, i64, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -297,3 +298,47 @@ def gemv_q4k_q8k(w, q, d, M: int, K: int, rows=None):
     S = np.empty((B, nr), np.float64)
     lib().orc_gemv_q4k_q8k(_p(w), _p(q), _p(d), M, K, B, _p(rows), nr, _p(y), _p(S))
     return y, S
+
+
+def q4k_terms(w, M: int, K: int, rows=None):
+    """The exact terms a = d*sc*q and c = dmin*m of every weight (w = a - c),
+    binary64 [nrows][K] each, for the given rows (all if None)."""
+    w = _u8(w)
+    _check(Q4_K, w, M, K)
+    rb = row_bytes(Q4_K, K)
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        w = np.ascontiguousarray(w[:M * rb].reshape(M, rb)[rows]).reshape(-1)
+        M = rows.size
+    a = np.empty((M, K), np.float64)
+    c = np.empty((M, K), np.float64)
+    lib().orc_q4k_terms(_p(w), M, K, _p(a), _p(c))
+    return a, c
+
+
+def gemm_q4k_q8k(w, q, d, M: int, K: int, rows=None, toks=None):
+    """Y[t][i] = sum_k w_exact[rows[i]][k] * d[toks[t]][k/256] * q[toks[t]][k]
+    (binary64; the integer-dot product over 8-bit activation codes) and its
+    bound S = sum_k (|d sc q4| + |dmin m|) * |d_x q| -- the plain loop of
+    gemv_q4k_q8k with the tokens as its batch rows, Y laid out [tokens][rows]."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.int8).reshape(-1, K))
+    d = np.ascontiguousarray(np.asarray(d, dtype=np.float32).reshape(q.shape[0], K // 256))
+    if toks is not None:
+        toks = np.asarray(toks, dtype=np.int64).reshape(-1)
+        q, d = np.ascontiguousarray(q[toks]), np.ascontiguousarray(d[toks])
+    return gemv_q4k_q8k(w, q, d, M, K, rows=rows)
+
+
+def gemm_q4k_q8k_matmul(w, q, d, M: int, K: int, rows=None, toks=None):
+    """gemm_q4k_q8k for large samples: the exact weight terms from q4k_terms
+    (C), the activation values d_x * q exact in binary64, and every product and
+    sum by numpy's binary64 matrix product (a library primitive in place of the
+    loop; only the summation order differs)."""
+    q = np.asarray(q, dtype=np.int8).reshape(-1, K)
+    d = np.asarray(d, dtype=np.float32).reshape(q.shape[0], K // 256)
+    if toks is not None:
+        toks = np.asarray(toks, dtype=np.int64).reshape(-1)
+        q, d = q[toks], d[toks]
+    a, c = q4k_terms(w, M, K, rows=rows)
+    xv = q.astype(np.float64) * np.repeat(d.astype(np.float64), 256, axis=1)
+    return xv @ (a - c).T, np.abs(xv) @ (np.abs(a) + np.abs(c)).T

@@ -553,3 +553,26 @@ void orc_gemv_q4k_q8k(const uint8_t *w, const int8_t *q, const float *d, int64_t
         }
     }
 }
+
+/* The two exact terms of every Q4_K weight, w = a - c with a = d * sc_j * q
+ * and c = dmin * m_j, in binary64 (both products are exact there), for an
+ * M x K matrix: a[r][k], c[r][k].  The integer-dot product scales exact
+ * integer sums, so its reference uses these terms unrounded (as in
+ * orc_gemv_q4k_q8k), and its error bound weighs |a| + |c|. */
+void orc_q4k_terms(const uint8_t *w, int64_t M, int64_t K, double *a, double *c)
+{
+    int64_t nsb = K / QK_K;
+    for (int64_t r = 0; r < M; r++) {
+        for (int64_t s = 0; s < nsb; s++) {
+            const uint8_t *blk = w + (r * nsb + s) * Q4_K_BYTES;
+            double dd = orc_half_to_double(le16(blk));
+            double dm = orc_half_to_double(le16(blk + 2));
+            for (int k = 0; k < QK_K; k++) {
+                int sc, m;
+                q4k_scale_min(blk + 4, k / 32, &sc, &m);
+                a[r * K + s * QK_K + k] = dd * (double)sc * (double)q4k_quant(blk + 16, k);
+                c[r * K + s * QK_K + k] = dm * (double)m;
+            }
+        }
+    }
+}

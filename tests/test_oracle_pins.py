@@ -676,3 +676,42 @@ def test_gemm_matmul_equals_gemm(orc):
         rows, toks = np.array([0, 5, M - 1]), np.array([N - 1, 2])
         y3, S3 = orc.gemm_matmul(fmt, w, x16, M, K, rows=rows, toks=toks)
         assert np.all(np.abs(y3 - y[np.ix_(toks, rows)]) <= 1e-13 * S[np.ix_(toks, rows)])
+
+
+def test_q4k_terms_against_independent_decoder(orc):
+    """The two exact weight terms from the C decoder equal those of the
+    independent numpy table decoder, and a - c rounded once to binary32 is the
+    oracle's binary32 weight."""
+    M, K = 7, 512
+    w = synth.q4k_blocks(43, 0, M, K)
+    dd, dmin, sc, m, qq = np_decode_q4k(w.reshape(-1, 144))
+    A = (dd[:, None] * np.repeat(sc, 32, axis=1) * qq).reshape(M, K)
+    C = (dmin[:, None] * np.repeat(m, 32, axis=1)).reshape(M, K)
+    a, c = orc.q4k_terms(w, M, K)
+    assert np.array_equal(a, A) and np.array_equal(c, C)
+    w32, _ = orc.dequant(orc.Q4_K, w, M, K)
+    assert np.array_equal((a - c).astype(np.float32).view(np.uint32), w32.view(np.uint32))
+    a2, c2 = orc.q4k_terms(w, M, K, rows=[6, 1])
+    assert np.array_equal(a2, a[[6, 1]]) and np.array_equal(c2, c[[6, 1]])
+
+
+def test_gemm_q4k_q8k_forms_agree(orc):
+    """The integer-dot product over many tokens: the plain loop with tokens as
+    its batch rows, the matrix-product form, and numpy on the independently
+    decoded weights all agree; a token subset indexes alike."""
+    M, K, N = 11, 512, 9
+    w = synth.q4k_blocks(44, 0, M, K)
+    x = synth.activations_f32(44, 1, N, K)
+    q, d, _ = orc.quantize_q8k(x, K)
+    y, S = orc.gemm_q4k_q8k(w, q, d, M, K)
+    y2, S2 = orc.gemm_q4k_q8k_matmul(w, q, d, M, K)
+    assert y.shape == (N, M)
+    assert np.all(np.abs(y - y2) <= 1e-13 * S) and np.allclose(S, S2, rtol=1e-13, atol=0)
+    dd, dmin, sc, m, qq = np_decode_q4k(w.reshape(-1, 144))
+    W = (dd[:, None] * np.repeat(sc, 32, axis=1) * qq
+         - dmin[:, None] * np.repeat(m, 32, axis=1)).reshape(M, K)
+    ref = (np.repeat(d.astype(np.float64), 256, axis=1) * q) @ W.T
+    assert np.all(np.abs(y - ref) <= 1e-12 * S)
+    toks, rows = np.array([8, 2]), np.array([0, 10, 5])
+    y3, _ = orc.gemm_q4k_q8k_matmul(w, q, d, M, K, rows=rows, toks=toks)
+    assert np.all(np.abs(y3 - y[np.ix_(toks, rows)]) <= 1e-13 * S[np.ix_(toks, rows)])
