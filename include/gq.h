@@ -333,6 +333,24 @@ gq_status gq_quantize_q8k(const float *x, int8_t *q, float *d, int32_t *bsum, in
 gq_status gq_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d, const int32_t *bsum,
                           float *y, int64_t M, int64_t K, int64_t B, void *stream);
 
+/* gq_gemm_q4k_q8k: the integer-dot matrix product (prefill) over 8-bit
+ * activation codes from gq_quantize_q8k (with B = N token rows):
+ *   Y[n][r] = sum_k w(r, k) * d[n][k/256] * q[n][k]
+ * for a Q4_K matrix (M rows of K/256 super-blocks), q [N][K] int8, d [N][K/256]
+ * float, Y [N][M] float (binary32, not rounded to binary16).  The reading of
+ * the pages is that of gq_quantize_q8k (page "Frink Inference: the Rust
+ * alternative to llama.cpp", section "Where llama.cpp is still ahead",
+ * K-quant item: llama.cpp's 8-bit activation blocks, the source of its logit
+ * drift; opt-in here, beside the binary16 product gq_gemm_q4k).  Per
+ * super-block the sums of q4 * sc * q and of m * q are exact integers (int8
+ * matrix cores, the 6-bit scale split into two 3-bit halves folded into the
+ * weight bytes); d, dmin and d[n] apply in binary32.  Error against the exact
+ * value of the same formula: within 1e-5 * sum_k (|d sc q4| + |dmin m|) *
+ * |d[n] q[n][k]|.  Requires K % 256 == 0, N*K <= 2^34; M = 0 or N = 0 does
+ * nothing; w, q, d, y 16-byte aligned. */
+gq_status gq_gemm_q4k_q8k(const void *w, const int8_t *q, const float *d, float *y, int64_t M,
+                          int64_t K, int64_t N, void *stream);
+
 /* Dequantization probes: write every weight of an M x K matrix as binary32
  * (out32, [M][K]) and/or binary16 (out16, [M][K] bits); either may be NULL.
  * Bit-exact with the rounding rule above. */

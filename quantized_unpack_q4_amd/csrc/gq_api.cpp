@@ -616,6 +616,26 @@ gq_status gq_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d, const 
                                                 (hipStream_t)stream));
 }
 
+gq_status gq_gemm_q4k_q8k(const void *w, const int8_t *q, const float *d, float *y, int64_t M,
+                          int64_t K, int64_t N, void *stream)
+{
+    static const char fn[] = "gq_gemm_q4k_q8k";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    GQ_TRY(check_dim(fn, "N", N, true));
+    if (M * (K / 256) * 144 >= ((int64_t)1 << 40) || N * K > ((int64_t)1 << 34) ||
+        (M + 127) / 128 * ((N + 63) / 64) > 0x7fffffff || M > 0x7fffffff || N > 0x7fffffff)
+        return fail(GQ_ESHAPE, "%s: M = %lld, K = %lld, N = %lld is too large", fn, (long long)M,
+                    (long long)K, (long long)N);
+    if (M == 0 || N == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "q", q));
+    GQ_TRY(check_ptr(fn, "d", d));
+    GQ_TRY(check_ptr(fn, "y", y));
+    return launched(fn, gq::launch_gemm_q4k_q8k(w, q, d, y, M, K, N, (hipStream_t)stream));
+}
+
 gq_status gq_dequant_q8_0(const void *w, float *out32, uint16_t *out16, int64_t M, int64_t K,
                           void *stream)
 {

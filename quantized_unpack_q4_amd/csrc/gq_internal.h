@@ -124,6 +124,11 @@ hipError_t launch_gemv_q4k_q8k(const void *w, const int8_t *q, const float *d,
                                const int32_t *bsum, float *y, int64_t M, int64_t K, int B,
                                hipStream_t s);
 
+// The integer-dot matrix product over 8-bit activation codes (prefill):
+// y [N][M] binary32 from Q4_K w, codes q [N][K] and scales d [N][K/256].
+hipError_t launch_gemm_q4k_q8k(const void *w, const int8_t *q, const float *d, float *y, int64_t M,
+                               int64_t K, int64_t N, hipStream_t s);
+
 // Top-k routing of T tokens over E <= 256 experts (one wave per token).
 hipError_t launch_moe_route(const float *logits, int32_t *ids, float *wts, int64_t T, int64_t E,
                             int64_t topk, bool renorm, hipStream_t s);

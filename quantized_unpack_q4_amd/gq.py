@@ -29,6 +29,7 @@ EXPORTS = (
     "gq_gemm_q4k_splitk_static_max_bytes",
     "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
     "gq_moe_gemm_q8_0_input_weighted", "gq_moe_route", "gq_quantize_q8k", "gq_gemv_q4k_q8k",
+    "gq_gemm_q4k_q8k",
     "gq_moe_workspace_bytes", "gq_moe_workspace_offsets", "gq_dequant_q8_0",
     "gq_dequant_q4k", "gq_last_error", "gq_status_str", "gq_version",
 )
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
         L.gq_quantize_q8k.restype = st
         L.gq_quantize_q8k.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+        L.gq_gemm_q4k_q8k.restype = st
+        L.gq_gemm_q4k_q8k.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         L.gq_gemv_q4k_q8k.restype = st
         L.gq_gemv_q4k_q8k.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.gq_moe_route.restype = st
@@ -278,6 +281,10 @@ def gq_quantize_q8k(x, q, d, bsum, B, K, stream=None):
 def gq_gemv_q4k_q8k(w, q, d, bsum, y, M, K, B, stream=None):
     _check(lib().gq_gemv_q4k_q8k(_ptr(w), _ptr(q), _ptr(d), _ptr(bsum), _ptr(y), M, K, B,
                                  _stream(stream)))
+
+
+def gq_gemm_q4k_q8k(w, q, d, y, M, K, N, stream=None):
+    _check(lib().gq_gemm_q4k_q8k(_ptr(w), _ptr(q), _ptr(d), _ptr(y), M, K, N, _stream(stream)))
 
 
 def gq_dequant_q8_0(w, out32, out16, M, K, stream=None):

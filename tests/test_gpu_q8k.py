@@ -116,3 +116,73 @@ def test_gemv_q4k_q8k_zero_and_one_hot():
     yr, S = oracle.gemv_q4k_q8k(w, host(q), host(d), M, K)
     err = np.abs(host(y).astype(np.float64) - yr)
     assert np.all(err <= 2.0 ** -21 * S), (err / S).max()
+
+
+# ---------------------------------------------------------------------------
+# The integer-dot matrix product (prefill): gq_gemm_q4k_q8k
+# ---------------------------------------------------------------------------
+
+def _gemm_q8k(w, x, M, K):
+    """Quantize x on the device (codes checked bit-exact against the oracle's)
+    and run the product; returns (Y, codes, scales)."""
+    torch = torch_cuda()
+    N = x.shape[0]
+    q, d, _ = gq.quantize_q8k(dev(x))
+    qh, dh = host(q), host(d)
+    qr, dr, _ = oracle.quantize_q8k(x, K)
+    assert np.array_equal(qh, qr) and np.array_equal(dh.view(np.uint32), dr.view(np.uint32))
+    y = torch.full((N, M), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_gemm_q4k_q8k(dev(w), q, d, y, M, K, N)
+    return host(y).astype(np.float64), qh, dh
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 256, 64), (130, 512, 37), (300, 1024, 200), (1, 256, 1),
+                                   (257, 768, 65), (64, 2048, 130)])
+def test_gemm_q4k_q8k_parity(M, K, N):
+    """Ragged rows and tokens around the 128 x 64 workgroup tiles, every
+    output against the oracle's plain loop."""
+    say("gemm q4k q8k", M, K, N)
+    w = synth.q4k_blocks(75, M, M, K)
+    x = _special_x(N, K, 75 + N)
+    y, q, d = _gemm_q8k(w, x, M, K)
+    yr, S = oracle.gemm_q4k_q8k(w, q, d, M, K)
+    r = within(y, yr, S, TOL, "gemm q8k %dx%dx%d" % (M, K, N))
+    say("  max err/S", r)
+
+
+def test_gemm_q4k_q8k_one_hot_exact():
+    """A code of 1 at one position with scale 1 reads out the binary32 weight
+    exactly: d*(8*P_hi + P_lo) - dmin*P_m is d*sc*q4 - dmin*m rounded once."""
+    torch = torch_cuda()
+    M, K = 200, 1024
+    w = synth.q4k_blocks(76, 0, M, K)
+    w32, _ = oracle.dequant(oracle.Q4_K, w, M, K)
+    ks = np.array([0, 31, 32, 100, 255, 256, 511, 777, 1023])
+    N = ks.size
+    q = np.zeros((N, K), np.int8)
+    q[np.arange(N), ks] = 1
+    d = np.ones((N, K // 256), np.float32)
+    y = torch.full((N, M), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_gemm_q4k_q8k(dev(w), dev(q), dev(d), y, M, K, N)
+    yh = host(y)
+    for i, k in enumerate(ks):
+        assert np.array_equal(yh[i].view(np.uint32), w32[:, k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("M,K,N", [(14336, 4096, 512), (4096, 14336, 512), (14336, 4096, 4096)])
+def test_gemm_q4k_q8k_prefill_sampled(M, K, N):
+    """Prefill shapes at full size: 512 rows over all tokens and all rows over
+    16 tokens (tile edges included), against the oracle's matrix-product form."""
+    say("gemm q4k q8k full", M, K, N)
+    g = np.random.default_rng(77)
+    w = synth.q4k_blocks(3, M, M, K)
+    x = synth.activations_f32(3, N + 7, N, K)
+    y, q, d = _gemm_q8k(w, x, M, K)
+    assert np.isfinite(y).all()
+    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], g.choice(M, 508, replace=False)]))
+    yr, S = oracle.gemm_q4k_q8k_matmul(w, q, d, M, K, rows=rows)
+    r1 = within(y[:, rows], yr, S, TOL, "%d rows x all tokens" % rows.size)
+    toks = np.unique(np.concatenate([[0, 63, 64, N - 1], g.choice(N, 12, replace=False)]))
+    yr2, S2 = oracle.gemm_q4k_q8k_matmul(w, q, d, M, K, toks=toks)
+    r2 = within(y[toks], yr2, S2, TOL, "all rows x %d tokens" % toks.size)
+    say("  max err/S", r1, r2)
