@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Q4_K fused-dequant GEMV weight GB/s (decode); dequant-GEMM TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP16_PEAK_TFLOPS = 2500.0    # MI355X dense binary16 matrix cores
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix cores
 WARM_FLOOR_S = 0.5           # least sustained warm-up before the timed steps
 LAYER = (("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
          ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336))
@@ -119,10 +120,13 @@ def probe_ceilings(torch, stream, prefill, decode_gbs, stack_bytes):
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.empty(16 * cus * 4, dtype=torch.int32, device="cuda")
     sp = ctypes.c_void_p(stream.cuda_stream)
-    # the best of two read forms and four grid sizes
+    # the best of four read forms (grid-stride; per-workgroup range with
+    # cached or non-temporal loads, 256 or 512 threads) and several grids
     read_gbs, read_cfg = 0.0, None
-    for kind in (0, 1):
-        for mult in (2, 4, 8, 16):
+    forms = ("grid-stride", "per-workgroup range", "per-workgroup range, non-temporal",
+             "per-workgroup range, non-temporal, 512 threads")
+    for kind in (0, 1, 2, 3):
+        for mult in ((1, 2, 4) if kind == 3 else (2, 4, 8, 16)):
             grid = mult * cus
 
             def read():
@@ -131,8 +135,7 @@ def probe_ceilings(torch, stream, prefill, decode_gbs, stack_bytes):
                     raise RuntimeError("gqp_stream_read launch failed")
             s = event_time(torch, stream, read, reps=10, warm_s=0.02)
             if nbytes / s / 1e9 > read_gbs:
-                read_gbs, read_cfg = nbytes / s / 1e9, "%s, %d workgroups" % (
-                    ("grid-stride", "per-workgroup range")[kind], grid)
+                read_gbs, read_cfg = nbytes / s / 1e9, "%s, %d workgroups" % (forms[kind], grid)
     out["stream_read_%dB_GB/s" % nbytes] = round(read_gbs, 1)
     out["stream_read_form"] = read_cfg
     out["decode_stack_frac_of_stream_read"] = round(decode_gbs / read_gbs, 4)
@@ -147,7 +150,8 @@ def probe_ceilings(torch, stream, prefill, decode_gbs, stack_bytes):
     mfma_tf = P.gqp_mfma_f16_flops(iters, cus) / s / 1e12
     out["mfma_f16_register_loop_TFLOP/s"] = round(mfma_tf, 1)
     for key, v in prefill.items():
-        out["prefill_%s_frac_of_mfma_loop" % key] = round(v["TFLOP/s"] / mfma_tf, 4)
+        if "TFLOP/s" in v:
+            out["prefill_%s_frac_of_mfma_loop" % key] = round(v["TFLOP/s"] / mfma_tf, 4)
     del msink
     return out
 
@@ -606,6 +610,21 @@ def main():
                         "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4),
                         "splits": need // (4 * N * M)}
                     del ws
+                # the opt-in integer-dot product over 8-bit activation codes
+                # (gq_quantize_q8k, then gq_gemm_q4k_q8k; binary32 out)
+                x32 = x16.float()
+                xq, xd, xs = gq.quantize_q8k(x32)
+                y32 = torch.empty((N, M), dtype=torch.float32, device="cuda")
+                s = event_time(torch, stream, lambda: gq.gq_gemm_q4k_q8k(
+                    w, xq, xd, y32, M, K, N, stream))
+                sq = event_time(torch, stream, lambda: gq.gq_quantize_q8k(
+                    x32, xq, xd, xs, N, K, stream))
+                tf = 2.0 * M * K * N / s / 1e12
+                pre["%dx%dxN%d_int_dot" % (M, K, N)] = {
+                    "us": round(s * 1e6, 1), "TOP/s": round(tf, 1),
+                    "frac_int8_peak": round(tf / INT8_PEAK_TOPS, 4),
+                    "quantize_us": round(sq * 1e6, 1)}
+                del x32, xq, xd, xs, y32
                 del x16, y16
             del w
         # the same product over Q8_0 weights (the LDS-tile kernel)

@@ -7,6 +7,9 @@
 //                    grid-stride with four 16-byte loads per thread in flight
 //                    (kind 0) or each workgroup streaming its own contiguous
 //                    range with eight loads per thread in flight (kind 1);
+//                    kinds 2 and 3: the range form with non-temporal loads
+//                    (every instruction reads whole cache lines), 256 or 512
+//                    threads per workgroup;
 //   gqp_mfma_f16     a register-only loop of v_mfma_f32_32x32x16_f16 on eight
 //                    independent accumulators per wave, eight waves (two per
 //                    SIMD) per workgroup.
@@ -45,24 +48,30 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint4 *
         sink[(long long)blockIdx.x * (kReadThreads / 64) + threadIdx.x / 64] = acc;
 }
 
-__global__ __launch_bounds__(kReadThreads) void range_read_kernel(const uint4 *__restrict__ p,
-                                                                  long long n16,
-                                                                  uint32_t *__restrict__ sink)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+
+template <bool NT = false, int T = kReadThreads>
+__global__ __launch_bounds__(T) void range_read_kernel(const uint4 *__restrict__ p, long long n16,
+                                                       uint32_t *__restrict__ sink)
 {
     constexpr int U = 8;
     const long long lo = n16 * blockIdx.x / gridDim.x, hi = n16 * (blockIdx.x + 1) / gridDim.x;
     long long i = lo + threadIdx.x;
     uint32_t acc = 0;
-    for (; i + (U - 1) * kReadThreads < hi; i += U * kReadThreads) {
+    for (; i + (U - 1) * T < hi; i += U * T) {
         uint4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = p[i + u * kReadThreads];
+        for (int u = 0; u < U; ++u) {
+            const g_u32x4 *a = (const g_u32x4 *)(p + i + u * T);
+            const u32x4 t = NT ? __builtin_nontemporal_load(a) : *a;
+            v[u] = make_uint4(t.x, t.y, t.z, t.w);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
             acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
-    for (; i < hi; i += kReadThreads) {
+    for (; i < hi; i += T) {
         const uint4 a = p[i];
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
@@ -70,7 +79,7 @@ __global__ __launch_bounds__(kReadThreads) void range_read_kernel(const uint4 *_
     for (int off = 32; off > 0; off >>= 1)
         acc ^= (uint32_t)__shfl_xor((int)acc, off, 64);
     if ((threadIdx.x & 63) == 0)
-        sink[(long long)blockIdx.x * (kReadThreads / 64) + threadIdx.x / 64] = acc;
+        sink[(long long)blockIdx.x * (T / 64) + threadIdx.x / 64] = acc;
 }
 
 __global__ __launch_bounds__(kMfmaThreads, 1) void mfma_f16_kernel(float *__restrict__ sink,
@@ -108,14 +117,22 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void mfma_f16_kernel(float *__rest
 extern "C" int gqp_stream_read(const void *buf, long long bytes, uint32_t *sink, int grid,
                                int kind, void *stream)
 {
-    if (!buf || !sink || bytes <= 0 || bytes % 16 != 0 || grid <= 0 || kind < 0 || kind > 1)
+    if (!buf || !sink || bytes <= 0 || bytes % 16 != 0 || grid <= 0 || kind < 0 || kind > 3)
         return (int)hipErrorInvalidValue;
+    const uint4 *p = (const uint4 *)buf;
+    const hipStream_t s = (hipStream_t)stream;
     if (kind == 0)
-        hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0,
-                           (hipStream_t)stream, (const uint4 *)buf, bytes / 16, sink);
+        hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0, s, p,
+                           bytes / 16, sink);
+    else if (kind == 1)
+        hipLaunchKernelGGL((range_read_kernel<false>), dim3((unsigned)grid), dim3(kReadThreads),
+                           0, s, p, bytes / 16, sink);
+    else if (kind == 2)
+        hipLaunchKernelGGL((range_read_kernel<true>), dim3((unsigned)grid), dim3(kReadThreads), 0,
+                           s, p, bytes / 16, sink);
     else
-        hipLaunchKernelGGL(range_read_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0,
-                           (hipStream_t)stream, (const uint4 *)buf, bytes / 16, sink);
+        hipLaunchKernelGGL((range_read_kernel<true, 512>), dim3((unsigned)grid), dim3(512), 0, s,
+                           p, bytes / 16, sink);
     return (int)hipGetLastError();
 }
 
