@@ -76,21 +76,43 @@ typedef enum gq_status {
  * w: M rows of K/32 Q8_0 blocks (M*K/32*34 bytes).  x: [B][K] float.  y: [B][M] float.
  * Requires K % 32 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH.  With B >= 2 and
  * K % 64 == 0 the block sums run on the matrix cores with x carried as a
- * binary16 hi + lo pair scaled per activation row and 32-weight block: x is
- * kept to 2^-24 of the largest |x| of its block, the products are exact and
- * the sums binary32.  Within 2 <= B <= 16 an activation row's result does not
- * depend on B or on the other rows (B = 1 runs another kernel). */
+ * binary16 hi + lo pair scaled per activation row and 32-weight block: every
+ * value at least 2^-20 of its block's largest |x| keeps a relative error
+ * below 2^-19; a block whose non-zero |x| span more than 2^20 is computed in
+ * binary32 instead (d*q times x).  Accuracy: see GQ_GEMV_ACCURACY below.
+ * Within 2 <= B <= 16 an activation row's result does not depend on B or on
+ * the other rows (B = 1 runs another kernel). */
 gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                        void *stream);
 
 /* Q4_K matrix-vector product, binary32 activations; same contract as
  * gq_gemv_q8_0 with w holding M rows of K/256 super-blocks (M*K/256*144
- * bytes).  Requires K % 256 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH.  Batch 1 runs
- * binary32 arithmetic on the vector units (the activation split into two
- * binary16 parts for the packed dot products); batches 2..16 run the
- * 4-bit-quant x binary16-split-activation products on the matrix cores
- * (see gq_gemv_q4k_multi_batched); both keep |y - y_exact| within 1e-5 of
- * sum_k |w_k x_k|. */
+ * bytes).  Requires K % 256 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH.  Per 32-weight
+ * sub-block the sum is taken in the factored form
+ * (d*sc)*sum(q*x) - (dmin*m)*sum(x), with x carried as a binary16 hi + lo
+ * pair (products exact, sums binary32): batch 1 on packed dot products with
+ * one power-of-two scale per sub-block, batches 2..16 on the matrix cores with
+ * one per activation row and super-block (see gq_gemv_q4k_multi_batched).
+ * Every split value keeps a relative error below 2^-19.  A sub-block whose
+ * non-zero |x| span more than 2^20 (batch 1; batches 2..16: holding a
+ * non-zero |x| below 2^-20 of its super-block's largest), or that holds more
+ * than 1/16 of the sum of |x| over its super-block, is computed exactly
+ * instead: each weight as its binary32 value times x in binary32.  K above
+ * 16384 at batch 1 (and matrices beyond the matrix-core kernel's 32-bit
+ * offsets) run a kernel that dequantizes every weight to binary32 first.
+ *
+ * GQ_GEMV_ACCURACY (every binary32-activation product of this header): with
+ * S = sum_k |w_k x_k| (w the binary32 weight) and finite inputs,
+ * |y - y_exact| <= 1e-5 * S, plus up to a few multiples of 2^-149 when y
+ * falls in the binary32 subnormal range, provided no result or partial sum
+ * overflows binary32 and the factored sums do not cancel heavily: their
+ * rounding follows S_f = sum over split sub-blocks of
+ * (|d*sc*q_k| + |dmin*m|) * |x_k|, and the bound is met while S_f stays
+ * within a few times S.  Rows of the seeded generator have S_f / S of 1.2 to
+ * 1.6; a row can exceed it only when d*sc*q and dmin*m nearly cancel for most
+ * of its weights at once.  Single large activations (their sub-block goes to
+ * the exact path), wide ranges inside one vector and whole vectors from 1e-40
+ * to 1e30 are inside the bound (tested). */
 gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                       void *stream);
 
