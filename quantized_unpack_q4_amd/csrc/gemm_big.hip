@@ -59,7 +59,9 @@ namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
 typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const u32x3 g_u32x3;
 
 __device__ __forceinline__ uint4 gload16(const uint8_t *p)
 {
@@ -224,11 +226,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
             load_lds16(xk, xoff[q], (buf ? mb1 : mb0) + 1024u * q);
     };
 
-    // packed weights of the two steps ahead: slot = step & 1
+    // packed weights of the two steps ahead: slot = step & 1.  Quant groups
+    // 0 and 1 need only the first 12 header bytes (d, dmin and scale/min bytes
+    // 0-7); loading 16 would leave the fourth register of the load dead, and
+    // the compiler may then reuse it while the load is in flight, which costs
+    // a wait for every load issued before it (the activation copies included).
     uint4 rh[2], rq[2];
     auto issue_w = [&](int kt, int slot, int g) {
         const uint8_t *blk = wrow + (size_t)(kt >> 2) * kQ4kBytes;
-        rh[slot] = gload16(blk);
+        if (g < 2) {
+            const u32x3 v = *(g_u32x3 *)(blk);
+            rh[slot] = make_uint4(v.x, v.y, v.z, 0u);
+        } else {
+            rh[slot] = gload16(blk);
+        }
         rq[slot] = gload16(blk + 16 + 32 * g + 16 * h);
     };
     // A operands of one step from slot `slot`, quant group g
