@@ -136,49 +136,24 @@ struct BigParams {
 // assignment list; h = binary16(silu(g) * u) is written.  MODE kBigDown:
 // 32 NW rows of an expert's down matrix against its rows of h, binary32
 // outputs.
-template <int MODE, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams p)
+// One tile: weight rows from m0 (BM = 32 NW of them) against activation rows
+// n0 .. n0 + 32 FNT - 1 (nvalid of them valid), over all of K (or split's run
+// of it).  FNT = 8 (256 activation rows) everywhere; the expert products take
+// FNT = 2 (64 rows) for a tile of 64 tokens or fewer, the remainder of an
+// expert's tokens, whose matrix work would otherwise be mostly empty.
+template <int MODE, int NW, int FNT>
+__device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int nvalid, int e,
+                                         int split, _Float16 *sX0, _Float16 *sX1)
 {
-    constexpr int BM = 32 * NW; // weight rows per tile (gate/up: gate + up rows)
-    constexpr int NQ = 32 / NW; // 1 KB activation copies per wave per step
+    constexpr int FN = FNT;
+    constexpr int BM = 32 * NW;            // weight rows per tile (gate/up: gate + up rows)
+    constexpr int NQ = 4 * FN / NW;        // 1 KB activation copies per wave per step
+    constexpr int VPM = FN >= 8 ? 3 : 24 / FN; // dequant instructions placed after each matrix instruction
+    static_assert(NQ >= 1, "each wave copies at least 1 KB per step");
     const int M = p.M, K = p.K;
-    __shared__ __attribute__((aligned(16))) _Float16 sX0[BN * KS];
-    __shared__ __attribute__((aligned(16))) _Float16 sX1[BN * KS];
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
     const int r = lane & 31, h = lane >> 5;
-    int m0, n0, nvalid, e = 0, split = 0;
-    if constexpr (MODE == kBigDense || MODE == kBigSplit) {
-        // XCD-aware tile order: the hardware deals consecutive workgroups to
-        // the 8 XCDs in turn; give XCD x the contiguous tile run
-        // [x*T/8, (x+1)*T/8) (split products: units split-major, so an XCD's
-        // run shares its splits' activation panels).
-        const int b = blockIdx.x;
-        const int units = p.tiles_total * (MODE == kBigSplit ? p.splits : 1);
-        const int per = (units + 7) / 8;
-        int tile = (b % 8) * per + b / 8;
-        if (tile >= units)
-            return;
-        if constexpr (MODE == kBigSplit) {
-            split = tile / p.tiles_total;
-            tile -= split * p.tiles_total;
-        }
-        const int n_t = tile / p.tiles_m, m_t = tile % p.tiles_m;
-        m0 = m_t * BM;
-        n0 = n_t * BN;
-        nvalid = p.N - n0 < BN ? p.N - n0 : BN;
-    } else {
-        const int t = blockIdx.y;
-        if (t >= p.offsets[p.E + 1])
-            return;
-        e = p.tiles[t];
-        n0 = p.tiles[p.max_tiles + t]; // first sorted position of the tile
-        const int end = p.offsets[e + 1];
-        nvalid = end - n0 < BN ? end - n0 : BN;
-        m0 = (int)blockIdx.x * (MODE == kBigGateUp ? BM / 2 : BM);
-    }
-
     const int nsb = K >> 8;
     const size_t rowb = (size_t)nsb * kQ4kBytes;
     // split products: this workgroup's run of K starts at super-block sb0
@@ -335,7 +310,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
         for (int u = 0; u < 4 * FN; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
         }
         // this wave's copies for the next step have landed (the two weight
         // loads stay in flight); after the barrier every wave's have
@@ -430,6 +405,50 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
                 }
             }
         }
+    }
+}
+
+template <int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams p)
+{
+    constexpr int BM = 32 * NW; // weight rows per tile (gate/up: gate + up rows)
+    __shared__ __attribute__((aligned(16))) _Float16 sX0[BN * KS];
+    __shared__ __attribute__((aligned(16))) _Float16 sX1[BN * KS];
+    int m0, n0, nvalid, e = 0, split = 0;
+    if constexpr (MODE == kBigDense || MODE == kBigSplit) {
+        // XCD-aware tile order: the hardware deals consecutive workgroups to
+        // the 8 XCDs in turn; give XCD x the contiguous tile run
+        // [x*T/8, (x+1)*T/8) (split products: units split-major, so an XCD's
+        // run shares its splits' activation panels).
+        const int b = blockIdx.x;
+        const int units = p.tiles_total * (MODE == kBigSplit ? p.splits : 1);
+        const int per = (units + 7) / 8;
+        int tile = (b % 8) * per + b / 8;
+        if (tile >= units)
+            return;
+        if constexpr (MODE == kBigSplit) {
+            split = tile / p.tiles_total;
+            tile -= split * p.tiles_total;
+        }
+        const int n_t = tile / p.tiles_m, m_t = tile % p.tiles_m;
+        m0 = m_t * BM;
+        n0 = n_t * BN;
+        nvalid = p.N - n0 < BN ? p.N - n0 : BN;
+        big_tile<MODE, NW, FN>(p, m0, n0, nvalid, e, split, sX0, sX1);
+    } else {
+        const int t = blockIdx.y;
+        if (t >= p.offsets[p.E + 1])
+            return;
+        e = p.tiles[t];
+        n0 = p.tiles[p.max_tiles + t]; // first sorted position of the tile
+        const int end = p.offsets[e + 1];
+        nvalid = end - n0 < BN ? end - n0 : BN;
+        m0 = (int)blockIdx.x * (MODE == kBigGateUp ? BM / 2 : BM);
+        // the same for the whole workgroup
+        if (__builtin_amdgcn_readfirstlane(nvalid) <= 64)
+            big_tile<MODE, NW, 2>(p, m0, n0, nvalid, e, split, sX0, sX1);
+        else
+            big_tile<MODE, NW, FN>(p, m0, n0, nvalid, e, split, sX0, sX1);
     }
 }
 
