@@ -8,15 +8,16 @@
 // the factored form of a Q4_K super-block,
 //     sum over sub-blocks j of  (d*sc_j) * sum_k q_k x_k  -  (dmin*m_j) * sum_k x_k,
 // with both sums exact or binary32-accurate:
-//   * sum_k q_k x_k runs on v_mfma_f32_16x16x32_f16, one sub-block (32
-//     weights) per instruction: the 4-bit quant enters as the binary16
-//     subnormal q*2^-24 (exact; high nibbles as 16q*2^-24) and the activation
-//     as two binary16 halves hi + lo of x * 2^e, where 2^e (per activation row
-//     and super-block) brings the largest |x| of the slice to [2^14, 2^15);
-//     the products are exact and the sums binary32, every value at least
-//     2^-17 of that maximum keeps 22 significant bits and every value at
-//     least 2^-20 of it a relative error below 2^-19;
-//   * (d*sc_j) * D_j is applied in binary32 per sub-block, 2^-e per super-block;
+//   * sum_j sc_j * sum_k q_k x_k runs on v_mfma_f32_16x16x32_f16, one
+//     sub-block (32 weights) per instruction and one accumulator over the
+//     super-block: the quant times its sub-block's 6-bit scale (at most 945)
+//     enters as the binary16 subnormal (sc*q)*2^-24 (exact) and the
+//     activation as two binary16 halves hi + lo of x * 2^e, where 2^e (per
+//     activation row and super-block) brings the largest |x| of the slice to
+//     [2^14, 2^15); the products are exact and the sums binary32, every value
+//     at least 2^-17 of that maximum keeps 22 significant bits and every value
+//     at least 2^-20 of it a relative error below 2^-19;
+//   * d * 2^-e is applied in binary32 once per super-block;
 //   * sum_j (dmin*m_j) * sum_k x_k is a 16 x 16 x 8 product per super-block on
 //     v_mfma_f32_16x16x4f32 from the binary32 sub-block sums of x.
 // A sub-block of an activation row holding a non-zero |x| below 2^-20 of the
@@ -46,6 +47,7 @@ namespace {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int RB = 128; // rows per block
 constexpr int NT = 256; // threads per workgroup
@@ -293,27 +295,30 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
 
         // one super-block from LDS buffer buf and packed weights wt
         auto compute = [&](int buf, const WTile(&wt)[2]) {
-            float4_t ch[2];
+            // the 6-bit scale of each sub-block is folded into the quant
+            // operand: sc*q <= 945 < 1024 is the binary16 subnormal
+            // (sc*q)*2^-24 exactly, so one accumulator per tile runs over all
+            // eight sub-blocks and d*2^24 is applied once per super-block
+            float4_t dacc[2];
             float mb[2][2]; // dmin*m_j for j = quarter and 4 + quarter, per tile
-            float sl[2][8]; // d*sc_j * 2^24 (even j) or 2^20 (odd j), per tile
+            float d24[2];
+            uint32_t scp[2][8]; // sc_j in both 16-bit halves
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                ch[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+                dacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
                 const uint4 h = wt[t].h;
-                const float d = half_to_float(h.x), dmin = half_to_float(h.x >> 16);
-                const float d24 = d * 16777216.f, d20 = d * 1048576.f;
+                const float dmin = half_to_float(h.x >> 16);
+                d24[t] = half_to_float(h.x) * 16777216.f;
                 const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
                 const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
                 const uint32_t m03 = h.z & 0x3F3F3F3Fu;
                 const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-                sl[t][0] = ubyte_to_float<0>(sc03) * d24;
-                sl[t][1] = ubyte_to_float<1>(sc03) * d20;
-                sl[t][2] = ubyte_to_float<2>(sc03) * d24;
-                sl[t][3] = ubyte_to_float<3>(sc03) * d20;
-                sl[t][4] = ubyte_to_float<0>(sc47) * d24;
-                sl[t][5] = ubyte_to_float<1>(sc47) * d20;
-                sl[t][6] = ubyte_to_float<2>(sc47) * d24;
-                sl[t][7] = ubyte_to_float<3>(sc47) * d20;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // byte j into bytes 0 and 2, zeros above
+                    scp[t][j] = __builtin_amdgcn_perm(0u, sc03, 0x0C000C00u | (j << 16) | j);
+                    scp[t][4 + j] = __builtin_amdgcn_perm(0u, sc47, 0x0C000C00u | (j << 16) | j);
+                }
                 mb[t][0] = dmin * (float)__builtin_amdgcn_ubfe(m03, 8 * quarter, 8);
                 mb[t][1] = dmin * (float)__builtin_amdgcn_ubfe(m47, 8 * quarter, 8);
             }
@@ -328,14 +333,20 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                     const half8_t al = __builtin_bit_cast(half8_t, xl);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        const uint32_t D0 = wt[t].q[g].x, D1 = wt[t].q[g].y;
-                        const uint32_t mk = hh ? 0x00F000F0u : 0x000F000Fu;
-                        // (k0,k2), (k1,k3), (k4,k6), (k5,k7) of this lane's 8
-                        const uint4 qv = make_uint4(D0 & mk, (D0 >> 8) & mk, D1 & mk, (D1 >> 8) & mk);
+                        // low nibbles (hh = 0) or high nibbles (hh = 1) of this
+                        // lane's 8 quant bytes, as 16-bit lanes:
+                        // (k0,k2), (k1,k3), (k4,k6), (k5,k7), times sc_j
+                        const uint32_t D0 = hh ? wt[t].q[g].x >> 4 : wt[t].q[g].x;
+                        const uint32_t D1 = hh ? wt[t].q[g].y >> 4 : wt[t].q[g].y;
+                        const uint32_t mk = 0x000F000Fu;
+                        const u16x2 sv = __builtin_bit_cast(u16x2, scp[t][j]);
+                        auto scq = [&](uint32_t v) {
+                            return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v & mk) * sv);
+                        };
+                        const uint4 qv = make_uint4(scq(D0), scq(D0 >> 8), scq(D1), scq(D1 >> 8));
                         const half8_t bq = __builtin_bit_cast(half8_t, qv);
-                        float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, D, 0, 0, 0);
-                        ch[t] = sl[t][j] * D + ch[t];
+                        dacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, dacc[t], 0, 0, 0);
+                        dacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, dacc[t], 0, 0, 0);
                     }
                 }
                 // bound the live ranges: one group's operands at a time
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             const float sx0 = sm.sx[buf][quarter][col], sx1 = sm.sx[buf][4 + quarter][col];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                acc[t] = iv * ch[t] + acc[t];
+                acc[t] = (d24[t] * iv) * dacc[t] + acc[t];
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx0, mb[t][0], macc[t], 0, 0, 0);
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx1, mb[t][1], macc[t], 0, 0, 0);
             }
