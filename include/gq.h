@@ -194,6 +194,20 @@ gq_status gq_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M,
 gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                             int64_t N, int64_t tile_rows, void *stream);
 
+/* gq_gemm_q4k on tiles of 256/groups weight rows by 128 activation rows whose
+ * K reduction is split across `groups` groups of waves inside each workgroup
+ * (groups = 2 or 4), for products whose large tiles are too few to fill the
+ * device (prefill with few tokens and a long K) when no workspace is at hand:
+ * group g sums the g-th of `groups` equal runs of K in binary32, the runs'
+ * sums are added in run order inside the workgroup (deterministic) and
+ * rounded once to binary16.  Same arguments, result and bound as
+ * gq_gemm_q4k; the summation order differs, so results agree to binary32
+ * rounding, not bit for bit.  Nothing is allocated.  Errors: GQ_EINVAL for
+ * other groups; GQ_ESHAPE when groups does not divide K/256 or
+ * N*K*2 >= 2^31. */
+gq_status gq_gemm_q4k_kgroups(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                              int64_t N, int64_t groups, void *stream);
+
 /* gq_gemm_q4k with K cut into `splits` equal runs of whole super-blocks, for
  * products whose 256 x 256 tiles are too few to fill the device (prefill with
  * few tokens and a long K): each run's product goes to the caller workspace

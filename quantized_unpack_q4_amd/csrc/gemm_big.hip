@@ -26,7 +26,7 @@
 //   * the activation slice (256 rows x 64 halves) is copied global -> LDS by
 //     direct-to-LDS loads one step ahead, shared by all waves;
 //   * the packed weights (16-byte header + 16 quant bytes per lane) are
-//     loaded into registers two steps ahead and dequantized one step ahead:
+//     loaded into registers three steps ahead and dequantized one step ahead:
 //     w16 = binary16(binary32(d*sc*q - dmin*m)), one mixed-precision FMA per
 //     weight (the quant enters as the binary16 subnormal q*2^-24, exactly)
 //     and one packed round-to-nearest conversion per two weights;
@@ -103,10 +103,9 @@ constexpr int KS = 64;  // weights per K step
 constexpr int BN = 256; // activation rows per tile
 constexpr int FN = BN / 32;
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
-// 6:4, lgkmcnt in 11:8): vmcnt <= vm with lgkmcnt == 0 or left free.
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8): vmcnt <= vm and lgkmcnt == 0.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
-constexpr int waitcnt_vm(int vm) { return waitcnt_vm_lgkm0(vm) | (15 << 8); }
 
 enum { kBigDense = 0, kBigGateUp = 1, kBigDown = 2, kBigSplit = 3 };
 
@@ -136,29 +135,43 @@ struct BigParams {
 // assignment list; h = binary16(silu(g) * u) is written.  MODE kBigDown:
 // 32 NW rows of an expert's down matrix against its rows of h, binary32
 // outputs.
-// One tile: weight rows from m0 (BM = 32 NW of them) against activation rows
-// n0 .. n0 + 32 FNT - 1 (nvalid of them valid), over all of K (or split's run
-// of it).  FNT = 8 (256 activation rows) everywhere; the expert products take
-// FNT = 2 (64 rows) for a tile of 64 tokens or fewer, the remainder of an
-// expert's tokens, whose matrix work would otherwise be mostly empty.
-template <int MODE, int NW, int FNT>
+// One tile: weight rows from m0 (BM = 32 NW / KG of them) against activation
+// rows n0 .. n0 + 32 FNT - 1 (nvalid of them valid), over all of K (or split's
+// run of it).  FNT = 8 (256 activation rows) for the full tiles; the expert
+// products take FNT = 2 (64 rows) for a tile of 64 tokens or fewer, the
+// remainder of an expert's tokens, whose matrix work would otherwise be mostly
+// empty.
+// KG > 1 (dense product only): the NW waves form KG groups of NW / KG; group g
+// runs the whole tile over the g-th of KG equal runs of K with its own LDS
+// buffers (KG (32 FNT x 64)-half slices per buffer), and at the end groups
+// 1 .. KG-1 hand their binary32 partial tiles to group 0 through LDS, which
+// adds them in group order (deterministic) and stores the tile.  The groups
+// step in lockstep (same number of steps, one barrier per step for all).
+template <int MODE, int NW, int FNT, int KG = 1>
 __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int nvalid, int e,
                                          int split, _Float16 *sX0, _Float16 *sX1)
 {
     constexpr int FN = FNT;
-    constexpr int BM = 32 * NW;            // weight rows per tile (gate/up: gate + up rows)
-    constexpr int NQ = 4 * FN / NW;        // 1 KB activation copies per wave per step
+    constexpr int NWG = NW / KG;           // waves per K group
+    constexpr int BM = 32 * NWG;           // weight rows per tile (gate/up: gate + up rows)
+    constexpr int NQ = 4 * FN / NWG;       // 1 KB activation copies per wave per step
+    constexpr int GX = 32 * FN * KS;       // halves of one group's slice of an LDS buffer
     constexpr int VPM = FN >= 8 ? 3 : 24 / FN; // dequant instructions placed after each matrix instruction
     static_assert(NQ >= 1, "each wave copies at least 1 KB per step");
+    static_assert(KG == 1 || MODE == kBigDense, "K groups: dense product only");
+    static_assert(NW % KG == 0, "whole waves per K group");
     const int M = p.M, K = p.K;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
+    const int wall = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
+    const int kg = wall / NWG;   // K group
+    const int wave = wall % NWG; // wave within its K group
     const int r = lane & 31, h = lane >> 5;
     const int nsb = K >> 8;
     const size_t rowb = (size_t)nsb * kQ4kBytes;
-    // split products: this workgroup's run of K starts at super-block sb0
-    const int krun = MODE == kBigSplit ? K / p.splits : K;
-    const int sb0 = MODE == kBigSplit ? split * (krun >> 8) : 0;
+    // split products: this workgroup's run of K starts at super-block sb0;
+    // K groups: this group's run
+    const int krun = MODE == kBigSplit ? K / p.splits : K / KG;
+    const int sb0 = MODE == kBigSplit ? split * (krun >> 8) : kg * (krun >> 8);
     const int nk = krun / KS;
 
     // this lane's weight row
@@ -191,8 +204,9 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
     }
     const uint32_t lds0 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)sX0;
     const uint32_t lds1 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)sX1;
-    const uint32_t mb0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * (1024u * NQ));
-    const uint32_t mb1 = __builtin_amdgcn_readfirstlane(lds1 + (uint32_t)wave * (1024u * NQ));
+    const uint32_t gofs = (uint32_t)kg * (2u * GX); // this group's slice, bytes
+    const uint32_t mb0 = __builtin_amdgcn_readfirstlane(lds0 + gofs + (uint32_t)wave * (1024u * NQ));
+    const uint32_t mb1 = __builtin_amdgcn_readfirstlane(lds1 + gofs + (uint32_t)wave * (1024u * NQ));
     const uint16_t *x = p.x + (size_t)sb0 * 256;
     auto issue_x = [&](int kt, int buf) {
         const uint16_t *xk = x + (size_t)kt * KS; // wave-uniform
@@ -201,12 +215,15 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
             load_lds16(xk, xoff[q], (buf ? mb1 : mb0) + 1024u * q);
     };
 
-    // packed weights of the two steps ahead: slot = step & 1.  Quant groups
-    // 0 and 1 need only the first 12 header bytes (d, dmin and scale/min bytes
-    // 0-7); loading 16 would leave the fourth register of the load dead, and
-    // the compiler may then reuse it while the load is in flight, which costs
-    // a wait for every load issued before it (the activation copies included).
-    uint4 rh[2], rq[2];
+    // packed weights of the steps ahead: slot = step & 3; step kt + 3 is
+    // loaded during step kt and has until the end of step kt + 1 to land (the
+    // wait that ends each step leaves only the newest step's two loads in
+    // flight).  Quant groups 0 and 1 need only the first 12 header bytes (d,
+    // dmin and scale/min bytes 0-7); loading 16 would leave the fourth
+    // register of the load dead, and the compiler may then reuse it while the
+    // load is in flight, which costs a wait for every load issued before it
+    // (the activation copies included).
+    uint4 rh[4], rq[4];
     auto issue_w = [&](int kt, int slot, int g) {
         const uint8_t *blk = wrow + (size_t)(kt >> 2) * kQ4kBytes;
         if (g < 2) {
@@ -268,7 +285,7 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
     half8_t bf0[FN], bf1[FN];
     auto read_b = [&](int buf, int s, half8_t(&bf)[FN]) {
         const int c = 2 * h + (s & 1) + 4 * (s >> 1);
-        const _Float16 *X = buf ? sX1 : sX0;
+        const _Float16 *X = (buf ? sX1 : sX0) + kg * GX;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int row = 32 * j + r;
@@ -283,20 +300,21 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
 
     // One K step kt with S = kt % 4: the activations of step kt are in LDS
     // buffer S & 1, its A operands in `cur` (dequantized during step kt-1),
-    // the packed weights of step kt+1 in slot (S+1) & 1 (arrived), and step
-    // kt+2's weight loads go to slot S & 1.
+    // the packed weights of step kt+1 in slot (S+1) & 3 (arrived), those of
+    // step kt+2 in slot (S+2) & 3 (in flight), and step kt+3's weight loads go
+    // to slot (S+3) & 3.
     auto step = [&](int kt, int S, half8_t(&cur)[4], half8_t(&nxt)[4]) {
         const int buf = S & 1;
         const int n1 = kt + 1 < nk ? kt + 1 : nk - 1;
-        const int n2 = kt + 2 < nk ? kt + 2 : nk - 1;
+        const int n3 = kt + 3 < nk ? kt + 3 : nk - 1;
         read_b(buf, 0, bf0);
-        // copies first: the wait that ends the step then leaves exactly the
-        // two weight loads in flight
+        // copies first: the wait that ends the step then leaves exactly this
+        // step's two weight loads in flight
         issue_x(n1, buf ^ 1);
-        issue_w(n2, S & 1, (S + 2) & 3);
+        issue_w(n3, (S + 3) & 3, (S + 3) & 3);
         read_b(buf, 1, bf1);
         mfma(cur[0], bf0);
-        dequant((S + 1) & 1, (S + 1) & 3, nxt);
+        dequant((S + 1) & 3, (S + 1) & 3, nxt);
         read_b(buf, 2, bf0);
         mfma(cur[1], bf1);
         read_b(buf, 3, bf1);
@@ -312,23 +330,25 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
         }
-        // this wave's copies for the next step have landed (the two weight
-        // loads stay in flight); after the barrier every wave's have
+        // this wave's copies for the next step and the weights of step kt+2
+        // have landed (loads complete in issue order; the two loads of step
+        // kt+3 stay in flight); after the barrier every wave's copies have.
+        // The compiler counts only the weight loads, so by its count too the
+        // weights of step kt+2 are in and it inserts no wait of its own
+        // before their dequantization in the next step.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));
         __builtin_amdgcn_s_barrier();
-        // retire the weight loads here, where nothing else is in flight, so
-        // that no wait the compiler places for them falls on later copies
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __builtin_amdgcn_sched_barrier(0);
     };
 
     // prologue: step 0's activations in LDS, A operands of step 0, packed
-    // weights of step 1 in slot 1
+    // weights of step 1 in slot 1, step 2's on the way to slot 2
     half8_t a0[4], a1[4];
     issue_x(0, 0);
     issue_w(0, 0, 0);
     issue_w(1, 1, 1); // nk >= 4
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    issue_w(2, 2, 2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));
     dequant(0, 0, a0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -339,6 +359,41 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
         step(kt + 1, 1, a1, a0);
         step(kt + 2, 2, a0, a1);
         step(kt + 3, 3, a1, a0);
+    }
+
+    if constexpr (KG > 1) {
+        // every wave's LDS reads and copies ended before the last step's
+        // barrier; the partial tiles of groups 1.. go to [g-1][wave][j][v4]
+        // (a float4 per lane), group 0 adds them in group order
+        float4_t *red = reinterpret_cast<float4_t *>(sX0);
+        if (kg > 0) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4)
+                    red[(((kg - 1) * NWG + wave) * FN * 4 + 4 * j + v4) * 64 + lane] =
+                        float4_t{acc[j][4 * v4], acc[j][4 * v4 + 1], acc[j][4 * v4 + 2],
+                                 acc[j][4 * v4 + 3]};
+        }
+        __syncthreads();
+        if (kg > 0)
+            return;
+#pragma unroll
+        for (int g = 1; g < KG; ++g)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const float4_t v = red[(((g - 1) * NWG + wave) * FN * 4 + 4 * j + v4) * 64 + lane];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[j][4 * v4 + c] += v[c];
+                }
+                // the sums land here, before the next fragment's reads (the
+                // compiler would otherwise sink the additions into the stores
+                // and hold every read's registers until then: 256 VGPRs)
+                asm volatile("" : "+v"(acc[j])::"memory");
+            }
     }
 
     // epilogue: element v of fragment j is fragment row 8*(v/4) + 4*h + v%4
@@ -452,6 +507,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
     }
 }
 
+// The dense product on tiles of 256/KG weight rows x 128 activation rows, K
+// split across KG groups of waves inside the workgroup (see big_tile); tiles
+// in the same XCD-aware order as the dense kernel.
+template <int KG>
+__global__ __launch_bounds__(512, 1) void gemm_q4k_kgroups_kernel(BigParams p)
+{
+    constexpr int FNT = 4, BM = 256 / KG, BNT = 32 * FNT, GX = BNT * KS;
+    // two step buffers of KG group slices; after the last step the partial
+    // tiles of groups 1..KG-1 reuse the space
+    __shared__ __attribute__((aligned(16))) _Float16 sX[2 * KG * GX];
+    static_assert((KG - 1) * BM * BNT * 4 <= (int)sizeof(sX), "partial tiles fit the step buffers");
+    const int b = blockIdx.x;
+    const int per = (p.tiles_total + 7) / 8;
+    const int tile = (b % 8) * per + b / 8;
+    if (tile >= p.tiles_total)
+        return;
+    const int n_t = tile / p.tiles_m, m_t = tile % p.tiles_m;
+    const int m0 = m_t * BM, n0 = n_t * BNT;
+    const int nvalid = p.N - n0 < BNT ? p.N - n0 : BNT;
+    big_tile<kBigDense, 8, FNT, KG>(p, m0, n0, nvalid, 0, 0, sX, sX + KG * GX);
+}
+
 // Y[n][m] = binary16(sum over s = 0..splits-1 of part[s][n][m]), summed in
 // binary32 in split order (deterministic), one rounding to binary16.
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float *__restrict__ part,
@@ -520,6 +597,58 @@ hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_
         hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 8>), dim3((unsigned)grid), dim3(512), 0, s, p);
     else
         hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 4>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+int gemm_kgroups_choice(int64_t M, int64_t K, int64_t N)
+{
+    // Only where the 256 x 256 tiles do not fill the device.  Estimated time:
+    // rounds of tiles on the device (one workgroup per CU at a time) times
+    // the time of one such round per 1024 of K, measured on 4096 x 14336 and
+    // 4096/6144/14336 x 4096 products with 128-1024 activation rows:
+    // 128 x 256 tiles (two per CU) 18 us, K groups of 2 (128 x 128 tiles)
+    // 10 us, K groups of 4 (64 x 128 tiles) 6.6 us.  The 128 x 256 tiles
+    // count when the large-tile choice would take them; the small-tile
+    // kernels otherwise, which the K groups beat wherever they apply.
+    if (M < 1 || N < 1 || K < 256 || K % 256 != 0 || !gemm_big_fits(M, K, N))
+        return 0;
+    const int big = gemm_big_choice(M, K, N);
+    if (big == 256)
+        return 0;
+    const int64_t cus = device_cus();
+    auto rounds = [&](int64_t tiles) { return (double)((tiles + cus - 1) / cus); };
+    const int64_t nsb = K / 256;
+    const double inf = 1e300;
+    const double t128 = big == 128 ? rounds(dense_tiles(M, N, 128)) * 18.0 : inf;
+    const double kg2 = nsb % 2 == 0 ? rounds(((M + 127) / 128) * ((N + 127) / 128)) * 10.0 : inf;
+    const double kg4 = nsb % 4 == 0 ? rounds(((M + 63) / 64) * ((N + 127) / 128)) * 6.6 : inf;
+    if (kg4 < inf && kg4 <= kg2 && kg4 < t128)
+        return 4;
+    if (kg2 < inf && kg2 < t128)
+        return 2;
+    return 0;
+}
+
+hipError_t launch_gemm_kgroups(const void *w, const uint16_t *x, uint16_t *y, int64_t M,
+                               int64_t K, int64_t N, int kg, hipStream_t s)
+{
+    if ((kg != 2 && kg != 4) || (K / 256) % kg != 0 || !gemm_big_fits(M, K, N))
+        return hipErrorInvalidValue;
+    const int bm = 256 / kg;
+    BigParams p{};
+    p.w = (const uint8_t *)w;
+    p.x = x;
+    p.y = y;
+    p.M = (int)M;
+    p.K = (int)K;
+    p.N = (int)N;
+    p.tiles_m = (int)((M + bm - 1) / bm);
+    p.tiles_total = (int)(p.tiles_m * ((N + 127) / 128));
+    const int grid = (p.tiles_total + 7) / 8 * 8;
+    if (kg == 4)
+        hipLaunchKernelGGL((gemm_q4k_kgroups_kernel<4>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_q4k_kgroups_kernel<2>), dim3((unsigned)grid), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 

@@ -313,8 +313,14 @@ static gq_status gemm_common(const char *fn, const void *w, const uint16_t *x, u
     GQ_TRY(check_ptr(fn, "w", w));
     GQ_TRY(check_ptr(fn, "x", x));
     GQ_TRY(check_ptr(fn, "y", y));
-    if (tile_rows == 0)
+    if (tile_rows == 0) {
+        // too few 256 x 256 tiles for the device: K groups where they are
+        // estimated fastest
+        const int kg = gq::gemm_kgroups_choice(M, K, N);
+        if (kg)
+            return launched(fn, gq::launch_gemm_kgroups(w, x, y, M, K, N, kg, (hipStream_t)stream));
         tile_rows = gq::gemm_big_choice(M, K, N);
+    }
     if (tile_rows == 0 || tile_rows == 64)
         return launched(fn, gq::launch_gemm_q4k(w, x, y, M, K, N, (hipStream_t)stream));
     if (!gq::gemm_big_fits(M, K, N))
@@ -355,6 +361,30 @@ gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64
         return fail(GQ_EINVAL, "%s: tile_rows = %lld must be 0, 64, 128 or 256", fn,
                     (long long)tile_rows);
     return gemm_common(fn, w, x, y, M, K, N, tile_rows, stream);
+}
+
+gq_status gq_gemm_q4k_kgroups(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                              int64_t N, int64_t groups, void *stream)
+{
+    static const char fn[] = "gq_gemm_q4k_kgroups";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    GQ_TRY(check_dim(fn, "N", N, true));
+    if (groups != 2 && groups != 4)
+        return fail(GQ_EINVAL, "%s: groups = %lld must be 2 or 4", fn, (long long)groups);
+    if ((K / 256) % groups != 0)
+        return fail(GQ_ESHAPE, "%s: groups = %lld does not divide the %lld super-blocks of K", fn,
+                    (long long)groups, (long long)(K / 256));
+    if (N > ((int64_t)1 << 21) || !gq::gemm_big_fits(M > 0 ? M : 1, K, N > 0 ? N : 1))
+        return fail(GQ_ESHAPE, "%s: N*K = %lld is too large for the large tiles", fn,
+                    (long long)(N * K));
+    if (M == 0 || N == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w", w));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "y", y));
+    return launched(fn, gq::launch_gemm_kgroups(w, x, y, M, K, N, (int)groups,
+                                                (hipStream_t)stream));
 }
 
 // Split count of the split-K product: `splits` as given, or the automatic choice.

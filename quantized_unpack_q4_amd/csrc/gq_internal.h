@@ -75,13 +75,23 @@ hipError_t launch_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64
                             int64_t N, hipStream_t s);
 // Large-tile matrix product (prefill): tiles of bm = 256 or 128 weight rows by
 // 256 activation rows.  gemm_big_fits: the shape fits the kernel's 32-bit
-// activation offsets.  gemm_big_choice: the tile height the automatic
-// dispatch uses (256 when there are 256 such tiles or more, else 128 when
-// there are 192 or more), 0 for the small-tile kernels.
+// activation offsets.  gemm_big_choice: the tile height of the large-tile
+// kernel for a shape (256 when there are 256 such tiles or more, else 128
+// when there are 192 or more), 0 for the small-tile kernels; the automatic
+// dispatch takes it where gemm_kgroups_choice returns 0.
 bool gemm_big_fits(int64_t M, int64_t K, int64_t N);
 int gemm_big_choice(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, int bm, hipStream_t s);
+// Large-tile product with K split across kg (2 or 4) groups of waves inside
+// each workgroup: tiles of 256/kg weight rows x 128 activation rows, one
+// workgroup per CU, no workspace; requires (K/256) % kg == 0 and
+// gemm_big_fits.  gemm_kgroups_choice: the group count the automatic dispatch
+// uses for a shape (0: another family), from an estimate of each family's
+// rounds of tiles on the device.
+int gemm_kgroups_choice(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_kgroups(const void *w, const uint16_t *x, uint16_t *y, int64_t M,
+                               int64_t K, int64_t N, int kg, hipStream_t s);
 // Split-K form of the 256 x 256 large-tile product: `splits` runs of K/splits
 // (whole super-blocks) into binary32 partials ws [splits][N][M], then a fixed
 // order sum rounded to binary16.  gemm_splitk_choice: the split count that

@@ -91,6 +91,11 @@ int main()
     LAUNCHED(gq_gemm_q8_0(p, x16, y16, 256, 1024, 512, nullptr));
     LAUNCHED(gq_gemm_q4k_tiles(p, x16, y16, 256, 1024, 512, 128, nullptr));
     REFUSED(gq_gemm_q4k_tiles(p, x16, y16, 256, 1024, 512, 100, nullptr), GQ_EINVAL);
+    LAUNCHED(gq_gemm_q4k(p, x16, y16, 256, 1024, 128, nullptr)); // the K-group path
+    LAUNCHED(gq_gemm_q4k_kgroups(p, x16, y16, 256, 1024, 512, 4, nullptr));
+    LAUNCHED(gq_gemm_q4k_kgroups(p, x16, y16, 256, 512, 512, 2, nullptr));
+    REFUSED(gq_gemm_q4k_kgroups(p, x16, y16, 256, 512, 512, 4, nullptr), GQ_ESHAPE);
+    REFUSED(gq_gemm_q4k_kgroups(p, x16, y16, 256, 1024, 512, 3, nullptr), GQ_EINVAL);
     REFUSED(gq_gemm_q8_0(p, x16, y16, 256, 96, 512, nullptr), GQ_ESHAPE);
     const size_t wsb = gq_gemm_q4k_splitk_workspace_bytes(4096, 14336, 512, 8);
     CHECK(wsb == (size_t)8 * 512 * 4096 * 4);

@@ -79,6 +79,16 @@ def test_gemm_refusals(L):
     s, m = status_and_msg(L, st)
     assert s == "GQ_ESHAPE" and "128-row" in m
     assert g(None, None, None, 64, 256, 0, 256, None) == 0
+    k = L.gq_gemm_q4k_kgroups
+    assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 1024, 8, 3, None))[0] == "GQ_EINVAL"
+    assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 1024, 8, 0, None))[0] == "GQ_EINVAL"
+    # 3 and 2 super-blocks: not divisible by the groups
+    assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 768, 8, 2, None))[0] == "GQ_ESHAPE"
+    assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 512, 8, 4, None))[0] == "GQ_ESHAPE"
+    assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 300, 8, 2, None))[0] == "GQ_ESHAPE"
+    assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 1 << 20, 1 << 10, 4, None))[0] == "GQ_ESHAPE"
+    assert status_and_msg(L, k(FAKE, FAKE, MISALIGNED, 64, 1024, 8, 2, None))[0] == "GQ_EALIGN"
+    assert k(None, None, None, 64, 1024, 0, 4, None) == 0
 
 
 def test_moe_workspace_and_refusals(L):

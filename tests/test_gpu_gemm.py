@@ -191,6 +191,76 @@ def test_gemm_deterministic(N):
     assert np.array_equal(a, b)
 
 
+def _gemm_kg(w_d, x16, M, K, groups):
+    torch = torch_cuda()
+    N = x16.shape[0]
+    y = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    y.fill_(float("nan"))
+    gq.gq_gemm_q4k_kgroups(w_d, dev(x16), y, M, K, N, groups)
+    return half_bits(y).view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("groups", [2, 4])
+@pytest.mark.parametrize("M,K,N", [(200, 1024, 300), (1000, 2048, 260), (1, 1024, 5),
+                                   (130, 4096, 37), (640, 1024, 1030)])
+def test_gemm_kgroups_parity(M, K, N, groups):
+    """K split across groups of waves inside each workgroup, at sizes the
+    oracle computes in full: ragged weight rows (tiles of 64 or 128) and
+    activation rows (tiles of 128), a single weight row, runs of K of one
+    super-block per group (K = 1024 with four groups).  The output starts as
+    NaN, so every element must be written."""
+    say("gemm kgroups", groups, M, K, N)
+    w = synth.q4k_blocks(99, M, M, K)
+    x16 = synth.activations_f16(99, N, N, K)
+    y = _gemm_kg(dev(w), x16, M, K, groups)
+    yr, S = oracle.gemm(oracle.Q4_K, w, x16, M, K)
+    r = within(y, yr, S, TOL, "gemm kgroups %d %dx%dx%d" % (groups, M, K, N))
+    say("  max err/S", r)
+
+
+@pytest.mark.parametrize("M,K,N,groups", [(4096, 14336, 512, 4), (4096, 14336, 1024, 2),
+                                          (6144, 4096, 512, 2), (4096, 4096, 512, 4)])
+def test_gemm_kgroups_prefill_sampled(M, K, N, groups):
+    """Few-token prefill shapes at full size, where the automatic dispatch
+    takes the K groups: gq_gemm_q4k equals the pinned group count bit for bit
+    (the same kernel), and 512 rows over all tokens and all rows over 16
+    tokens match the oracle."""
+    say("gemm kgroups full", groups, M, K, N)
+    g = np.random.default_rng(100)
+    w = synth.q4k_blocks(3, M, M, K)
+    x16 = synth.activations_f16(3, N, N, K)
+    wd = dev(w)
+    y = _gemm_kg(wd, x16, M, K, groups)
+    assert np.array_equal(_gemm(wd, x16, M, K), y)
+    r1, r2 = check_prefill_sample(y, w, x16, M, K, N, g)
+    say("  max err/S", r1, r2)
+
+
+@pytest.mark.parametrize("groups", [2, 4])
+def test_gemm_kgroups_one_hot_exact(groups):
+    """One-hot activation rows read out the binary16 weights exactly with K
+    split in groups: the group whose run holds the one-hot k sums the weight
+    exactly and the others add exact zeros.  The k of row i walks every
+    position of a 64-weight step and every group's run."""
+    M, K, N = 300, 1024, 270
+    w = synth.q4k_blocks(101, 0, M, K)
+    _, w16 = oracle.dequant(oracle.Q4_K, w, M, K)
+    ks = (np.arange(N) * 37 + 5) % K
+    x16 = np.zeros((N, K), np.float16)
+    x16[np.arange(N), ks] = 1.0
+    y = _gemm_kg(dev(w), x16, M, K, groups)
+    for i, k in enumerate(ks):
+        assert np.array_equal(y[i].astype(np.float16).view(np.uint16), w16[:, k]), (i, k)
+
+
+@pytest.mark.parametrize("groups", [2, 4])
+def test_gemm_kgroups_deterministic(groups):
+    M, K, N = 384, 2048, 300
+    w = dev(synth.q4k_blocks(102, 0, M, K))
+    x16 = synth.activations_f16(102, 0, N, K)
+    assert np.array_equal(_gemm_kg(w, x16, M, K, groups), _gemm_kg(w, x16, M, K, groups))
+
+
 def _gemm_splitk(w_d, x16, M, K, splits):
     torch = torch_cuda()
     N = x16.shape[0]
