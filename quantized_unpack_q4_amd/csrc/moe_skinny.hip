@@ -91,21 +91,25 @@ __device__ __forceinline__ uint32_t deq2(uint32_t qa, int sela, uint32_t qb, int
     return r;
 }
 
-// This lane's packed weights of one super-block: the header of its row and its
-// 8 quant bytes (k = 8q .. 8q+7 of each 32-byte group).
+// This lane's packed weights of one super-block: the header of its row and
+// the 32 bytes of quant group `quarter`, i.e. sub-blocks 2*quarter (low
+// nibbles) and 2*quarter + 1 (high nibbles).
 struct WSb {
-    uint4 h;
-    u32x2 q[4];
+    uint4 h, qa, qb;
 };
+
+__device__ __forceinline__ uint4 gload16(const uint8_t *p)
+{
+    const u32x4 v = *(g_u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ void load_wsb(const uint8_t *row, int sb, int quarter, WSb &w)
 {
     const uint8_t *blk = row + (size_t)sb * kQ4kBytes;
-    const u32x4 h = *(g_u32x4 *)blk;
-    w.h = make_uint4(h.x, h.y, h.z, h.w);
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-        w.q[g] = *(g_u32x2 *)(blk + 16 + 32 * g + 8 * quarter);
+    w.h = gload16(blk);
+    w.qa = gload16(blk + 16 + 32 * quarter);
+    w.qb = gload16(blk + 32 + 32 * quarter);
 }
 
 // Q8_0: this lane's two blocks (2*quarter, 2*quarter + 1) of one 256-weight
@@ -228,47 +232,45 @@ __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, 
         }
     };
 
+    // Q4_K: the 32 weights of matrix-core step (p, hh) in quarter q are
+    // positions 8p .. 8p+7 of sub-blocks 2q + hh (the lane's quant group q,
+    // low nibbles for hh = 0, high for hh = 1), paired with activation chunk
+    // 4(2q + hh) + p of the slice, so that a lane needs the scales of two
+    // sub-blocks only
     auto compute = [&](const _Float16 *buf, const WSb (&w)[NMAT]) {
-        float sl[NMAT][8], ol[NMAT][8];
+        float sl[NMAT], ol[NMAT], sh[NMAT], oh[NMAT];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
             const uint4 h = w[m].h;
             const float d = half_to_float(h.x), dmin = half_to_float(h.x >> 16);
             const float d24 = d * 16777216.f, d20 = d * 1048576.f;
-            const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
-            const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-            const uint32_t m03 = h.z & 0x3F3F3F3Fu;
-            const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-            sl[m][0] = ubyte_to_float<0>(sc03) * d24;
-            sl[m][1] = ubyte_to_float<1>(sc03) * d20;
-            sl[m][2] = ubyte_to_float<2>(sc03) * d24;
-            sl[m][3] = ubyte_to_float<3>(sc03) * d20;
-            sl[m][4] = ubyte_to_float<0>(sc47) * d24;
-            sl[m][5] = ubyte_to_float<1>(sc47) * d20;
-            sl[m][6] = ubyte_to_float<2>(sc47) * d24;
-            sl[m][7] = ubyte_to_float<3>(sc47) * d20;
-            ol[m][0] = -dmin * ubyte_to_float<0>(m03);
-            ol[m][1] = -dmin * ubyte_to_float<1>(m03);
-            ol[m][2] = -dmin * ubyte_to_float<2>(m03);
-            ol[m][3] = -dmin * ubyte_to_float<3>(m03);
-            ol[m][4] = -dmin * ubyte_to_float<0>(m47);
-            ol[m][5] = -dmin * ubyte_to_float<1>(m47);
-            ol[m][6] = -dmin * ubyte_to_float<2>(m47);
-            ol[m][7] = -dmin * ubyte_to_float<3>(m47);
+            // scale and min bytes of sub-blocks 0-3 (q < 2) or 4-7; sub-blocks
+            // 2q and 2q + 1 are bytes 2(q & 1) and 2(q & 1) + 1 of them
+            const uint32_t scw = quarter < 2 ? (h.y & 0x3F3F3F3Fu)
+                                             : ((h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u));
+            const uint32_t mnw = quarter < 2
+                                     ? (h.z & 0x3F3F3F3Fu)
+                                     : (((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u));
+            const uint32_t b0 = 16u * (uint32_t)(quarter & 1);
+            sl[m] = (float)__builtin_amdgcn_ubfe(scw, b0, 8) * d24;
+            sh[m] = (float)__builtin_amdgcn_ubfe(scw, b0 + 8, 8) * d20;
+            ol[m] = -dmin * (float)__builtin_amdgcn_ubfe(mnw, b0, 8);
+            oh[m] = -dmin * (float)__builtin_amdgcn_ubfe(mnw, b0 + 8, 8);
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            half8_t bop[NMAT][2]; // [matrix][sub-block 2g, 2g+1], k = 8q .. 8q+7 in order
+        for (int pp = 0; pp < 4; ++pp) {
+            half8_t bop[NMAT][2]; // [matrix][hh], positions 8pp .. 8pp+7 in order
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-                const uint32_t D0 = w[m].q[g].x, D1 = w[m].q[g].y;
+                const uint4 &qv = pp < 2 ? w[m].qa : w[m].qb;
+                const uint32_t D0 = (pp & 1) ? qv.z : qv.x, D1 = (pp & 1) ? qv.w : qv.y;
                 const uint32_t t0 = D0 >> 8, t1 = D1 >> 8;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const uint32_t mk = hh ? 0x00F000F0u : 0x000F000Fu;
                     const uint32_t a0 = D0 & mk, a1 = t0 & mk; // bytes (0,2), (1,3)
                     const uint32_t a2 = D1 & mk, a3 = t1 & mk; // bytes (4,6), (5,7)
-                    const float s = sl[m][2 * g + hh], o = ol[m][2 * g + hh];
+                    const float s = hh ? sh[m] : sl[m], o = hh ? oh[m] : ol[m];
                     const uint4 v = make_uint4(deq2(a0, 0, a1, 0, s, o), deq2(a0, 1, a1, 1, s, o),
                                                deq2(a2, 0, a3, 0, s, o), deq2(a2, 1, a3, 1, s, o));
                     bop[m][hh] = __builtin_bit_cast(half8_t, v);
@@ -276,7 +278,7 @@ __device__ __forceinline__ void run_chunk(const SkinnyParams &p, int e, int p0, 
             }
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const int c = 4 * (2 * g + hh) + quarter; // 16-byte chunk of the 512-byte slice
+                const int c = 4 * (2 * quarter + hh) + pp; // 16-byte chunk of the 512-byte slice
 #pragma unroll
                 for (int tg = 0; tg < NG; ++tg) {
                     const int t = 16 * tg + col;
