@@ -491,14 +491,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
         nvalid = p.N - n0 < BN ? p.N - n0 : BN;
         big_tile<MODE, NW, FN>(p, m0, n0, nvalid, e, split, sX0, sX1);
     } else {
-        const int t = blockIdx.y;
+        // XCD-aware order: the hardware deals consecutive workgroups to the 8
+        // XCDs in turn; XCD x takes token tiles x, x + 8, x + 16, ... each
+        // with all its row tiles, so that a token tile's activations are read
+        // into one XCD's L2 (gridDim.y is a multiple of 8, which makes the
+        // map one-to-one)
+        const int rt = (int)gridDim.x;
+        const int b = (int)blockIdx.x + rt * (int)blockIdx.y;
+        const int k = b >> 3;
+        const int t = 8 * (k / rt) + (b & 7);
         if (t >= p.offsets[p.E + 1])
             return;
         e = p.tiles[t];
         n0 = p.tiles[p.max_tiles + t]; // first sorted position of the tile
         const int end = p.offsets[e + 1];
         nvalid = end - n0 < BN ? end - n0 : BN;
-        m0 = (int)blockIdx.x * (MODE == kBigGateUp ? BM / 2 : BM);
+        m0 = (k % rt) * (MODE == kBigGateUp ? BM / 2 : BM);
         // the same for the whole workgroup
         if (__builtin_amdgcn_readfirstlane(nvalid) <= 64)
             big_tile<MODE, NW, 2>(p, m0, n0, nvalid, e, split, sX0, sX1);
@@ -782,8 +790,10 @@ hipError_t launch_moe_big(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.M = (int)a.I;
     p.K = (int)a.H;
     p.expert_bytes = a.I * (a.H / kQ4kWeights) * kQ4kBytes;
-    hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigGateUp, 8>),
-                       dim3((unsigned)(a.I / 128), (unsigned)max_tiles), dim3(512), 0, s, p);
+    // token tiles rounded up to a multiple of 8 for the XCD-aware order
+    const unsigned ty = (unsigned)((max_tiles + 7) / 8 * 8);
+    hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigGateUp, 8>), dim3((unsigned)(a.I / 128), ty),
+                       dim3(512), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -796,8 +806,8 @@ hipError_t launch_moe_big(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.M = (int)a.H;
     p.K = (int)a.I;
     p.expert_bytes = a.H * (a.I / kQ4kWeights) * kQ4kBytes;
-    hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDown, 8>),
-                       dim3((unsigned)(a.H / 256), (unsigned)max_tiles), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDown, 8>), dim3((unsigned)(a.H / 256), ty),
+                       dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
