@@ -142,10 +142,18 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
         for (int w = 0; w < kGroupWaves; ++w)
             cnt += wstart[w][tid];
     }
-    int total_valid = 0, total_tiles = 0;
+    int total_valid = 0, total_big = 0, total_small = 0;
     const int base = block_exclusive_scan(tid < E ? cnt : 0, nw, scratch, &total_valid);
     const int ntile = tid < E ? (cnt + BN - 1) / BN : 0;
-    const int tbase = block_exclusive_scan(ntile, nw, scratch, &total_tiles);
+    // tiles of 64 tokens or fewer (an expert's remainder when BN > 64) are
+    // the cheapest: they go after every other tile, so that they fill the
+    // last round of workgroups instead of leaving large tiles for it
+    const int rem = tid < E ? cnt % BN : 0;
+    const int nsmall = BN > 64 && rem > 0 && rem <= 64 ? 1 : 0;
+    const int nbig = ntile - nsmall;
+    const int tbase = block_exclusive_scan(nbig, nw, scratch, &total_big);
+    const int sbase = block_exclusive_scan(nsmall, nw, scratch, &total_small);
+    const int total_tiles = total_big + total_small;
     if (tid < E) {
         offsets[tid] = base;
         int run = base;
@@ -154,9 +162,13 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
             wstart[w][tid] = run;
             run += t;
         }
-        for (int i = 0; i < ntile; ++i) {
+        for (int i = 0; i < nbig; ++i) {
             tiles[tbase + i] = tid;
             tiles[max_tiles + tbase + i] = base + i * BN;
+        }
+        if (nsmall) {
+            tiles[total_big + sbase] = tid;
+            tiles[max_tiles + total_big + sbase] = base + nbig * BN;
         }
     }
     if (tid == 0) {
