@@ -559,6 +559,30 @@ def main():
         extra["gemv_swiglu_%dx%d_b1" % (M, K)] = {
             "fused_us": round(sf * 1e6, 2), "fused_GB/s": round(2 * q4k_bytes(M, K) / sf / 1e9, 1),
             "two_launches_us": round(ss * 1e6, 2)}
+        # the same at batch 4 and 16 on the matrix cores (gq_gemv_q4k_swiglu_batched)
+        for B in (4, 16):
+            xb = torch.from_numpy(synth.activations_f32(1, 2 * M + B, B, K)).cuda()
+            hb = torch.empty((B, M), dtype=torch.float32, device="cuda")
+            yb = torch.empty((2, B, M), dtype=torch.float32, device="cuda")
+            it["i"] = 0
+
+            def fused_b():
+                i = it["i"] % len(gates)
+                it["i"] += 1
+                gq.gq_gemv_q4k_swiglu_batched(gates[i], ups[i], xb, hb, M, K, B, stream)
+
+            def separate_b():
+                i = it["i"] % len(gates)
+                it["i"] += 1
+                gq.gq_gemv_q4k(gates[i], xb, yb[0], M, K, B, stream)
+                gq.gq_gemv_q4k(ups[i], xb, yb[1], M, K, B, stream)
+            sf = event_time(torch, stream, fused_b, reps=len(gates), warmup=len(gates))
+            ss = event_time(torch, stream, separate_b, reps=len(gates), warmup=len(gates))
+            extra["gemv_swiglu_%dx%d_b%d" % (M, K, B)] = {
+                "fused_us": round(sf * 1e6, 2),
+                "fused_GB/s": round(2 * q4k_bytes(M, K) / sf / 1e9, 1),
+                "two_launches_us": round(ss * 1e6, 2)}
+            del xb, hb, yb
         # the opt-in integer-dot path (8-bit activation codes) on the same
         # rotated gate matrices at batch 1 and 16, beside the binary32 path
         q8k = {}

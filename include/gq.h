@@ -158,6 +158,18 @@ gq_status gq_gemv_q4k_multi(const void *table, const void *table_dev, void *stre
 gq_status gq_gemv_q4k_swiglu(const void *w_gate, const void *w_up, const float *x, float *h,
                              int64_t M, int64_t K, void *stream);
 
+/* gq_gemv_q4k_swiglu at batch B (1 <= B <= 16): x [B][K] binary32, h [B][M]
+ * binary32, h[b][r] = silu(g_r(x[b])) * u_r(x[b]).  B = 1 is
+ * gq_gemv_q4k_swiglu; for B >= 2 g and u are computed as by
+ * gq_gemv_q4k_multi_batched (the matrix cores, the same error bound), one
+ * launch streaming both matrices, the epilogue in binary32.  Requires
+ * K % 256 == 0, M * (K/256) * 144 < 2^32 and B * K * 4 < 2^31 for B >= 2
+ * (GQ_ESHAPE otherwise; B = 1 as gq_gemv_q4k_swiglu), B in [1, 16]
+ * (GQ_EINVAL), 16-byte aligned pointers; M = 0 launches nothing; h must not
+ * overlap the inputs. */
+gq_status gq_gemv_q4k_swiglu_batched(const void *w_gate, const void *w_up, const float *x,
+                                     float *h, int64_t M, int64_t K, int64_t B, void *stream);
+
 /* The same planned products at batch B (1 <= B <= 16): descriptor i's x is
  * [B][K] and y is [B][M] (row-major), y_i[b] = W_i x_i[b].  B = 1 is
  * gq_gemv_q4k_multi.  For B >= 2 the products run on the matrix cores (the

@@ -30,6 +30,11 @@
 // activation would meet a near-cancelling d*sc*q - dmin*m through the
 // factored form, whose error follows the two terms, not their difference.
 //
+// Gate/up pairs (PAIR): a block is 64 output rows r of the gate and up
+// matrices (same shape); a wave's two 16-row tiles are gate rows and up rows
+// r0 .. r0+15, so each lane holds g and u of the same (row, activation row)
+// and writes h = silu(g) * u (binary32) instead of either product.
+//
 // Work split.  A block is 128 consecutive rows of one matrix (4 waves x 2
 // tiles x 16 rows) over the whole K.  The 256 threads first stage the
 // activations of one super-block (B rows x 256) into LDS in the matrix-core
@@ -121,10 +126,15 @@ struct WTile {
 
 } // namespace
 
+template <bool PAIR>
 __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *__restrict__ table,
                                                                GemvEntry inline0, int n,
-                                                               long long total, int B)
+                                                               long long total, int B,
+                                                               const uint8_t *__restrict__ w2)
 {
+    // output rows per block; a pair's output row holds two weight rows, so a
+    // block streams the same 128 weight rows either way
+    constexpr int RBO = PAIR ? RB / 2 : RB;
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,10 +174,10 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         e = a;
     }
     GemvEntry E = entry(e);
-    long long rowb = (long long)(E.K >> 8) * kQ4kBytes;
-    long long blkb = rowb * RB;
+    long long rowb = (long long)(E.K >> 8) * kQ4kBytes; // bytes of one weight row
+    long long blkb = rowb * RB;                          // bytes of one block
     // first block of entry e starting at or after lo_b
-    int row0 = lo_b > E.byte_begin ? (int)((lo_b - E.byte_begin + blkb - 1) / blkb) * RB : 0;
+    int row0 = lo_b > E.byte_begin ? (int)((lo_b - E.byte_begin + blkb - 1) / blkb) * RBO : 0;
 
     for (;;) {
         while (row0 >= E.M) {
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             blkb = rowb * RB;
             row0 = 0;
         }
-        if (E.byte_begin + (long long)row0 * rowb >= hi_b)
+        if (E.byte_begin + (long long)(row0 / RBO) * blkb >= hi_b)
             return;
 
         // ---- one block: rows [row0, row0 + 128) of entry E, all of K ----
@@ -190,25 +200,29 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         // the end return zeros)
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             (void *)E.w, (short)0, (int)(uint32_t)((long long)M * rowb), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rw2 = PAIR ? __builtin_amdgcn_make_buffer_rsrc(
+            (void *)w2, (short)0, (int)(uint32_t)((long long)M * rowb), 0x00020000) : rw;
         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
             (void *)E.x, (short)0, (int)(uint32_t)((long long)B * K * 4), 0x00020000);
         int rows[2];
         uint32_t woff[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            rows[t] = row0 + 32 * wave + 16 * t + col;
+            // PAIR: tile 0 is gate rows, tile 1 the same up rows
+            rows[t] = PAIR ? row0 + 16 * wave + col : row0 + 32 * wave + 16 * t + col;
             woff[t] = (uint32_t)min(rows[t], M - 1) * (uint32_t)rowb;
         }
         auto load_w = [&](int s, WTile(&wt)[2]) {
             const int so = s * kQ4kBytes;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff[t], so, 0);
+                const __amdgpu_buffer_rsrc_t r = t ? rw2 : rw;
+                const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(r, (int)woff[t], so, 0);
                 wt[t].h = make_uint4(h.x, h.y, h.z, h.w);
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
                     wt[t].q[g] = __builtin_amdgcn_raw_buffer_load_b64(
-                        rw, (int)(woff[t] + 8 * quarter) + 16 + 32 * g, so, 0);
+                        r, (int)(woff[t] + 8 * quarter) + 16 + 32 * g, so, 0);
             }
         };
         const bool stager = sb < B;
@@ -440,19 +454,31 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             __builtin_amdgcn_s_barrier();
         }
 
-        // y[b][row] for b = 4*quarter + i
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if (rows[t] < M) {
+        // y[b][row] for b = 4*quarter + i (PAIR: h[b][row] = silu(g) * u)
+        if constexpr (PAIR) {
+            if (rows[0] < M) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int b = 4 * quarter + i;
                     if (b < B)
-                        E.y[(size_t)b * M + rows[t]] = acc[t][i] - macc[t][i];
+                        E.y[(size_t)b * M + rows[0]] =
+                            silu(acc[0][i] - macc[0][i]) * (acc[1][i] - macc[1][i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (rows[t] < M) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int b = 4 * quarter + i;
+                        if (b < B)
+                            E.y[(size_t)b * M + rows[t]] = acc[t][i] - macc[t][i];
+                    }
                 }
             }
         }
-        row0 += RB;
+        row0 += RBO;
     }
 }
 
@@ -463,8 +489,21 @@ hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0
 {
     const int cus = device_cus();
     const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
-    hipLaunchKernelGGL(gemv_q4k_mfma_kernel, dim3((unsigned)grid), dim3(NT), 0, s, table_dev,
-                       inline0, n, total_bytes, B);
+    hipLaunchKernelGGL(gemv_q4k_mfma_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, s,
+                       table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_swiglu_mfma(const void *w_gate, const void *w_up, const float *x, float *h,
+                                   int64_t M, int64_t K, int B, hipStream_t s)
+{
+    const GemvEntry e{(const uint8_t *)w_gate, x, h, (int)M, (int)K, 0, 0};
+    const long long total = 2LL * M * (K / 256) * kQ4kBytes;
+    const long long blocks = (M + RB / 2 - 1) / (RB / 2);
+    const int cus = device_cus();
+    const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
+    hipLaunchKernelGGL(gemv_q4k_mfma_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, s, nullptr,
+                       e, 1, total, B, (const uint8_t *)w_up);
     return hipGetLastError();
 }
 

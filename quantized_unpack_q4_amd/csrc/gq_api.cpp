@@ -588,6 +588,29 @@ gq_status gq_gemv_q4k_swiglu(const void *w_gate, const void *w_up, const float *
     return launched(fn, gq::launch_gemv_swiglu(w_gate, w_up, x, h, M, K, (hipStream_t)stream));
 }
 
+gq_status gq_gemv_q4k_swiglu_batched(const void *w_gate, const void *w_up, const float *x,
+                                     float *h, int64_t M, int64_t K, int64_t B, void *stream)
+{
+    static const char fn[] = "gq_gemv_q4k_swiglu_batched";
+    GQ_TRY(check_dim(fn, "M", M, true));
+    GQ_TRY(check_k(fn, "K", K, 256));
+    if (B < 1 || B > 16)
+        return fail(GQ_EINVAL, "%s: B = %lld is outside [1, 16]", fn, (long long)B);
+    if (B == 1)
+        return gq_gemv_q4k_swiglu(w_gate, w_up, x, h, M, K, stream);
+    if (!gemv_mfma_fits(M, K, B))
+        return fail(GQ_ESHAPE, "%s: M = %lld, K = %lld is too large for batch %lld", fn,
+                    (long long)M, (long long)K, (long long)B);
+    if (M == 0)
+        return GQ_OK;
+    GQ_TRY(check_ptr(fn, "w_gate", w_gate));
+    GQ_TRY(check_ptr(fn, "w_up", w_up));
+    GQ_TRY(check_ptr(fn, "x", x));
+    GQ_TRY(check_ptr(fn, "h", h));
+    return launched(fn, gq::launch_gemv_swiglu_mfma(w_gate, w_up, x, h, M, K, (int)B,
+                                                    (hipStream_t)stream));
+}
+
 gq_status gq_moe_route(const float *logits, int32_t *topk_ids, float *topk_w, int64_t T,
                        int64_t E, int64_t topk, int64_t renormalize, void *stream)
 {

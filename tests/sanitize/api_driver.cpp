@@ -85,6 +85,10 @@ int main()
     REFUSED(gq_gemv_q4k_multi(junk.data(), p, nullptr), GQ_EINVAL);
     LAUNCHED(gq_gemv_q4k_swiglu(p, p, xf, yf, 128, 4096, nullptr));
     REFUSED(gq_gemv_q4k_swiglu(p, p, xf, yf, 128, 32768, nullptr), GQ_ESHAPE);
+    LAUNCHED(gq_gemv_q4k_swiglu_batched(p, p, xf, yf, 128, 4096, 4, nullptr));
+    LAUNCHED(gq_gemv_q4k_swiglu_batched(p, p, xf, yf, 128, 4096, 1, nullptr));
+    REFUSED(gq_gemv_q4k_swiglu_batched(p, p, xf, yf, 128, 4096, 17, nullptr), GQ_EINVAL);
+    REFUSED(gq_gemv_q4k_swiglu_batched(p, p, xf, yf, 1 << 22, 16384, 2, nullptr), GQ_ESHAPE);
 
     // matrix products
     LAUNCHED(gq_gemm_q4k(p, x16, y16, 256, 1024, 512, nullptr));

@@ -29,6 +29,7 @@ hipError_t launch_gemv_stream(const GemvEntry *, const GemvEntry &, int, long lo
 hipError_t launch_gemv_swiglu(const void *, const void *, const float *, float *, int64_t, int64_t, hipStream_t) { return launch(); }
 long long gemv_mfma_blocks(int64_t M) { return (M + 127) / 128; }
 hipError_t launch_gemv_mfma(const GemvEntry *, const GemvEntry &, int, long long, long long, int, hipStream_t) { return launch(); }
+hipError_t launch_gemv_swiglu_mfma(const void *, const void *, const float *, float *, int64_t, int64_t, int, hipStream_t) { return launch(); }
 hipError_t launch_gemm_q4k(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, hipStream_t) { return launch(); }
 hipError_t launch_gemm_q8_0(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, hipStream_t) { return launch(); }
 bool gemm_big_fits(int64_t, int64_t K, int64_t N) { return N * K * 2 < ((int64_t)1 << 31); }

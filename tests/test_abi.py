@@ -162,6 +162,17 @@ def test_gemv_swiglu_refusals(L):
     s, m = status_and_msg(L, f(FAKE, FAKE, FAKE, MISALIGNED, 16, 256, None))
     assert s == "GQ_EALIGN" and "h" in m
     assert f(None, None, None, None, 0, 256, None) == 0
+    b = L.gq_gemv_q4k_swiglu_batched
+    for args, code in (((16, 300, 4), "GQ_ESHAPE"), ((16, 256, 0), "GQ_EINVAL"),
+                       ((16, 256, 17), "GQ_EINVAL"), ((1 << 22, 16384, 2), "GQ_ESHAPE"),
+                       ((16, 32768, 1), "GQ_ESHAPE"), ((-1, 256, 4), "GQ_EINVAL")):
+        s, m = status_and_msg(L, b(FAKE, FAKE, FAKE, FAKE, *args, None))
+        assert s == code and "swiglu" in m, (args, s, m)
+    s, m = status_and_msg(L, b(FAKE, None, FAKE, FAKE, 16, 256, 4, None))
+    assert s == "GQ_EINVAL" and "w_up" in m
+    s, m = status_and_msg(L, b(FAKE, FAKE, FAKE, MISALIGNED, 16, 256, 4, None))
+    assert s == "GQ_EALIGN" and "h" in m
+    assert b(None, None, None, None, 0, 256, 4, None) == 0
 
 
 def test_q8k_refusals(L):

@@ -141,6 +141,29 @@ def test_q4k_swiglu_spikes():
         assert np.all(err <= bound), "swiglu %s: worst %.3g of bound" % (pat, np.nanmax(err / bound))
 
 
+def test_q4k_swiglu_batched_spikes():
+    """Gate/up with the SwiGLU epilogue at batch 4 on the matrix cores, one
+    spiked or wide-range pattern per activation row."""
+    torch = torch_cuda()
+    M, K = 264, 4096
+    wg, _ = adversarial_q4k(97, 0, M, K)
+    wu, _ = adversarial_q4k(97, 1, M, K)
+    pats = ["spike", "spike_alone", "lograng", "advice"]
+    x = np.stack([activations(p, K, 600 + i) for i, p in enumerate(pats)])
+    x = (x * (np.float32(1e3) / np.abs(x).max(axis=1, keepdims=True))).astype(np.float32)
+    B = x.shape[0]
+    h = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q4k_swiglu_batched(dev(wg), dev(wu), dev(x), h, M, K, B)
+    hg = host(h).astype(np.float64)
+    g, Sg = oracle.gemv(oracle.Q4_K, wg, x, M, K)
+    u, Su = oracle.gemv(oracle.Q4_K, wu, x, M, K)
+    hr = oracle.swiglu(g, u)
+    sg = oracle.swiglu(g, np.ones_like(g))
+    bound = TOL * (1.1 * Sg * np.abs(u) + np.abs(sg) * Su) + (4 + np.abs(g)) * 2.0 ** -23 * np.abs(hr)
+    err = np.abs(hg - hr)
+    assert np.all(err <= bound), "swiglu batched: worst %.3g of bound" % np.nanmax(err / bound)
+
+
 @pytest.mark.parametrize("B", [1, 4, 16])
 def test_q8_0_patterns(B):
     torch = torch_cuda()

@@ -253,3 +253,31 @@ def test_gemv_swiglu(M, K):
     assert np.isfinite(hg).all()
     assert np.all(err <= bound), "swiglu %dx%d: worst %.3g of bound" % (M, K, (err / bound).max())
     say("  worst err/bound", (err / bound).max())
+
+
+@pytest.mark.parametrize("B", [2, 5, 16])
+@pytest.mark.parametrize("M,K", [(1, 256), (300, 1024), (37, 14336), (14336, 4096)])
+def test_gemv_swiglu_batched(M, K, B):
+    """Gate and up products with the SwiGLU epilogue at batch 2-16 in one
+    launch on the matrix cores (blocks of 64 output rows, each pairing 64 gate
+    rows with the same up rows; ragged M, a single row): every output of
+    every activation row against the oracle, with the bound of the batch-1
+    test.  The output starts as NaN, so every element must be written."""
+    torch = torch_cuda()
+    say("swiglu batched", M, K, B)
+    wg = synth.q4k_blocks(53, 2 * M, M, K)
+    wu = synth.q4k_blocks(53, 2 * M + 1, M, K)
+    x = synth.activations_f32(53, M, B, K)
+    h = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q4k_swiglu_batched(dev(wg), dev(wu), dev(x), h, M, K, B)
+    hg = host(h).astype(np.float64)
+    g, Sg = oracle.gemv(oracle.Q4_K, wg, x, M, K)
+    u, Su = oracle.gemv(oracle.Q4_K, wu, x, M, K)
+    hr = oracle.swiglu(g, u)
+    sg = oracle.swiglu(g, np.ones_like(g))
+    bound = TOL * (1.1 * Sg * np.abs(u) + np.abs(sg) * Su) + (4 + np.abs(g)) * 2.0 ** -23 * np.abs(hr)
+    err = np.abs(hg - hr)
+    assert np.isfinite(hg).all()
+    assert np.all(err <= bound), "swiglu B=%d %dx%d: worst %.3g of bound" % (
+        B, M, K, (err / bound).max())
+    say("  worst err/bound", (err / bound).max())
