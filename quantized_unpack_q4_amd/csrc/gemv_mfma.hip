@@ -8,9 +8,11 @@
 // the factored form of a Q4_K super-block,
 //     sum over sub-blocks j of  (d*sc_j) * sum_k q_k x_k  -  (dmin*m_j) * sum_k x_k,
 // with both sums exact or binary32-accurate:
-//   * sum_j sc_j * sum_k q_k x_k runs on v_mfma_f32_16x16x32_f16, one
-//     sub-block (32 weights) per instruction and one accumulator over the
-//     super-block: the quant times its sub-block's 6-bit scale (at most 945)
+//   * sum_j sc_j * sum_k q_k x_k runs on v_mfma_f32_16x16x32_f16 with one
+//     accumulator over the super-block; the lanes of quarter q own quant group
+//     q (sub-blocks 2q and 2q+1, 32 bytes), so an instruction takes 8 weights
+//     of one sub-block from each quarter: the quant times its sub-block's
+//     6-bit scale (at most 945)
 //     enters as the binary16 subnormal (sc*q)*2^-24 (exact) and the
 //     activation as two binary16 halves hi + lo of x * 2^e, where 2^e (per
 //     activation row and super-block) brings the largest |x| of the slice to
@@ -118,10 +120,10 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p)
 }
 
 // Packed weights of one 16-row tile for one super-block, as this lane needs
-// them: the 16-byte header of its row and its 8 quant bytes of each 32-byte group.
+// them: the 16-byte header of its row and the 32 bytes of quant group
+// `quarter` (sub-blocks 2*quarter and 2*quarter + 1).
 struct WTile {
-    uint4 h;
-    u32x2 q[4];
+    uint4 h, qa, qb;
 };
 
 } // namespace
@@ -218,11 +220,13 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             for (int t = 0; t < 2; ++t) {
                 const __amdgpu_buffer_rsrc_t r = t ? rw2 : rw;
                 const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(r, (int)woff[t], so, 0);
+                const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, (int)(woff[t] + 32 * quarter) + 16, so, 0);
+                const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, (int)(woff[t] + 32 * quarter) + 32, so, 0);
                 wt[t].h = make_uint4(h.x, h.y, h.z, h.w);
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    wt[t].q[g] = __builtin_amdgcn_raw_buffer_load_b64(
-                        r, (int)(woff[t] + 8 * quarter) + 16 + 32 * g, so, 0);
+                wt[t].qa = make_uint4(a.x, a.y, a.z, a.w);
+                wt[t].qb = make_uint4(b.x, b.y, b.z, b.w);
             }
         };
         const bool stager = sb < B;
@@ -307,7 +311,12 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             macc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
 
-        // one super-block from LDS buffer buf and packed weights wt
+        // one super-block from LDS buffer buf and packed weights wt.  Matrix-
+        // core step (p, hh) takes, in quarter q, positions 8p .. 8p+7 of
+        // sub-block 2q + hh (the lane's quant group q: low nibbles for hh = 0,
+        // high for hh = 1) against activation chunk (2q + hh, p); the k order
+        // is permuted alike for both operands, and a lane needs the 6-bit
+        // scales of two sub-blocks only
         auto compute = [&](int buf, const WTile(&wt)[2]) {
             // the 6-bit scale of each sub-block is folded into the quant
             // operand: sc*q <= 945 < 1024 is the binary16 subnormal
@@ -316,7 +325,10 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             float4_t dacc[2];
             float mb[2][2]; // dmin*m_j for j = quarter and 4 + quarter, per tile
             float d24[2];
-            uint32_t scp[2][8]; // sc_j in both 16-bit halves
+            uint32_t scp[2][2]; // sc of sub-blocks 2q, 2q+1 in both 16-bit halves
+            // sub-blocks 2q and 2q + 1: bytes 2(q & 1) and 2(q & 1) + 1 of the
+            // packed scale word of sub-blocks 0-3 (q < 2) or 4-7
+            const uint32_t bsel = 2u * (uint32_t)(quarter & 1);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 dacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -327,43 +339,42 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                 const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
                 const uint32_t m03 = h.z & 0x3F3F3F3Fu;
                 const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // byte j into bytes 0 and 2, zeros above
-                    scp[t][j] = __builtin_amdgcn_perm(0u, sc03, 0x0C000C00u | (j << 16) | j);
-                    scp[t][4 + j] = __builtin_amdgcn_perm(0u, sc47, 0x0C000C00u | (j << 16) | j);
-                }
+                const uint32_t scw = quarter < 2 ? sc03 : sc47;
+                scp[t][0] = __builtin_amdgcn_perm(0u, scw, 0x0C000C00u | (bsel << 16) | bsel);
+                scp[t][1] = __builtin_amdgcn_perm(0u, scw, 0x0C000C00u | ((bsel + 1) << 16) | (bsel + 1));
                 mb[t][0] = dmin * (float)__builtin_amdgcn_ubfe(m03, 8 * quarter, 8);
                 mb[t][1] = dmin * (float)__builtin_amdgcn_ubfe(m47, 8 * quarter, 8);
             }
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int pp = 0; pp < 4; ++pp) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const int j = 2 * g + hh;
-                    const uint4 xh = sm.xh[buf][j][quarter][col ^ swz(j, quarter)];
-                    const uint4 xl = sm.xl[buf][j][quarter][col ^ swz(j, quarter)];
+                    const int j = 2 * quarter + hh;
+                    const uint4 xh = sm.xh[buf][j][pp][col ^ swz(j, pp)];
+                    const uint4 xl = sm.xl[buf][j][pp][col ^ swz(j, pp)];
                     const half8_t ah = __builtin_bit_cast(half8_t, xh);
                     const half8_t al = __builtin_bit_cast(half8_t, xl);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        // low nibbles (hh = 0) or high nibbles (hh = 1) of this
-                        // lane's 8 quant bytes, as 16-bit lanes:
-                        // (k0,k2), (k1,k3), (k4,k6), (k5,k7), times sc_j
-                        const uint32_t D0 = hh ? wt[t].q[g].x >> 4 : wt[t].q[g].x;
-                        const uint32_t D1 = hh ? wt[t].q[g].y >> 4 : wt[t].q[g].y;
+                        // positions 8pp .. 8pp+7 of the group: low nibbles
+                        // (hh = 0) or high nibbles (hh = 1) as 16-bit lanes
+                        // (k0,k2), (k1,k3), (k4,k6), (k5,k7), times sc
+                        const uint4 &qv = pp < 2 ? wt[t].qa : wt[t].qb;
+                        const uint32_t W0 = (pp & 1) ? qv.z : qv.x, W1 = (pp & 1) ? qv.w : qv.y;
+                        const uint32_t D0 = hh ? W0 >> 4 : W0;
+                        const uint32_t D1 = hh ? W1 >> 4 : W1;
                         const uint32_t mk = 0x000F000Fu;
-                        const u16x2 sv = __builtin_bit_cast(u16x2, scp[t][j]);
+                        const u16x2 sv = __builtin_bit_cast(u16x2, scp[t][hh]);
                         auto scq = [&](uint32_t v) {
                             return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v & mk) * sv);
                         };
-                        const uint4 qv = make_uint4(scq(D0), scq(D0 >> 8), scq(D1), scq(D1 >> 8));
-                        const half8_t bq = __builtin_bit_cast(half8_t, qv);
+                        const uint4 qv2 = make_uint4(scq(D0), scq(D0 >> 8), scq(D1), scq(D1 >> 8));
+                        const half8_t bq = __builtin_bit_cast(half8_t, qv2);
                         dacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, dacc[t], 0, 0, 0);
                         dacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, dacc[t], 0, 0, 0);
                     }
                 }
-                // bound the live ranges: one group's operands at a time
+                // bound the live ranges: one position group's operands at a time
                 __builtin_amdgcn_sched_barrier(0);
             }
             // sub-blocks computed exactly (rare; the condition is the same for
@@ -383,31 +394,30 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                         const int bit = __builtin_ctzll(bits);
                         bits &= bits - 1;
                         const int b = 4 * wv + (bit >> 4), j = (bit & 15) >> 1;
-                        // this lane's 8 activations of the sub-block: k = 32j + 8*quarter + i
-                        const float4_t xa = *reinterpret_cast<const float4_t *>(&sm.xf[buf][j][b][8 * quarter]);
-                        const float4_t xb = *reinterpret_cast<const float4_t *>(&sm.xf[buf][j][b][8 * quarter + 4]);
-                        const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+                        // the lanes of quarter j >> 1 hold the 32 quants of
+                        // sub-block j of their row (bytes 0-31 of the group,
+                        // low nibbles for even j, high for odd)
+                        const float *xs = &sm.xf[buf][j][b][0];
 #pragma unroll
                         for (int t = 0; t < 2; ++t) {
-                            const uint4 h = wt[t].h;
-                            uint32_t sc, m;
-                            q4k_scale_min(h.y, h.z, h.w, j, sc, m);
-                            const float dsc = half_to_float(h.x) * (float)sc;
-                            const float dmm = half_to_float(h.x >> 16) * (float)m;
-                            const uint32_t D0 = (j >> 1) == 0 ? wt[t].q[0].x : (j >> 1) == 1 ? wt[t].q[1].x
-                                              : (j >> 1) == 2 ? wt[t].q[2].x : wt[t].q[3].x;
-                            const uint32_t D1 = (j >> 1) == 0 ? wt[t].q[0].y : (j >> 1) == 1 ? wt[t].q[1].y
-                                              : (j >> 1) == 2 ? wt[t].q[2].y : wt[t].q[3].y;
-                            const int sh = 4 * (j & 1);
                             float part = 0.f;
+                            if (quarter == (j >> 1)) {
+                                const uint4 h = wt[t].h;
+                                uint32_t sc, m;
+                                q4k_scale_min(h.y, h.z, h.w, j, sc, m);
+                                const float dsc = half_to_float(h.x) * (float)sc;
+                                const float dmm = half_to_float(h.x >> 16) * (float)m;
+                                const uint32_t qw[8] = {wt[t].qa.x, wt[t].qa.y, wt[t].qa.z, wt[t].qa.w,
+                                                        wt[t].qb.x, wt[t].qb.y, wt[t].qb.z, wt[t].qb.w};
+                                const int sh = 4 * (j & 1);
 #pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                const uint32_t q = ((i < 4 ? D0 : D1) >> (8 * (i & 3) + sh)) & 15u;
-                                part = fmaf(fmaf(dsc, (float)q, -dmm), xv[i], part);
+                                for (int i = 0; i < 32; ++i) {
+                                    const uint32_t q = (qw[i >> 2] >> (8 * (i & 3) + sh)) & 15u;
+                                    part = fmaf(fmaf(dsc, (float)q, -dmm), xs[i], part);
+                                }
                             }
-                            // the four quarters of weight row col
-                            part += __shfl_xor(part, 16, 64);
-                            part += __shfl_xor(part, 32, 64);
+                            // from the lane of weight row col in quarter j >> 1
+                            part = __shfl(part, col + 16 * (j >> 1), 64);
                             if (quarter == (b >> 2)) {
                                 const int i = b & 3;
                                 acc[t][0] += i == 0 ? part : 0.f;
