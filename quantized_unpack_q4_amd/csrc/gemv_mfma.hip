@@ -37,8 +37,9 @@
 // r0 .. r0+15, so each lane holds g and u of the same (row, activation row)
 // and writes h = silu(g) * u (binary32) instead of either product.
 //
-// Work split.  A block is 128 consecutive rows of one matrix (4 waves x 2
-// tiles x 16 rows) over the whole K.  The 256 threads first stage the
+// Work split.  A block is 192 consecutive rows of one matrix (4 waves x 3
+// tiles x 16 rows; 128 with two tiles when there are too few blocks of 192
+// for the grid) over the whole K.  The 256 threads first stage the
 // activations of one super-block (B rows x 256) into LDS in the matrix-core
 // layout, then every wave multiplies its two 16-row tiles against them; the
 // staging of super-block s+1 and the packed weight loads of s+2 overlap the
@@ -56,7 +57,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int RB = 128; // rows per block
+// rows per block: 64 per 16-row tile of each wave (two or three tiles)
+constexpr int rows_per_block(int tiles) { return 64 * tiles; }
 constexpr int NT = 256; // threads per workgroup
 
 struct Smem {
@@ -128,15 +130,17 @@ struct WTile {
 
 } // namespace
 
-template <bool PAIR>
+template <bool PAIR, int TW>
 __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *__restrict__ table,
                                                                GemvEntry inline0, int n,
                                                                long long total, int B,
                                                                const uint8_t *__restrict__ w2)
 {
-    // output rows per block; a pair's output row holds two weight rows, so a
-    // block streams the same 128 weight rows either way
-    constexpr int RBO = PAIR ? RB / 2 : RB;
+    // TW 16-row tiles per wave; a pair's output row holds two weight rows
+    // (tile 0 gate, tile 1 up), so a pair block is 64 output rows
+    static_assert(!PAIR || TW == 2, "pairs take two tiles per wave");
+    constexpr int RB = rows_per_block(TW);  // weight rows per block
+    constexpr int RBO = PAIR ? RB / 2 : RB; // output rows per block
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -206,19 +210,19 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             (void *)w2, (short)0, (int)(uint32_t)((long long)M * rowb), 0x00020000) : rw;
         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
             (void *)E.x, (short)0, (int)(uint32_t)((long long)B * K * 4), 0x00020000);
-        int rows[2];
-        uint32_t woff[2];
+        int rows[TW];
+        uint32_t woff[TW];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TW; ++t) {
             // PAIR: tile 0 is gate rows, tile 1 the same up rows
-            rows[t] = PAIR ? row0 + 16 * wave + col : row0 + 32 * wave + 16 * t + col;
+            rows[t] = PAIR ? row0 + 16 * wave + col : row0 + 16 * TW * wave + 16 * t + col;
             woff[t] = (uint32_t)min(rows[t], M - 1) * (uint32_t)rowb;
         }
-        auto load_w = [&](int s, WTile(&wt)[2]) {
+        auto load_w = [&](int s, WTile(&wt)[TW]) {
             const int so = s * kQ4kBytes;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const __amdgpu_buffer_rsrc_t r = t ? rw2 : rw;
+            for (int t = 0; t < TW; ++t) {
+                const __amdgpu_buffer_rsrc_t r = PAIR && t ? rw2 : rw;
                 const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(r, (int)woff[t], so, 0);
                 const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(
                     r, (int)(woff[t] + 32 * quarter) + 16, so, 0);
@@ -304,9 +308,9 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                 sm.inv[buf][sb] = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
         };
 
-        float4_t acc[2], macc[2];
+        float4_t acc[TW], macc[TW];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TW; ++t) {
             acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
             macc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
@@ -317,20 +321,20 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         // high for hh = 1) against activation chunk (2q + hh, p); the k order
         // is permuted alike for both operands, and a lane needs the 6-bit
         // scales of two sub-blocks only
-        auto compute = [&](int buf, const WTile(&wt)[2]) {
+        auto compute = [&](int buf, const WTile(&wt)[TW]) {
             // the 6-bit scale of each sub-block is folded into the quant
             // operand: sc*q <= 945 < 1024 is the binary16 subnormal
             // (sc*q)*2^-24 exactly, so one accumulator per tile runs over all
             // eight sub-blocks and d*2^24 is applied once per super-block
-            float4_t dacc[2];
-            float mb[2][2]; // dmin*m_j for j = quarter and 4 + quarter, per tile
-            float d24[2];
-            uint32_t scp[2][2]; // sc of sub-blocks 2q, 2q+1 in both 16-bit halves
+            float4_t dacc[TW];
+            float mb[TW][2]; // dmin*m_j for j = quarter and 4 + quarter, per tile
+            float d24[TW];
+            uint32_t scp[TW][2]; // sc of sub-blocks 2q, 2q+1 in both 16-bit halves
             // sub-blocks 2q and 2q + 1: bytes 2(q & 1) and 2(q & 1) + 1 of the
             // packed scale word of sub-blocks 0-3 (q < 2) or 4-7
             const uint32_t bsel = 2u * (uint32_t)(quarter & 1);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < TW; ++t) {
                 dacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
                 const uint4 h = wt[t].h;
                 const float dmin = half_to_float(h.x >> 16);
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                     const half8_t ah = __builtin_bit_cast(half8_t, xh);
                     const half8_t al = __builtin_bit_cast(half8_t, xl);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         // positions 8pp .. 8pp+7 of the group: low nibbles
                         // (hh = 0) or high nibbles (hh = 1) as 16-bit lanes
                         // (k0,k2), (k1,k3), (k4,k6), (k5,k7), times sc
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                         // low nibbles for even j, high for odd)
                         const float *xs = &sm.xf[buf][j][b][0];
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) {
+                        for (int t = 0; t < TW; ++t) {
                             float part = 0.f;
                             if (quarter == (j >> 1)) {
                                 const uint4 h = wt[t].h;
@@ -432,14 +436,14 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             const float4_t iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][4 * quarter]);
             const float sx0 = sm.sx[buf][quarter][col], sx1 = sm.sx[buf][4 + quarter][col];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < TW; ++t) {
                 acc[t] = (d24[t] * iv) * dacc[t] + acc[t];
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx0, mb[t][0], macc[t], 0, 0, 0);
                 macc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx1, mb[t][1], macc[t], 0, 0, 0);
             }
         };
 
-        WTile wa[2], wb[2];
+        WTile wa[TW], wb[TW];
         load_x(0);
         load_w(0, wa);
         load_w(min(1, nsb - 1), wb);
@@ -477,7 +481,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             }
         } else {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < TW; ++t) {
                 if (rows[t] < M) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -492,15 +496,28 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
     }
 }
 
-long long gemv_mfma_blocks(int64_t M) { return (M + RB - 1) / RB; }
+long long gemv_mfma_blocks(int64_t M, int tiles)
+{
+    const int rb = rows_per_block(tiles);
+    return (M + rb - 1) / rb;
+}
 
 hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
-                            long long total_bytes, long long blocks, int B, hipStream_t s)
+                            long long total_bytes, long long blocks2, long long blocks3, int B,
+                            hipStream_t s)
 {
+    // three tiles per wave (192-row blocks: each block's activation staging
+    // serves 1.5 times the weights; decode stack at batch 4 1273 -> 1196 us)
+    // when they still give every workgroup of the grid a block, else two
     const int cus = device_cus();
-    const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
-    hipLaunchKernelGGL(gemv_q4k_mfma_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, s,
-                       table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr);
+    if (blocks3 >= 2LL * cus) {
+        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 3>), dim3((unsigned)(2 * cus)), dim3(NT), 0,
+                           s, table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr);
+    } else {
+        const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
+        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2>), dim3((unsigned)grid), dim3(NT), 0, s,
+                           table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr);
+    }
     return hipGetLastError();
 }
 
@@ -509,11 +526,11 @@ hipError_t launch_gemv_swiglu_mfma(const void *w_gate, const void *w_up, const f
 {
     const GemvEntry e{(const uint8_t *)w_gate, x, h, (int)M, (int)K, 0, 0};
     const long long total = 2LL * M * (K / 256) * kQ4kBytes;
-    const long long blocks = (M + RB / 2 - 1) / (RB / 2);
+    const long long blocks = (M + 63) / 64;
     const int cus = device_cus();
     const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
-    hipLaunchKernelGGL(gemv_q4k_mfma_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, s, nullptr,
-                       e, 1, total, B, (const uint8_t *)w_up);
+    hipLaunchKernelGGL((gemv_q4k_mfma_kernel<true, 2>), dim3((unsigned)grid), dim3(NT), 0, s,
+                       nullptr, e, 1, total, B, (const uint8_t *)w_up);
     return hipGetLastError();
 }
 

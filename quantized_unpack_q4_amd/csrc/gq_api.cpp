@@ -167,8 +167,9 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
     if (B >= 2 && gemv_mfma_fits(M, K, B)) {
         gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0, 0};
         const long long total = (long long)M * (K / 256) * 144;
-        return launched(fn, gq::launch_gemv_mfma(nullptr, e, 1, total, gq::gemv_mfma_blocks(M),
-                                                 (int)B, (hipStream_t)stream));
+        return launched(fn, gq::launch_gemv_mfma(nullptr, e, 1, total, gq::gemv_mfma_blocks(M, 2),
+                                                 gq::gemv_mfma_blocks(M, 3), (int)B,
+                                                 (hipStream_t)stream));
     }
     return launched(fn, gq::launch_gemv_q4k(w, x, y, M, K, (int)B, (hipStream_t)stream));
 }
@@ -286,17 +287,18 @@ gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, in
     }
     const gq::GemvEntry *ent =
         reinterpret_cast<const gq::GemvEntry *>((const uint8_t *)table + sizeof h);
-    long long blocks = 0;
+    long long blocks2 = 0, blocks3 = 0;
     for (int64_t i = 0; i < h.n; ++i) {
         gq::GemvEntry e;
         memcpy(&e, &ent[i], sizeof e);
         if (!gemv_mfma_fits(e.M, e.K, B))
             return fail(GQ_ESHAPE, "%s: entry %lld (M = %d, K = %d) is too large for batch %lld",
                         fn, (long long)i, e.M, e.K, (long long)B);
-        blocks += gq::gemv_mfma_blocks(e.M);
+        blocks2 += gq::gemv_mfma_blocks(e.M, 2);
+        blocks3 += gq::gemv_mfma_blocks(e.M, 3);
     }
-    return launched(fn, gq::launch_gemv_mfma(dev, none, (int)h.n, h.total_bytes, blocks, (int)B,
-                                             (hipStream_t)stream));
+    return launched(fn, gq::launch_gemv_mfma(dev, none, (int)h.n, h.total_bytes, blocks2, blocks3,
+                                             (int)B, (hipStream_t)stream));
 }
 
 static gq_status gemm_common(const char *fn, const void *w, const uint16_t *x, uint16_t *y,

@@ -64,13 +64,14 @@ hipError_t launch_gemv_swiglu(const void *w_gate, const void *w_up, const float 
 // Small-batch (2 <= B <= 16) products on the matrix cores, over a table of
 // entries (or the single entry inline0 when table_dev is null); blocks of 128
 // rows are dealt to workgroups by byte ranges of the packed weights.
-long long gemv_mfma_blocks(int64_t M);
+long long gemv_mfma_blocks(int64_t M, int tiles); // blocks of 64*tiles rows (tiles 2 or 3)
 // h[b][r] = silu(w_gate_r x[b]) * (w_up_r x[b]) for 2 <= B <= 16 on the same
 // kernel: blocks of 64 output rows pair 64 gate rows with the same up rows.
 hipError_t launch_gemv_swiglu_mfma(const void *w_gate, const void *w_up, const float *x, float *h,
                                    int64_t M, int64_t K, int B, hipStream_t s);
 hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
-                            long long total_bytes, long long blocks, int B, hipStream_t s);
+                            long long total_bytes, long long blocks2, long long blocks3, int B,
+                            hipStream_t s);
 
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s);

@@ -27,8 +27,8 @@ long long gemv_stream_tiles(int64_t M, int64_t) { return (M + 23) / 24; }
 int gemv_stream_grid(long long, long long tiles) { return tiles < 512 ? (int)tiles : 512; }
 hipError_t launch_gemv_stream(const GemvEntry *, const GemvEntry &, int, long long, int, hipStream_t) { return launch(); }
 hipError_t launch_gemv_swiglu(const void *, const void *, const float *, float *, int64_t, int64_t, hipStream_t) { return launch(); }
-long long gemv_mfma_blocks(int64_t M) { return (M + 127) / 128; }
-hipError_t launch_gemv_mfma(const GemvEntry *, const GemvEntry &, int, long long, long long, int, hipStream_t) { return launch(); }
+long long gemv_mfma_blocks(int64_t M, int tiles) { return (M + 64 * tiles - 1) / (64 * tiles); }
+hipError_t launch_gemv_mfma(const GemvEntry *, const GemvEntry &, int, long long, long long, long long, int, hipStream_t) { return launch(); }
 hipError_t launch_gemv_swiglu_mfma(const void *, const void *, const float *, float *, int64_t, int64_t, int, hipStream_t) { return launch(); }
 hipError_t launch_gemm_q4k(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, hipStream_t) { return launch(); }
 hipError_t launch_gemm_q8_0(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, hipStream_t) { return launch(); }
