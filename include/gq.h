@@ -180,6 +180,22 @@ gq_status gq_gemv_q4k_swiglu_batched(const void *w_gate, const void *w_up, const
 gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, int64_t B,
                                     void *stream);
 
+/* gq_gemv_q4k_multi_batched with the activations staged once per product and
+ * super-block into a caller workspace by a pre-pass, instead of by every block
+ * of 192 weight rows: three launches on the stream (a prefix of the entries'
+ * super-blocks, the staging, the products).  Same results, bit for bit, and
+ * the same limits; B = 1 is gq_gemv_q4k_multi (ws unused, may be NULL).
+ * ws: at least gq_gemv_q4k_multi_batched_ws_bytes(table, B) bytes, 16-byte
+ * aligned, contents on entry ignored; it must not be in use by another call
+ * while this one runs.  Errors as gq_gemv_q4k_multi_batched, plus
+ * GQ_EWORKSPACE (ws NULL or too small) and GQ_EALIGN. */
+gq_status gq_gemv_q4k_multi_batched_ws(const void *table, const void *table_dev, int64_t B,
+                                       void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of gq_gemv_q4k_multi_batched_ws (1 for B = 1); 0 if the
+ * table or B is invalid. */
+size_t gq_gemv_q4k_multi_batched_ws_bytes(const void *table, int64_t B);
+
 /* Q4_K matrix product for prefill, binary16 activations and output:
  *   Y[n][r] = binary16( sum_k X[n][k] * w16[r][k] ),  accumulated in binary32,
  * where w16 is each weight rounded to binary16 as described above.

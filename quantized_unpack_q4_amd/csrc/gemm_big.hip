@@ -52,6 +52,7 @@
 
 #include "gq_device.h"
 #include "gq_internal.h"
+#include "gq_lds_dma.h"
 
 namespace gq {
 
@@ -67,20 +68,6 @@ __device__ __forceinline__ uint4 gload16(const uint8_t *p)
 {
     const u32x4 v = *(g_u32x4 *)(p);
     return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// 16 bytes per lane, global -> LDS: lane l reads gbase + voff (gbase
-// wave-uniform, voff a 32-bit byte offset) and lands at LDS byte address
-// m0 + 16*l (m0 wave-uniform).  Issued as inline assembly so that the
-// compiler's wait insertion does not see it: the kernel waits for these
-// copies itself, with an explicit vmcnt before the barrier that publishes
-// them.  The compiler then counts fewer outstanding loads than there are, so
-// every wait it inserts for its own loads errs on the safe side.
-__device__ __forceinline__ void load_lds16(const void *gbase, uint32_t voff, uint32_t m0)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
-                 "s"(m0)
-                 : "memory", "m0");
 }
 
 // Two weights from two binary16 quants (subnormal q*2^-24 or 16q*2^-24, the

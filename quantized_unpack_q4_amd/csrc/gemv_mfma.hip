@@ -47,6 +47,7 @@
 // byte ranges of packed weights, as in the batch-1 streaming kernel.
 #include "gq_device.h"
 #include "gq_internal.h"
+#include "gq_lds_dma.h"
 
 namespace gq {
 
@@ -113,6 +114,84 @@ __device__ __forceinline__ void split2(float xa, float xb, float s, uint32_t &hi
     lo = pack_h2(la, lb);
 }
 
+// The staging of one activation slice by the 16 lanes of an activation row
+// (lane sc_ holds x[16 sc_ .. 16 sc_ + 15] of the super-block, xr): the
+// wave's exact-path flags (eb, one bit per even lane), and for stagers the
+// binary16 hi/lo parts of quarters 2(sc_ & 1) + h, h = 0, 1, of sub-block
+// sc_ / 2 (handed to put(h, hi, lo)), its sum sx (0 when it is computed
+// exactly) and the row's 2^-e (inv).  Every lane of the wave must call it
+// (cross-lane reductions).  Returns whether the sub-block is computed exactly.
+template <typename Put>
+__device__ __forceinline__ bool stage_slice(const float4_t (&xr)[4], bool stager, int lane,
+                                            uint64_t &eb, float &sx, float &inv, Put &&put)
+{
+    const int sc_ = lane & 15;
+    float m = 0.f, mn = INFINITY, l1 = 0.f, sum = 0.f;
+    if (stager) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a[4] = {fabsf(xr[i].x), fabsf(xr[i].y), fabsf(xr[i].z), fabsf(xr[i].w)};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                m = fmaxf(m, a[c]);
+                mn = a[c] > 0.f ? fminf(mn, a[c]) : mn;
+                l1 += a[c];
+            }
+            sum += (xr[i].x + xr[i].y) + (xr[i].z + xr[i].w);
+        }
+    }
+    // the partner lane holds the other half of sub-block sc_ / 2
+    float mj = fmaxf(m, dpp_f(m, 0));
+    mn = fminf(mn, dpp_f(mn, 0));
+    sum += dpp_f(sum, 0);
+    // max and sum of |x| over the 16 lanes of this activation row
+    m = mj;
+    m = fmaxf(m, dpp_f(m, 1));
+    m = fmaxf(m, dpp_f(m, 2));
+    m = fmaxf(m, dpp_f(m, 3));
+    l1 += dpp_f(l1, 0);
+    l1 += dpp_f(l1, 1);
+    l1 += dpp_f(l1, 2);
+    l1 += dpp_f(l1, 3);
+    const bool exact = stager && mj > 0.f && (kSplitSpan * mn < m || mj > kDominant * l1);
+    eb = __ballot(exact && (sc_ & 1) == 0);
+    if (!stager)
+        return false;
+    // 2^e with the largest |x| in [2^14, 2^15): exponent field 268 - ex,
+    // kept in [1, 253] (zero or tiny slices get 2^126)
+    const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 255u);
+    const int fe = min(max(268 - ex, 1), 253);
+    const float s = exact ? 0.f : __builtin_bit_cast(float, (uint32_t)fe << 23);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        // quarter 2(sc_ & 1) + h: elements k = 8h .. 8h+7 of this lane's 16
+        const float4_t a = xr[2 * h], c = xr[2 * h + 1];
+        uint4 hv, lv;
+        split2(a.x, a.z, s, hv.x, lv.x); // k0, k2
+        split2(a.y, a.w, s, hv.y, lv.y); // k1, k3
+        split2(c.x, c.z, s, hv.z, lv.z); // k4, k6
+        split2(c.y, c.w, s, hv.w, lv.w); // k5, k7
+        put(h, hv, lv);
+    }
+    sx = exact ? 0.f : sum;
+    inv = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
+    return exact;
+}
+
+// Activations staged once per (product, super-block) for batch B into a
+// caller workspace (gq_gemv_q4k_multi_batched_ws), as records that a block
+// copies into LDS as they are:
+//   bytes [0, 32)            exact-path flags, uint64 [4] (as Smem::exact)
+//   bytes [32, 96)           2^-e per activation row, float [16]
+//   bytes [96, 608)          sub-block sums, float [8 j][16 rows]
+//   bytes [608, 608 + 512 B) binary16 hi parts, 16 bytes [8 j][4 q][B rows]
+//   then the lo parts, same layout; padded to whole KiB (the copies move
+//   1 KiB per wave instruction).  Rows past B are not written (their
+//   outputs are discarded).
+constexpr int kRecInv = 32, kRecSx = 96, kRecHi = 608;
+constexpr int rec_bytes(int B) { return (kRecHi + 1024 * B + 1023) / 1024 * 1024; }
+constexpr int kRecMax = rec_bytes(16);
+
 __device__ __forceinline__ const void *uniform_ptr(const void *p)
 {
     const uint64_t v = (uint64_t)p;
@@ -128,17 +207,29 @@ struct WTile {
     uint4 h, qa, qb;
 };
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8): vmcnt <= vm and lgkmcnt == 0.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
 } // namespace
 
-template <bool PAIR, int TW>
+// PRE: the activations come pre-staged (one record per entry and super-block
+// in ws, entry e's first record at prefix[e], rbytes each) and are copied into
+// LDS by direct-to-LDS loads instead of being staged by every block.
+template <bool PAIR, int TW, bool PRE = false>
 __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *__restrict__ table,
                                                                GemvEntry inline0, int n,
                                                                long long total, int B,
-                                                               const uint8_t *__restrict__ w2)
+                                                               const uint8_t *__restrict__ w2,
+                                                               const uint8_t *__restrict__ ws,
+                                                               const int *__restrict__ prefix,
+                                                               int rbytes)
 {
     // TW 16-row tiles per wave; a pair's output row holds two weight rows
     // (tile 0 gate, tile 1 up), so a pair block is 64 output rows
     static_assert(!PAIR || TW == 2, "pairs take two tiles per wave");
+    static_assert(!PRE || !PAIR, "pre-staged activations: tables of plain products");
+    static_assert(2 * kRecMax <= (int)sizeof(Smem), "two records fit the staging area");
     constexpr int RB = rows_per_block(TW);  // weight rows per block
     constexpr int RBO = PAIR ? RB / 2 : RB; // output rows per block
     __shared__ Smem sm;
@@ -180,6 +271,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         e = a;
     }
     GemvEntry E = entry(e);
+    int recbase = PRE ? __builtin_amdgcn_readfirstlane(prefix[e]) : 0; // first record of entry e
     long long rowb = (long long)(E.K >> 8) * kQ4kBytes; // bytes of one weight row
     long long blkb = rowb * RB;                          // bytes of one block
     // first block of entry e starting at or after lo_b
@@ -190,6 +282,8 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             if (++e >= n)
                 return;
             E = entry(e);
+            if constexpr (PRE)
+                recbase = __builtin_amdgcn_readfirstlane(prefix[e]);
             rowb = (long long)(E.K >> 8) * kQ4kBytes;
             blkb = rowb * RB;
             row0 = 0;
@@ -246,67 +340,40 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         };
         // binary16 hi/lo parts, sub-block sums and scale of the staged slice
         auto store_x = [&](int buf) {
-            float m = 0.f, mn = INFINITY, l1 = 0.f, sum = 0.f;
-            if (stager) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float a[4] = {fabsf(xr[i].x), fabsf(xr[i].y), fabsf(xr[i].z), fabsf(xr[i].w)};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        m = fmaxf(m, a[c]);
-                        mn = a[c] > 0.f ? fminf(mn, a[c]) : mn;
-                        l1 += a[c];
-                    }
-                    sum += (xr[i].x + xr[i].y) + (xr[i].z + xr[i].w);
-                }
-            }
-            // the partner lane holds the other half of sub-block sj
-            float mj = fmaxf(m, dpp_f(m, 0));
-            mn = fminf(mn, dpp_f(mn, 0));
-            sum += dpp_f(sum, 0);
-            // max and sum of |x| over the 16 lanes of this activation row
-            m = mj;
-            m = fmaxf(m, dpp_f(m, 1));
-            m = fmaxf(m, dpp_f(m, 2));
-            m = fmaxf(m, dpp_f(m, 3));
-            l1 += dpp_f(l1, 0);
-            l1 += dpp_f(l1, 1);
-            l1 += dpp_f(l1, 2);
-            l1 += dpp_f(l1, 3);
-            const bool exact = stager && mj > 0.f && (kSplitSpan * mn < m || mj > kDominant * l1);
-            const uint64_t eb = __ballot(exact && (sc_ & 1) == 0);
+            uint64_t eb;
+            float sx, inv;
+            const bool exact = stage_slice(xr, stager, lane, eb, sx, inv,
+                                           [&](int h, const uint4 &hv, const uint4 &lv) {
+                                               const int q = sq0 + h;
+                                               sm.xh[buf][sj][q][sb ^ swz(sj, q)] = hv;
+                                               sm.xl[buf][sj][q][sb ^ swz(sj, q)] = lv;
+                                           });
             if (lane == 0)
                 sm.exact[buf][wave] = eb;
             if (!stager)
                 return;
-            // 2^e with the largest |x| in [2^14, 2^15): exponent field 268 - ex,
-            // kept in [1, 253] (zero or tiny slices get 2^126)
-            const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 255u);
-            const int fe = min(max(268 - ex, 1), 253);
-            const float s = exact ? 0.f : __builtin_bit_cast(float, (uint32_t)fe << 23);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                // quarter sq0 + h: elements k = 8h .. 8h+7 of this lane's 16
-                const float4_t a = xr[2 * h], c = xr[2 * h + 1];
-                uint4 hv, lv;
-                split2(a.x, a.z, s, hv.x, lv.x); // k0, k2
-                split2(a.y, a.w, s, hv.y, lv.y); // k1, k3
-                split2(c.x, c.z, s, hv.z, lv.z); // k4, k6
-                split2(c.y, c.w, s, hv.w, lv.w); // k5, k7
-                const int q = sq0 + h;
-                sm.xh[buf][sj][q][sb ^ swz(sj, q)] = hv;
-                sm.xl[buf][sj][q][sb ^ swz(sj, q)] = lv;
-            }
             if (exact) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<float4_t *>(&sm.xf[buf][sj][sb][16 * (sc_ & 1) + 4 * i]) = xr[i];
             }
             if ((sc_ & 1) == 0)
-                sm.sx[buf][sj][sb] = exact ? 0.f : sum;
+                sm.sx[buf][sj][sb] = sx;
             if (sc_ == 0)
-                sm.inv[buf][sb] = __builtin_bit_cast(float, (uint32_t)(254 - fe) << 23);
+                sm.inv[buf][sb] = inv;
         };
+
+        // PRE: record s of this entry into LDS buffer buf, 1 KiB per copy,
+        // the copies dealt to the waves in turn
+        const uint32_t lds_rec = (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)&sm;
+        auto issue_rec = [&](int s, int buf) {
+            const uint8_t *src = ws + (size_t)(recbase + s) * (size_t)rbytes; // wave-uniform
+            const uint32_t dst = lds_rec + (uint32_t)(buf * kRecMax);
+            for (int c = wave; c < (rbytes >> 10); c += 4)
+                load_lds16(src + 1024 * c, 16u * (uint32_t)lane, dst + 1024u * (uint32_t)c);
+        };
+        auto recp = [&](int buf) { return reinterpret_cast<const uint8_t *>(&sm) + buf * kRecMax; };
+        const int bcol = min(col, B - 1); // rows past B read row B - 1 (outputs discarded)
 
         float4_t acc[TW], macc[TW];
 #pragma unroll
@@ -321,7 +388,7 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         // high for hh = 1) against activation chunk (2q + hh, p); the k order
         // is permuted alike for both operands, and a lane needs the 6-bit
         // scales of two sub-blocks only
-        auto compute = [&](int buf, const WTile(&wt)[TW]) {
+        auto compute = [&](int buf, const WTile(&wt)[TW], int s) {
             // the 6-bit scale of each sub-block is folded into the quant
             // operand: sc*q <= 945 < 1024 is the binary16 subnormal
             // (sc*q)*2^-24 exactly, so one accumulator per tile runs over all
@@ -354,8 +421,15 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int j = 2 * quarter + hh;
-                    const uint4 xh = sm.xh[buf][j][pp][col ^ swz(j, pp)];
-                    const uint4 xl = sm.xl[buf][j][pp][col ^ swz(j, pp)];
+                    uint4 xh, xl;
+                    if constexpr (PRE) {
+                        const uint8_t *r = recp(buf) + kRecHi + ((j * 4 + pp) * B + bcol) * 16;
+                        xh = *reinterpret_cast<const uint4 *>(r);
+                        xl = *reinterpret_cast<const uint4 *>(r + 512 * B);
+                    } else {
+                        xh = sm.xh[buf][j][pp][col ^ swz(j, pp)];
+                        xl = sm.xl[buf][j][pp][col ^ swz(j, pp)];
+                    }
                     const half8_t ah = __builtin_bit_cast(half8_t, xh);
                     const half8_t al = __builtin_bit_cast(half8_t, xl);
 #pragma unroll
@@ -386,7 +460,8 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
             uint64_t ex4[4];
 #pragma unroll
             for (int wv = 0; wv < 4; ++wv) {
-                const uint64_t v = sm.exact[buf][wv];
+                const uint64_t v = PRE ? reinterpret_cast<const uint64_t *>(recp(buf))[wv]
+                                       : sm.exact[buf][wv];
                 ex4[wv] = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
                           __builtin_amdgcn_readfirstlane((uint32_t)v);
             }
@@ -401,7 +476,8 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                         // the lanes of quarter j >> 1 hold the 32 quants of
                         // sub-block j of their row (bytes 0-31 of the group,
                         // low nibbles for even j, high for odd)
-                        const float *xs = &sm.xf[buf][j][b][0];
+                        const float *xs = PRE ? E.x + (size_t)b * K + 256 * s + 32 * j
+                                              : &sm.xf[buf][j][b][0];
 #pragma unroll
                         for (int t = 0; t < TW; ++t) {
                             float part = 0.f;
@@ -433,8 +509,18 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
                     }
                 }
             }
-            const float4_t iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][4 * quarter]);
-            const float sx0 = sm.sx[buf][quarter][col], sx1 = sm.sx[buf][4 + quarter][col];
+            float4_t iv;
+            float sx0, sx1;
+            if constexpr (PRE) {
+                iv = *reinterpret_cast<const float4_t *>(recp(buf) + kRecInv + 16 * quarter);
+                const float *sxr = reinterpret_cast<const float *>(recp(buf) + kRecSx);
+                sx0 = sxr[16 * quarter + col];
+                sx1 = sxr[16 * (4 + quarter) + col];
+            } else {
+                iv = *reinterpret_cast<const float4_t *>(&sm.inv[buf][4 * quarter]);
+                sx0 = sm.sx[buf][quarter][col];
+                sx1 = sm.sx[buf][4 + quarter][col];
+            }
 #pragma unroll
             for (int t = 0; t < TW; ++t) {
                 acc[t] = (d24[t] * iv) * dacc[t] + acc[t];
@@ -444,28 +530,56 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         };
 
         WTile wa[TW], wb[TW];
-        load_x(0);
-        load_w(0, wa);
-        load_w(min(1, nsb - 1), wb);
-        store_x(0);
-        __syncthreads();
-        // two super-blocks per iteration so that the register sets stay fixed;
-        // prefetches past the end reload the last super-block (unused)
-        for (int s = 0; s < nsb; s += 2) {
-            load_x(min(s + 1, nsb - 1));
-            compute(0, wa);
-            load_w(min(s + 2, nsb - 1), wa);
-            store_x(1);
-            __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's LDS writes
+        if constexpr (PRE) {
+            // the copies of record s+1 and the weights of s+2 are issued
+            // while s is computed; the wait that ends a step retires the
+            // copies and the previous step's weights (loads complete in issue
+            // order) and leaves this step's 3 TW weight loads in flight; the
+            // compiler, which counts only the weight loads, sees the same
+            issue_rec(0, 0);
+            load_w(0, wa);
+            load_w(min(1, nsb - 1), wb);
+            __builtin_amdgcn_s_waitcnt(0); // everything, the previous block's stores included
             __builtin_amdgcn_s_barrier();
-            if (s + 1 >= nsb)
-                break;
-            load_x(min(s + 2, nsb - 1));
-            compute(1, wb);
-            load_w(min(s + 3, nsb - 1), wb);
+            for (int s = 0; s < nsb; s += 2) {
+                issue_rec(min(s + 1, nsb - 1), 1);
+                compute(0, wa, s);
+                load_w(min(s + 2, nsb - 1), wa);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * TW));
+                __builtin_amdgcn_s_barrier();
+                if (s + 1 >= nsb)
+                    break;
+                issue_rec(min(s + 2, nsb - 1), 0);
+                compute(1, wb, s + 1);
+                load_w(min(s + 3, nsb - 1), wb);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * TW));
+                __builtin_amdgcn_s_barrier();
+            }
+        } else {
+            load_x(0);
+            load_w(0, wa);
+            load_w(min(1, nsb - 1), wb);
             store_x(0);
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_s_barrier();
+            __syncthreads();
+            // two super-blocks per iteration so that the register sets stay
+            // fixed; prefetches past the end reload the last super-block
+            // (unused)
+            for (int s = 0; s < nsb; s += 2) {
+                load_x(min(s + 1, nsb - 1));
+                compute(0, wa, s);
+                load_w(min(s + 2, nsb - 1), wa);
+                store_x(1);
+                __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's LDS writes
+                __builtin_amdgcn_s_barrier();
+                if (s + 1 >= nsb)
+                    break;
+                load_x(min(s + 2, nsb - 1));
+                compute(1, wb, s + 1);
+                load_w(min(s + 3, nsb - 1), wb);
+                store_x(0);
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                __builtin_amdgcn_s_barrier();
+            }
         }
 
         // y[b][row] for b = 4*quarter + i (PAIR: h[b][row] = silu(g) * u)
@@ -496,6 +610,128 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
     }
 }
 
+// prefix[e] = sum over entries e' < e of K/256 (records before entry e),
+// prefix[n] = all records; one workgroup.
+__global__ __launch_bounds__(1024) void gemv_prefix_kernel(const GemvEntry *__restrict__ table,
+                                                          int n, int *__restrict__ prefix)
+{
+    __shared__ int part[16];
+    __shared__ int carry;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0)
+        carry = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += 1024) {
+        const int e = base + tid;
+        const int v = e < n ? table[e].K >> 8 : 0;
+        int inc = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(inc, off, 64);
+            if (lane >= off)
+                inc += u;
+        }
+        if (lane == 63)
+            part[wave] = inc;
+        __syncthreads();
+        int before = carry;
+        for (int w = 0; w < wave; ++w)
+            before += part[w];
+        if (e < n)
+            prefix[e] = before + inc - v;
+        __syncthreads();
+        if (tid == 1023)
+            carry = before + inc;
+        __syncthreads();
+    }
+    if (tid == 0)
+        prefix[n] = carry;
+}
+
+// One record of pre-staged activations per workgroup: record r belongs to the
+// entry e with prefix[e] <= r < prefix[e + 1], super-block r - prefix[e]; the
+// 16 lanes of activation row sb = 4*wave + lane/16 stage it as the blocks of
+// the main kernel do.
+__global__ __launch_bounds__(NT) void gemv_stage_kernel(const GemvEntry *__restrict__ table, int n,
+                                                       const int *__restrict__ prefix, int B,
+                                                       uint8_t *__restrict__ recs, int rbytes)
+{
+    const int r = blockIdx.x;
+    int a = 0, z = n - 1;
+    while (a < z) { // last entry whose first record is at or before r
+        const int mid = (a + z + 1) >> 1;
+        if (prefix[mid] <= r)
+            a = mid;
+        else
+            z = mid - 1;
+    }
+    const GemvEntry E = table[a];
+    const int s = r - prefix[a];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sb = 4 * wave + (lane >> 4), sc_ = lane & 15;
+    const int sj = sc_ >> 1, sq0 = 2 * (sc_ & 1);
+    const bool stager = sb < B;
+    float4_t xr[4];
+    if (stager) {
+        const float *xp = E.x + (size_t)sb * E.K + 256 * s + 16 * sc_;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xr[i] = *reinterpret_cast<const float4_t *>(xp + 4 * i);
+    }
+    uint8_t *rec = recs + (size_t)r * (size_t)rbytes;
+    uint64_t eb;
+    float sx, inv;
+    stage_slice(xr, stager, lane, eb, sx, inv, [&](int h, const uint4 &hv, const uint4 &lv) {
+        uint8_t *d = rec + kRecHi + ((sj * 4 + sq0 + h) * B + sb) * 16;
+        *reinterpret_cast<uint4 *>(d) = hv;
+        *reinterpret_cast<uint4 *>(d + 512 * B) = lv;
+    });
+    if (lane == 0)
+        reinterpret_cast<uint64_t *>(rec)[wave] = eb;
+    if (!stager)
+        return;
+    if ((sc_ & 1) == 0)
+        reinterpret_cast<float *>(rec + kRecSx)[16 * sj + sb] = sx;
+    if (sc_ == 0)
+        reinterpret_cast<float *>(rec + kRecInv)[sb] = inv;
+}
+
+long long gemv_mfma_prestaged_bytes(int64_t n, long long records, int B)
+{
+    return (long long)gemv_prestaged_records_offset(n) + records * (long long)rec_bytes(B);
+}
+
+hipError_t launch_gemv_mfma_prestaged(const GemvEntry *table_dev, int n, long long total_bytes,
+                                      long long blocks2, long long blocks3, long long records,
+                                      int B, void *ws, hipStream_t s)
+{
+    int *prefix = static_cast<int *>(ws);
+    uint8_t *recs = static_cast<uint8_t *>(ws) + gemv_prestaged_records_offset(n);
+    const int rb = rec_bytes(B);
+    hipLaunchKernelGGL(gemv_prefix_kernel, dim3(1), dim3(1024), 0, s, table_dev, n, prefix);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    hipLaunchKernelGGL(gemv_stage_kernel, dim3((unsigned)records), dim3(NT), 0, s, table_dev, n,
+                       (const int *)prefix, B, recs, rb);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int cus = device_cus();
+    const GemvEntry none{};
+    if (blocks3 >= 2LL * cus) {
+        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 3, true>), dim3((unsigned)(2 * cus)),
+                           dim3(NT), 0, s, table_dev, none, n, total_bytes, B,
+                           (const uint8_t *)nullptr, (const uint8_t *)recs, (const int *)prefix, rb);
+    } else {
+        const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
+        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2, true>), dim3((unsigned)grid), dim3(NT),
+                           0, s, table_dev, none, n, total_bytes, B, (const uint8_t *)nullptr,
+                           (const uint8_t *)recs, (const int *)prefix, rb);
+    }
+    return hipGetLastError();
+}
+
 long long gemv_mfma_blocks(int64_t M, int tiles)
 {
     const int rb = rows_per_block(tiles);
@@ -512,11 +748,13 @@ hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0
     const int cus = device_cus();
     if (blocks3 >= 2LL * cus) {
         hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 3>), dim3((unsigned)(2 * cus)), dim3(NT), 0,
-                           s, table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr);
+                           s, table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr,
+                           (const uint8_t *)nullptr, (const int *)nullptr, 0);
     } else {
         const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
         hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2>), dim3((unsigned)grid), dim3(NT), 0, s,
-                           table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr);
+                           table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr,
+                           (const uint8_t *)nullptr, (const int *)nullptr, 0);
     }
     return hipGetLastError();
 }
@@ -530,7 +768,8 @@ hipError_t launch_gemv_swiglu_mfma(const void *w_gate, const void *w_up, const f
     const int cus = device_cus();
     const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
     hipLaunchKernelGGL((gemv_q4k_mfma_kernel<true, 2>), dim3((unsigned)grid), dim3(NT), 0, s,
-                       nullptr, e, 1, total, B, (const uint8_t *)w_up);
+                       nullptr, e, 1, total, B, (const uint8_t *)w_up, (const uint8_t *)nullptr,
+                       (const int *)nullptr, 0);
     return hipGetLastError();
 }
 

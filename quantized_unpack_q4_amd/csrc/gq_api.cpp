@@ -301,6 +301,78 @@ gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, in
                                              (int)B, (hipStream_t)stream));
 }
 
+// Table checks shared by the batched multi-product forms: header, B, every
+// entry within the matrix-core path's limits; block and record counts.
+static gq_status batched_table(const char *fn, const void *table, int64_t B, TableHeader &h,
+                               long long &blocks2, long long &blocks3, long long &records)
+{
+    if (!table)
+        return fail(GQ_EINVAL, "%s: table is NULL", fn);
+    memcpy(&h, table, sizeof h);
+    if (h.magic != kTableMagic || h.version != kTableVersion || h.n < 1)
+        return fail(GQ_EINVAL, "%s: table was not written by gq_gemv_q4k_multi_plan", fn);
+    if (B < 1 || B > GQ_GEMV_MAX_BATCH)
+        return fail(GQ_EINVAL, "%s: B = %lld is outside [1, %d]", fn, (long long)B,
+                    GQ_GEMV_MAX_BATCH);
+    const gq::GemvEntry *ent =
+        reinterpret_cast<const gq::GemvEntry *>((const uint8_t *)table + sizeof h);
+    blocks2 = blocks3 = records = 0;
+    for (int64_t i = 0; i < h.n; ++i) {
+        gq::GemvEntry e;
+        memcpy(&e, &ent[i], sizeof e);
+        if (B >= 2 && !gemv_mfma_fits(e.M, e.K, B))
+            return fail(GQ_ESHAPE, "%s: entry %lld (M = %d, K = %d) is too large for batch %lld",
+                        fn, (long long)i, e.M, e.K, (long long)B);
+        blocks2 += gq::gemv_mfma_blocks(e.M, 2);
+        blocks3 += gq::gemv_mfma_blocks(e.M, 3);
+        records += e.K / 256;
+    }
+    return GQ_OK;
+}
+
+size_t gq_gemv_q4k_multi_batched_ws_bytes(const void *table, int64_t B)
+{
+    char saved[sizeof g_err];
+    memcpy(saved, g_err, sizeof g_err);
+    TableHeader h;
+    long long b2 = 0, b3 = 0, recs = 0;
+    const gq_status st = batched_table("gq_gemv_q4k_multi_batched_ws_bytes", table, B, h, b2, b3,
+                                       recs);
+    memcpy(g_err, saved, sizeof g_err);
+    if (st != GQ_OK)
+        return 0;
+    if (B == 1)
+        return 1; // no workspace used; 1 so that 0 keeps meaning "invalid"
+    return (size_t)gq::gemv_mfma_prestaged_bytes(h.n, recs, (int)B);
+}
+
+gq_status gq_gemv_q4k_multi_batched_ws(const void *table, const void *table_dev, int64_t B,
+                                       void *ws, size_t ws_bytes, void *stream)
+{
+    static const char fn[] = "gq_gemv_q4k_multi_batched_ws";
+    TableHeader h;
+    long long blocks2 = 0, blocks3 = 0, records = 0;
+    GQ_TRY(batched_table(fn, table, B, h, blocks2, blocks3, records));
+    GQ_TRY(check_ptr(fn, "table_dev", table_dev));
+    if (B == 1)
+        return gq_gemv_q4k_multi(table, table_dev, stream);
+    const size_t need = (size_t)gq::gemv_mfma_prestaged_bytes(h.n, records, (int)B);
+    if (!ws)
+        return fail(GQ_EWORKSPACE, "%s: ws is NULL (needs %zu bytes)", fn, need);
+    if (!aligned16(ws))
+        return fail(GQ_EALIGN, "%s: ws (%p) is not 16-byte aligned", fn, ws);
+    if (ws_bytes < need)
+        return fail(GQ_EWORKSPACE, "%s: ws_bytes = %zu is below the required %zu", fn, ws_bytes,
+                    need);
+    if (records > ((long long)1 << 31) - 1)
+        return fail(GQ_ESHAPE, "%s: %lld super-blocks in the table exceed 2^31", fn, records);
+    const gq::GemvEntry *dev = reinterpret_cast<const gq::GemvEntry *>(
+        (const uint8_t *)table_dev + sizeof(TableHeader));
+    return launched(fn, gq::launch_gemv_mfma_prestaged(dev, (int)h.n, h.total_bytes, blocks2,
+                                                       blocks3, records, (int)B, ws,
+                                                       (hipStream_t)stream));
+}
+
 static gq_status gemm_common(const char *fn, const void *w, const uint16_t *x, uint16_t *y,
                              int64_t M, int64_t K, int64_t N, int64_t tile_rows, void *stream)
 {

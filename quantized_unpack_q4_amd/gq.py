@@ -24,7 +24,8 @@ MAX_BATCH = 16
 
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
-    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_swiglu", "gq_gemv_q4k_swiglu_batched", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_kgroups", "gq_gemm_q4k_splitk",
+    "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_multi_batched_ws",
+    "gq_gemv_q4k_multi_batched_ws_bytes", "gq_gemv_q4k_swiglu", "gq_gemv_q4k_swiglu_batched", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_kgroups", "gq_gemm_q4k_splitk",
     "gq_gemm_q4k_splitk_workspace_bytes", "gq_gemm_q4k_splitk_static",
     "gq_gemm_q4k_splitk_static_max_bytes",
     "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.gq_gemm_q8_0.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.gq_gemm_q4k_tiles.restype = st
         L.gq_gemm_q4k_tiles.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
+        L.gq_gemv_q4k_multi_batched_ws.restype = st
+        L.gq_gemv_q4k_multi_batched_ws.argtypes = [vp, vp, i64, vp, sz, vp]
+        L.gq_gemv_q4k_multi_batched_ws_bytes.restype = sz
+        L.gq_gemv_q4k_multi_batched_ws_bytes.argtypes = [vp, i64]
         L.gq_gemv_q4k_swiglu_batched.restype = st
         L.gq_gemv_q4k_swiglu_batched.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         L.gq_gemm_q4k_kgroups.restype = st
@@ -185,7 +190,7 @@ class GemvTable:
     table is used.
     """
 
-    def __init__(self, items, batch=1):
+    def __init__(self, items, batch=1, prestaged=False):
         import torch
         n = len(items)
         arr = (GemvDesc * n)()
@@ -204,12 +209,32 @@ class GemvTable:
         self.items = items
         self.n = n
         self.batch = batch
+        # prestaged: batch 2-16 with the activations staged once per product
+        # into a workspace owned by the table (gq_gemv_q4k_multi_batched_ws)
+        self.ws = None
+        if prestaged and batch >= 2:
+            nws = gq_gemv_q4k_multi_batched_ws_bytes(self.host, batch)
+            if nws == 0:
+                raise ValueError("table not valid at batch %d" % batch)
+            self.ws = torch.empty(nws, dtype=torch.uint8, device=items[0][0].device)
 
     def run(self, stream=None):
         if self.batch == 1:
             gq_gemv_q4k_multi(self.host, self.dev, stream)
+        elif self.ws is not None:
+            gq_gemv_q4k_multi_batched_ws(self.host, self.dev, self.batch, self.ws,
+                                         self.ws.numel(), stream)
         else:
             gq_gemv_q4k_multi_batched(self.host, self.dev, self.batch, stream)
+
+
+def gq_gemv_q4k_multi_batched_ws_bytes(table, B) -> int:
+    return lib().gq_gemv_q4k_multi_batched_ws_bytes(table, B)
+
+
+def gq_gemv_q4k_multi_batched_ws(table, table_dev, B, ws, ws_bytes, stream=None):
+    _check(lib().gq_gemv_q4k_multi_batched_ws(table, _ptr(table_dev), B, _ptr(ws), ws_bytes,
+                                              _stream(stream)))
 
 
 def gq_gemm_q4k(w, x, y, M, K, N, stream=None):

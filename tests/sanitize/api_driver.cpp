@@ -75,6 +75,13 @@ int main()
     LAUNCHED(gq_gemv_q4k_multi(table.data(), p, nullptr));
     LAUNCHED(gq_gemv_q4k_multi_batched(table.data(), p, 4, nullptr));
     REFUSED(gq_gemv_q4k_multi_batched(table.data(), p, 17, nullptr), GQ_EINVAL);
+    {
+        const size_t nws = gq_gemv_q4k_multi_batched_ws_bytes(table.data(), 4);
+        CHECK(nws > 0 && gq_gemv_q4k_multi_batched_ws_bytes(table.data(), 17) == 0);
+        LAUNCHED(gq_gemv_q4k_multi_batched_ws(table.data(), p, 4, p, nws, nullptr));
+        REFUSED(gq_gemv_q4k_multi_batched_ws(table.data(), p, 4, p, nws - 1, nullptr), GQ_EWORKSPACE);
+        REFUSED(gq_gemv_q4k_multi_batched_ws(table.data(), p, 4, nullptr, nws, nullptr), GQ_EWORKSPACE);
+    }
     REFUSED(gq_gemv_q4k_multi_plan(d.data(), 5, table.data(), tb - 1), GQ_EWORKSPACE);
     d[2].K = 16640; // above the one-launch limit
     REFUSED(gq_gemv_q4k_multi_plan(d.data(), 5, table.data(), tb), GQ_ESHAPE);

@@ -283,6 +283,20 @@ def test_multi_plan_checks_and_layout(L):
     assert L.gq_status_str(f(None, FAKE, 4, None)).decode() == "GQ_EINVAL"
     assert L.gq_status_str(f(table, None, 4, None)).decode() == "GQ_EINVAL"
     assert L.gq_status_str(f(table, MISALIGNED, 4, None)).decode() == "GQ_EALIGN"
+    # the pre-staged form: workspace size from the table, refusals on the host
+    g, gb = L.gq_gemv_q4k_multi_batched_ws, L.gq_gemv_q4k_multi_batched_ws_bytes
+    need4 = gb(table, 4)
+    assert need4 > 0 and gb(table, 16) > need4 and gb(table, 1) == 1
+    assert gb(table, 17) == 0 and gb(bad, 4) == 0 and gb(None, 4) == 0
+    for B in (0, 17):
+        assert L.gq_status_str(g(table, FAKE, B, FAKE, need4, None)).decode() == "GQ_EINVAL"
+    assert L.gq_status_str(g(bad, FAKE, 4, FAKE, need4, None)).decode() == "GQ_EINVAL"
+    assert L.gq_status_str(g(table, None, 4, FAKE, need4, None)).decode() == "GQ_EINVAL"
+    s, m = status_and_msg(L, g(table, FAKE, 4, None, need4, None))
+    assert s == "GQ_EWORKSPACE" and "ws is NULL" in m
+    s, m = status_and_msg(L, g(table, FAKE, 4, FAKE, need4 - 1, None))
+    assert s == "GQ_EWORKSPACE" and "below the required" in m
+    assert L.gq_status_str(g(table, FAKE, 4, MISALIGNED, need4, None)).decode() == "GQ_EALIGN"
 
 
 def test_probe_library_loads_and_refuses_bad_arguments():

@@ -115,6 +115,15 @@ def test_q4k_batched(B):
     t.run()
     _compare(host(y1), w, xs, M, K, oracle.Q4_K, "mfma", "batched table B=%d" % B)
     _compare(host(y2), w2, xs2, M2, K2, oracle.Q4_K, "mfma", "batched table B=%d K=%d" % (B, K2))
+    # the same table with the activations pre-staged into a workspace (the
+    # exact path then reads the binary32 activations from global memory)
+    z1 = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
+    z2 = torch.full((B, M2), float("nan"), dtype=torch.float32, device="cuda")
+    tp = gq.GemvTable([(dev(w), dev(x), z1, M, K), (dev(w2), dev(x2), z2, M2, K2)], batch=B,
+                      prestaged=True)
+    tp.run()
+    assert np.array_equal(host(z1).view(np.uint32), host(y1).view(np.uint32))
+    assert np.array_equal(host(z2).view(np.uint32), host(y2).view(np.uint32))
     say("  worst err/S", w1)
 
 

@@ -83,3 +83,28 @@ def test_decode_stack_as_timed(stack, B):
         worst = max(worst, within(yg[:, rows], yr, S, TOL, "product %d (%s) B=%d" % (t, name, B)))
     say("  max err/S", worst)
     del items
+
+
+@pytest.mark.parametrize("B", [4, 16])
+def test_decode_stack_prestaged(stack, B):
+    """The same stack with the activations staged once per product into a
+    workspace (gq_gemv_q4k_multi_batched_ws): every output bit-identical to
+    the per-block staging, which the test above checks against the oracle;
+    the workspace starts as all-ones bytes (NaN as binary32)."""
+    torch = torch_cuda()
+    say("decode stack prestaged batch", B)
+    items, items2 = [], []
+    for name, M, K, t, wd, rows, wrows in stack:
+        x = torch.from_numpy(synth.activations_f32(WORKLOAD, 100 * t + B, B, K)).cuda()
+        items.append((wd, x, torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda"), M, K))
+        items2.append((wd, x, torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda"), M, K))
+    tab = gq.GemvTable(items, batch=B)
+    tab2 = gq.GemvTable(items2, batch=B, prestaged=True)
+    tab2.ws.fill_(255)
+    tab.run()
+    tab2.run()
+    for (name, M, K, t, wd, rows, wrows), a, b in zip(stack, items, items2):
+        ya, yb = host(a[2]), host(b[2])
+        assert np.isfinite(yb).all(), "product %d (%s) B=%d: outputs not written" % (t, name, B)
+        assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), (t, name, B)
+    del items, items2, tab, tab2
