@@ -513,7 +513,15 @@ def main():
                 "ms_per_step": round(s * 1e3, 4),
                 "weight_GB/s": round(stack.weight_bytes / s / 1e9, 1),
                 "TFLOP/s": round(flops / s / 1e12, 2)}
-            del itB, tabB
+            # the same with the activations staged once per product into a
+            # workspace (gq_gemv_q4k_multi_batched_ws: three launches)
+            tabP = gq.GemvTable(itB, batch=B, prestaged=True)
+            s = event_time(torch, stream, lambda: tabP.run(stream), reps=max(5, args.steps // 2))
+            extra["stack_b%d_prestaged" % B] = {
+                "ms_per_step": round(s * 1e3, 4),
+                "weight_GB/s": round(stack.weight_bytes / s / 1e9, 1),
+                "workspace_bytes": int(tabP.ws.numel())}
+            del itB, tabB, tabP
         # single decode matrices: hot (one matrix again and again) and rotated
         for name, M, K in (("q", 4096, 4096), ("gate", 14336, 4096)):
             mats = [m for m in stack.mats if m[0] == name or (name == "q" and m[0] == "o")]
