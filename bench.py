@@ -524,15 +524,21 @@ def main():
             del itB, tabB, tabP
         # single decode matrices: hot (one matrix again and again) and rotated
         for name, M, K in (("q", 4096, 4096), ("gate", 14336, 4096)):
-            mats = [m for m in stack.mats if m[0] == name or (name == "q" and m[0] == "o")]
+            mats = [m[4] for m in stack.mats if m[0] == name or (name == "q" and m[0] == "o")]
+            # at least 1 GiB of distinct weights, past the 256 MB memory-side
+            # cache (the stack's 64 q/o matrices are 604 MB: add copies)
+            extra_copies = []
+            while (len(mats) + len(extra_copies)) * q4k_bytes(M, K) < (1 << 30):
+                extra_copies.append(mats[len(extra_copies) % len(mats)].clone())
+            mats = mats + extra_copies
             x = torch.from_numpy(synth.activations_f32(1, M, 1, K)).cuda()
             y = torch.empty((1, M), dtype=torch.float32, device="cuda")
-            w0 = mats[0][4]
+            w0 = mats[0]
             hot = event_time(torch, stream, lambda: gq.gq_gemv_q4k(w0, x, y, M, K, 1, stream))
             it = {"i": 0}
 
             def rot():
-                w = mats[it["i"] % len(mats)][4]
+                w = mats[it["i"] % len(mats)]
                 it["i"] += 1
                 gq.gq_gemv_q4k(w, x, y, M, K, 1, stream)
             rotated = event_time(torch, stream, rot, reps=len(mats), warmup=len(mats))
@@ -541,6 +547,7 @@ def main():
                 "rotated_us": round(rotated * 1e6, 2),
                 "rotated_GB/s": round(q4k_bytes(M, K) / rotated / 1e9, 1),
                 "rotated_over_MB": round(len(mats) * q4k_bytes(M, K) / 1e6, 1)}
+            del mats, extra_copies
         # a layer's gate and up products with the SwiGLU epilogue in one launch
         # (gq_gemv_q4k_swiglu), rotated over the 32 layers' pairs, beside the
         # same two products as two launches
@@ -694,6 +701,10 @@ def main():
         wg = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 0, E * I, H)).cuda()
         wu = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 1, E * I, H)).cuda()
         wd = torch.from_numpy(synth.q4k_blocks(MOE_WORKLOAD, 2, E * H, I)).cuda()
+        # the 226 MB of expert weights fit the 256 MB memory-side cache: the
+        # layer is timed rotating over 4 copies (906 MB), and on one copy
+        # again and again (hot) beside it
+        wcopies = [(wg, wu, wd)] + [(wg.clone(), wu.clone(), wd.clone()) for _ in range(3)]
         moe, moe_in = {}, {}
         wbytes = 3 * E * q4k_bytes(I, H)
         for T in (256, 2048):
@@ -704,20 +715,35 @@ def main():
             need = gq.gq_moe_workspace_bytes(T, H, I, E, k)
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
             out = torch.empty((T, H), dtype=torch.float16, device="cuda")
-            s = event_time(torch, stream, lambda: gq.gq_moe_gemm_q4k(
+            it = {"i": 0}
+
+            def moe_rot():
+                cg, cu, cd = wcopies[it["i"] % len(wcopies)]
+                it["i"] += 1
+                gq.gq_moe_gemm_q4k(cg, cu, cd, x16, ids_d, wts_d, out, T, H, I, E, k, ws, need,
+                                   stream)
+            s = event_time(torch, stream, moe_rot, reps=24, warmup=8)
+            hot = event_time(torch, stream, lambda: gq.gq_moe_gemm_q4k(
                 wg, wu, wd, x16, ids_d, wts_d, out, T, H, I, E, k, ws, need, stream))
             flops = 2.0 * T * k * 3 * H * I
             moe["T%d" % T] = {"us": round(s * 1e6, 1), "TFLOP/s": round(flops / s / 1e12, 1),
-                              "weight_GB/s": round(wbytes / s / 1e9, 1)}
+                              "weight_GB/s": round(wbytes / s / 1e9, 1),
+                              "rotated_over_MB": round(len(wcopies) * wbytes / 1e6, 1),
+                              "hot_us": round(hot * 1e6, 1)}
             # the routing step itself (gq_moe_route), timed apart
             rid = torch.empty((T, k), dtype=torch.int32, device="cuda")
             rwt = torch.empty((T, k), dtype=torch.float32, device="cuda")
             s = event_time(torch, stream, lambda: gq.gq_moe_route(lg, rid, rwt, T, E, k, 0, stream))
             moe["T%d" % T]["route_us"] = round(s * 1e6, 2)
             # the same layer with the weights on the experts' inputs (Llama 4 form)
-            s = event_time(torch, stream, lambda: gq.gq_moe_gemm_q4k(
-                wg, wu, wd, x16, ids_d, wts_d, out, T, H, I, E, k, ws, need, stream,
-                input_weighted=True))
+            it["i"] = 0
+
+            def moe_rot_iw():
+                cg, cu, cd = wcopies[it["i"] % len(wcopies)]
+                it["i"] += 1
+                gq.gq_moe_gemm_q4k(cg, cu, cd, x16, ids_d, wts_d, out, T, H, I, E, k, ws, need,
+                                   stream, input_weighted=True)
+            s = event_time(torch, stream, moe_rot_iw, reps=24, warmup=8)
             moe["T%d" % T]["input_weighted_us"] = round(s * 1e6, 1)
             moe_in[T] = (x16, ids_d, wts_d, ws, need, out)
         extra["moe_olmoe"] = moe
@@ -745,7 +771,7 @@ def main():
                              "TFLOP/s": round(2.0 * R * 3 * H * I / s / 1e12, 1),
                              "weight_GB/s": round(3 * (E // 8) * q4k_bytes(I, H) / s / 1e9, 1)}
         extra["moe_olmoe_ep8_shard"] = ep
-        del wg, wu, wd
+        del wg, wu, wd, wcopies
         # the same layer over Q8_0 expert stacks
         wg = torch.from_numpy(synth.q8_0_blocks(MOE_WORKLOAD, 0, E * I, H)).cuda()
         wu = torch.from_numpy(synth.q8_0_blocks(MOE_WORKLOAD, 1, E * I, H)).cuda()
