@@ -216,7 +216,10 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // PRE: the activations come pre-staged (one record per entry and super-block
 // in ws, entry e's first record at prefix[e], rbytes each) and are copied into
 // LDS by direct-to-LDS loads instead of being staged by every block.
-template <bool PAIR, int TW, bool PRE = false>
+// NS weight register sets: 2 (the weights of s+2 are issued once s is
+// computed) or 3 (issued before s is computed, into the set s-1 used, so each
+// weight load has two steps to land).
+template <bool PAIR, int TW, bool PRE = false, int NS = 2>
 __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *__restrict__ table,
                                                                GemvEntry inline0, int n,
                                                                long long total, int B,
@@ -230,6 +233,9 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
     static_assert(!PAIR || TW == 2, "pairs take two tiles per wave");
     static_assert(!PRE || !PAIR, "pre-staged activations: tables of plain products");
     static_assert(2 * kRecMax <= (int)sizeof(Smem), "two records fit the staging area");
+    static_assert(NS == 2 || NS == 3, "two or three weight register sets");
+    static_assert(NS == 2 || !PRE || 3 * kRecMax <= (int)sizeof(Smem),
+                  "three records fit the staging area");
     constexpr int RB = rows_per_block(TW);  // weight rows per block
     constexpr int RBO = PAIR ? RB / 2 : RB; // output rows per block
     __shared__ Smem sm;
@@ -530,7 +536,59 @@ __global__ __launch_bounds__(NT, 2) void gemv_q4k_mfma_kernel(const GemvEntry *_
         };
 
         WTile wa[TW], wb[TW];
-        if constexpr (PRE) {
+        if constexpr (PRE && NS == 3) {
+            // records in a ring of three; the wait that ends a step retires
+            // the copies and the weights of s+1 and leaves the weights of
+            // s+2 in flight (the compiler, counting only weight loads, sees
+            // the same)
+            WTile wc[TW];
+            issue_rec(0, 0);
+            load_w(0, wa);
+            load_w(min(1, nsb - 1), wb);
+            __builtin_amdgcn_s_waitcnt(0); // everything, the previous block's stores included
+            __builtin_amdgcn_s_barrier();
+            auto step3 = [&](int s, int S, const WTile(&cur)[TW], WTile(&far)[TW]) -> bool {
+                issue_rec(min(s + 1, nsb - 1), S == 2 ? 0 : S + 1);
+                load_w(min(s + 2, nsb - 1), far);
+                compute(S, cur, s);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * TW));
+                __builtin_amdgcn_s_barrier();
+                return s + 1 < nsb;
+            };
+            for (int s = 0;; s += 3) {
+                if (!step3(s, 0, wa, wc))
+                    break;
+                if (!step3(s + 1, 1, wb, wa))
+                    break;
+                if (!step3(s + 2, 2, wc, wb))
+                    break;
+            }
+        } else if constexpr (NS == 3) {
+            WTile wc[TW];
+            load_x(0);
+            load_w(0, wa);
+            load_w(min(1, nsb - 1), wb);
+            store_x(0);
+            __syncthreads();
+            auto step3 = [&](int s, const WTile(&cur)[TW], WTile(&far)[TW]) -> bool {
+                const int buf = s & 1;
+                load_x(min(s + 1, nsb - 1));
+                load_w(min(s + 2, nsb - 1), far);
+                compute(buf, cur, s);
+                store_x(buf ^ 1);
+                __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's LDS writes
+                __builtin_amdgcn_s_barrier();
+                return s + 1 < nsb;
+            };
+            for (int s = 0;; s += 3) {
+                if (!step3(s, wa, wc))
+                    break;
+                if (!step3(s + 1, wb, wa))
+                    break;
+                if (!step3(s + 2, wc, wb))
+                    break;
+            }
+        } else if constexpr (PRE) {
             // the copies of record s+1 and the weights of s+2 are issued
             // while s is computed; the wait that ends a step retires the
             // copies and the previous step's weights (loads complete in issue
@@ -717,18 +775,17 @@ hipError_t launch_gemv_mfma_prestaged(const GemvEntry *table_dev, int n, long lo
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
+    // 128-row blocks with three weight sets: the records are staged once per
+    // product, so larger blocks save nothing, and the third set keeps more
+    // weight loads in flight (decode stack at batch 4 1155 -> 1108 us, at
+    // batch 16 1375 -> 1313 us, against 192-row blocks with two sets)
+    (void)blocks3;
     const int cus = device_cus();
     const GemvEntry none{};
-    if (blocks3 >= 2LL * cus) {
-        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 3, true>), dim3((unsigned)(2 * cus)),
-                           dim3(NT), 0, s, table_dev, none, n, total_bytes, B,
-                           (const uint8_t *)nullptr, (const uint8_t *)recs, (const int *)prefix, rb);
-    } else {
-        const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
-        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2, true>), dim3((unsigned)grid), dim3(NT),
-                           0, s, table_dev, none, n, total_bytes, B, (const uint8_t *)nullptr,
-                           (const uint8_t *)recs, (const int *)prefix, rb);
-    }
+    const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
+    hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2, true, 3>), dim3((unsigned)grid), dim3(NT),
+                       0, s, table_dev, none, n, total_bytes, B, (const uint8_t *)nullptr,
+                       (const uint8_t *)recs, (const int *)prefix, rb);
     return hipGetLastError();
 }
 
@@ -752,9 +809,10 @@ hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0
                            (const uint8_t *)nullptr, (const int *)nullptr, 0);
     } else {
         const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
-        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2>), dim3((unsigned)grid), dim3(NT), 0, s,
-                           table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr,
-                           (const uint8_t *)nullptr, (const int *)nullptr, 0);
+        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2, false, 3>), dim3((unsigned)grid),
+                           dim3(NT), 0, s, table_dev, inline0, n, total_bytes, B,
+                           (const uint8_t *)nullptr, (const uint8_t *)nullptr, (const int *)nullptr,
+                           0);
     }
     return hipGetLastError();
 }
@@ -767,9 +825,9 @@ hipError_t launch_gemv_swiglu_mfma(const void *w_gate, const void *w_up, const f
     const long long blocks = (M + 63) / 64;
     const int cus = device_cus();
     const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
-    hipLaunchKernelGGL((gemv_q4k_mfma_kernel<true, 2>), dim3((unsigned)grid), dim3(NT), 0, s,
-                       nullptr, e, 1, total, B, (const uint8_t *)w_up, (const uint8_t *)nullptr,
-                       (const int *)nullptr, 0);
+    hipLaunchKernelGGL((gemv_q4k_mfma_kernel<true, 2, false, 3>), dim3((unsigned)grid), dim3(NT),
+                       0, s, nullptr, e, 1, total, B, (const uint8_t *)w_up,
+                       (const uint8_t *)nullptr, (const int *)nullptr, 0);
     return hipGetLastError();
 }
 
