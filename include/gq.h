@@ -205,11 +205,20 @@ gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, 
 
 /* The same product over Q8_0 weights (M rows of K/32 blocks):
  *   Y[n][r] = binary16( sum_k X[n][k] * w16[r][k] ),  w16 = binary16(d * q)
- * accumulated in binary32 (d * q is exact in binary32; one rounding to
- * binary16).  Requires K % 64 == 0 (the kernel takes two blocks per step;
- * GQ_ESHAPE otherwise), N <= 2^21. */
+ * accumulated in binary32 (d * q is exact; one rounding to binary16).
+ * Requires K % 64 == 0 (the small-tile kernel takes two blocks per step;
+ * GQ_ESHAPE otherwise), N <= 2^21.  With K % 256 == 0 and enough tiles the
+ * large-tile kernel runs it, as for gq_gemm_q4k. */
 gq_status gq_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                        int64_t N, void *stream);
+
+/* gq_gemm_q8_0 with the kernel family pinned, as gq_gemm_q4k_tiles pins it
+ * for Q4_K: tile_rows = 0 automatic, 64 the small-tile kernel (K % 64 == 0),
+ * 128 and 256 the large-tile kernel (K % 256 == 0 and N*K*2 < 2^31, else
+ * GQ_ESHAPE).  Same result and bound; the summation order differs between
+ * families.  GQ_EINVAL for any other tile_rows. */
+gq_status gq_gemm_q8_0_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                             int64_t N, int64_t tile_rows, void *stream);
 
 /* gq_gemm_q4k with the kernel family pinned instead of chosen from the shape:
  * tile_rows = 0 is the automatic choice of gq_gemm_q4k, 64 the small-tile

@@ -63,6 +63,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
 typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
 typedef __attribute__((address_space(1))) const u32x3 g_u32x3;
+typedef unsigned int u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef __attribute__((address_space(1))) const u32x4a4 g_u32x4a4;
+typedef __attribute__((address_space(1))) const unsigned int g_u32;
 
 __device__ __forceinline__ uint4 gload16(const uint8_t *p)
 {
@@ -84,6 +87,21 @@ __device__ __forceinline__ uint32_t deq2(uint32_t qa, int sela, uint32_t qb, int
     uint32_t r;
     asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
     return r;
+}
+
+// Four binary16 weights binary16(d * q) from four signed quant bytes of a
+// Q8_0 block (d its binary16 scale, in both halves of d2).  Each byte, offset
+// to u = q + 128, becomes the binary16 1024 + u (exponent bits 0x64 above the
+// byte), and subtracting 1152 leaves q exactly; one packed binary16 multiply
+// then rounds the exact product d * q once.
+__device__ __forceinline__ void deq4_q8(uint32_t q, h2_t d2, uint32_t &lo, uint32_t &hi)
+{
+    const uint32_t u = q ^ 0x80808080u;
+    const h2_t off = {(_Float16)1152.f, (_Float16)1152.f};
+    const h2_t a = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off;
+    const h2_t b = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off;
+    lo = __builtin_bit_cast(uint32_t, a * d2);
+    hi = __builtin_bit_cast(uint32_t, b * d2);
 }
 
 constexpr int KS = 64;  // weights per K step
@@ -134,7 +152,7 @@ struct BigParams {
 // 1 .. KG-1 hand their binary32 partial tiles to group 0 through LDS, which
 // adds them in group order (deterministic) and stores the tile.  The groups
 // step in lockstep (same number of steps, one barrier per step for all).
-template <int MODE, int NW, int FNT, int KG = 1>
+template <int MODE, int NW, int FNT, int KG = 1, bool Q8 = false>
 __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int nvalid, int e,
                                          int split, _Float16 *sX0, _Float16 *sX1)
 {
@@ -154,7 +172,10 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
     const int wave = wall % NWG; // wave within its K group
     const int r = lane & 31, h = lane >> 5;
     const int nsb = K >> 8;
-    const size_t rowb = (size_t)nsb * kQ4kBytes;
+    // bytes per 256 weights of a row: one Q4_K super-block or eight Q8_0 blocks
+    constexpr int kSbBytes = Q8 ? 8 * kQ80Bytes : kQ4kBytes;
+    constexpr int NWL = Q8 ? 4 : 2; // weight loads per lane and step
+    const size_t rowb = (size_t)nsb * kSbBytes;
     // split products: this workgroup's run of K starts at super-block sb0;
     // K groups: this group's run
     const int krun = MODE == kBigSplit ? K / p.splits : K / KG;
@@ -172,7 +193,7 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
         wbase += (size_t)e * p.expert_bytes;
     const bool wok = wr_want < M;
     const uint8_t *wrow =
-        wbase + (size_t)(wok ? wr_want : M - 1) * rowb + (size_t)sb0 * kQ4kBytes;
+        wbase + (size_t)(wok ? wr_want : M - 1) * rowb + (size_t)sb0 * kSbBytes;
 
     // activation copies: copy q of wave v fills LDS 16-byte units
     // [(NQ v + q) * 64, +64), i.e. row (NQ v + q) * 8 + lane / 8, slot lane % 8,
@@ -204,14 +225,31 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
 
     // packed weights of the steps ahead: slot = step & 3; step kt + 3 is
     // loaded during step kt and has until the end of step kt + 1 to land (the
-    // wait that ends each step leaves only the newest step's two loads in
+    // wait that ends each step leaves only the newest step's NWL loads in
     // flight).  Quant groups 0 and 1 need only the first 12 header bytes (d,
     // dmin and scale/min bytes 0-7); loading 16 would leave the fourth
     // register of the load dead, and the compiler may then reuse it while the
     // load is in flight, which costs a wait for every load issued before it
     // (the activation copies included).
     uint4 rh[4], rq[4];
+    uint32_t r8b[4], r8d[4]; // Q8_0: the 4-byte loads
     auto issue_w = [&](int kt, int slot, int g) {
+        if constexpr (Q8) {
+            // step kt is blocks 2kt and 2kt+1 (68 bytes from a 4-byte aligned
+            // start): lane half h takes bytes 16h .. 16h+19 (its 16 quants of
+            // the first block start at byte 2 + 16h), its 16 quants of the
+            // second block (bytes 36 + 16h ..) and the dword holding the scale
+            // it lacks (the second block's for h = 0, the first's for h = 1)
+            const uint8_t *st = wrow + (size_t)kt * (2 * kQ80Bytes);
+            const u32x4a4 a = *(g_u32x4a4 *)(st + 16 * h);
+            rh[slot] = make_uint4(a.x, a.y, a.z, a.w);
+            r8b[slot] = *(g_u32 *)(st + 16 + 16 * h);
+            const u32x4a4 c = *(g_u32x4a4 *)(st + 36 + 16 * h);
+            rq[slot] = make_uint4(c.x, c.y, c.z, c.w);
+            r8d[slot] = *(g_u32 *)(st + (h ? 0 : 32));
+            (void)g;
+            return;
+        }
         const uint8_t *blk = wrow + (size_t)(kt >> 2) * kQ4kBytes;
         if (g < 2) {
             const u32x3 v = *(g_u32x3 *)(blk);
@@ -223,6 +261,34 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
     };
     // A operands of one step from slot `slot`, quant group g
     auto dequant = [&](int slot, int g, half8_t(&dst)[4]) {
+        if constexpr (Q8) {
+            // sub-steps 0, 1: quants 16h .. 16h+15 of the first block; 2, 3:
+            // of the second block
+            const uint4 a = rh[slot], c = rq[slot];
+            const uint32_t b = r8b[slot], dd = r8d[slot];
+            // rows past M (read from row M - 1) get zero weights
+            const uint32_t d0 = wok ? (h ? (dd & 0xFFFFu) : (a.x & 0xFFFFu)) : 0u;
+            const uint32_t d1 = wok ? (h ? (b >> 16) : (dd >> 16)) : 0u;
+            const h2_t d0v = __builtin_bit_cast(h2_t, d0 | (d0 << 16));
+            const h2_t d1v = __builtin_bit_cast(h2_t, d1 | (d1 << 16));
+            const uint32_t q0[4] = {__builtin_amdgcn_alignbyte(a.y, a.x, 2),
+                                    __builtin_amdgcn_alignbyte(a.z, a.y, 2),
+                                    __builtin_amdgcn_alignbyte(a.w, a.z, 2),
+                                    __builtin_amdgcn_alignbyte(b, a.w, 2)};
+            const uint32_t q1[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                uint32_t w[4];
+                deq4_q8(q0[2 * v], d0v, w[0], w[1]);
+                deq4_q8(q0[2 * v + 1], d0v, w[2], w[3]);
+                dst[v] = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
+                deq4_q8(q1[2 * v], d1v, w[0], w[1]);
+                deq4_q8(q1[2 * v + 1], d1v, w[2], w[3]);
+                dst[2 + v] = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
+            }
+            (void)g;
+            return;
+        }
         const uint4 hd = rh[slot];
         uint32_t scl, ml, sch, mh;
         if (g < 2) {
@@ -296,7 +362,7 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
         const int n3 = kt + 3 < nk ? kt + 3 : nk - 1;
         read_b(buf, 0, bf0);
         // copies first: the wait that ends the step then leaves exactly this
-        // step's two weight loads in flight
+        // step's NWL weight loads in flight
         issue_x(n1, buf ^ 1);
         issue_w(n3, (S + 3) & 3, (S + 3) & 3);
         read_b(buf, 1, bf1);
@@ -307,10 +373,10 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
         read_b(buf, 3, bf1);
         mfma(cur[2], bf0);
         mfma(cur[3], bf1);
-        // schedule: the first sub-step's reads, the two weight loads, then
+        // schedule: the first sub-step's reads, the NWL weight loads, then
         // each matrix instruction followed by one LDS read and three VALU ops
         __builtin_amdgcn_sched_group_barrier(0x100, FN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, NWL, 0);
 #pragma unroll
         for (int u = 0; u < 4 * FN; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -318,12 +384,12 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
             __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
         }
         // this wave's copies for the next step and the weights of step kt+2
-        // have landed (loads complete in issue order; the two loads of step
+        // have landed (loads complete in issue order; the NWL loads of step
         // kt+3 stay in flight); after the barrier every wave's copies have.
         // The compiler counts only the weight loads, so by its count too the
         // weights of step kt+2 are in and it inserts no wait of its own
         // before their dequantization in the next step.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(NWL));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -331,11 +397,20 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
     // prologue: step 0's activations in LDS, A operands of step 0, packed
     // weights of step 1 in slot 1, step 2's on the way to slot 2
     half8_t a0[4], a1[4];
+    // (Q8_0: fenced so that each step's four loads stay together, since the
+    // wait below counts on step 2's being the newest; the compiler keeps the
+    // Q4_K loads in order by itself)
     issue_x(0, 0);
     issue_w(0, 0, 0);
+    if constexpr (Q8)
+        __builtin_amdgcn_sched_barrier(0);
     issue_w(1, 1, 1); // nk >= 4
+    if constexpr (Q8)
+        __builtin_amdgcn_sched_barrier(0);
     issue_w(2, 2, 2);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));
+    if constexpr (Q8)
+        __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(NWL));
     dequant(0, 0, a0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -450,7 +525,8 @@ __device__ __forceinline__ void big_tile(const BigParams &p, int m0, int n0, int
     }
 }
 
-template <int MODE, int NW>
+// Q8: Q8_0 weights (rows of K/32 34-byte blocks) instead of Q4_K
+template <int MODE, int NW, bool Q8 = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams p)
 {
     constexpr int BM = 32 * NW; // weight rows per tile (gate/up: gate + up rows)
@@ -476,7 +552,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
         m0 = m_t * BM;
         n0 = n_t * BN;
         nvalid = p.N - n0 < BN ? p.N - n0 : BN;
-        big_tile<MODE, NW, FN>(p, m0, n0, nvalid, e, split, sX0, sX1);
+        big_tile<MODE, NW, FN, 1, Q8>(p, m0, n0, nvalid, e, split, sX0, sX1);
     } else {
         // XCD-aware order: the hardware deals consecutive workgroups to the 8
         // XCDs in turn; XCD x takes token tiles x, x + 8, x + 16, ... each
@@ -496,9 +572,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
         m0 = (k % rt) * (MODE == kBigGateUp ? BM / 2 : BM);
         // the same for the whole workgroup
         if (__builtin_amdgcn_readfirstlane(nvalid) <= 64)
-            big_tile<MODE, NW, 2>(p, m0, n0, nvalid, e, split, sX0, sX1);
+            big_tile<MODE, NW, 2, 1, Q8>(p, m0, n0, nvalid, e, split, sX0, sX1);
         else
-            big_tile<MODE, NW, FN>(p, m0, n0, nvalid, e, split, sX0, sX1);
+            big_tile<MODE, NW, FN, 1, Q8>(p, m0, n0, nvalid, e, split, sX0, sX1);
     }
 }
 
@@ -574,7 +650,7 @@ bool gemm_big_fits(int64_t M, int64_t K, int64_t N)
 }
 
 hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int bm, hipStream_t s)
+                           int64_t N, int bm, bool q8, hipStream_t s)
 {
     if ((bm != 256 && bm != 128) || !gemm_big_fits(M, K, N))
         return hipErrorInvalidValue;
@@ -588,7 +664,13 @@ hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_
     p.tiles_m = (int)((M + bm - 1) / bm);
     p.tiles_total = (int)dense_tiles(M, N, bm);
     const int grid = (p.tiles_total + 7) / 8 * 8;
-    if (bm == 256)
+    if (q8 && bm == 256)
+        hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 8, true>), dim3((unsigned)grid),
+                           dim3(512), 0, s, p);
+    else if (q8)
+        hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 4, true>), dim3((unsigned)grid),
+                           dim3(256), 0, s, p);
+    else if (bm == 256)
         hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 8>), dim3((unsigned)grid), dim3(512), 0, s, p);
     else
         hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDense, 4>), dim3((unsigned)grid), dim3(256), 0, s, p);
@@ -776,11 +858,16 @@ hipError_t launch_moe_big(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.y = a.ws + a.off[4];
     p.M = (int)a.I;
     p.K = (int)a.H;
-    p.expert_bytes = a.I * (a.H / kQ4kWeights) * kQ4kBytes;
+    p.expert_bytes = a.q8_0 ? a.I * (a.H / kQ80Weights) * kQ80Bytes
+                            : a.I * (a.H / kQ4kWeights) * kQ4kBytes;
     // token tiles rounded up to a multiple of 8 for the XCD-aware order
     const unsigned ty = (unsigned)((max_tiles + 7) / 8 * 8);
-    hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigGateUp, 8>), dim3((unsigned)(a.I / 128), ty),
-                       dim3(512), 0, s, p);
+    if (a.q8_0)
+        hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigGateUp, 8, true>), dim3((unsigned)(a.I / 128), ty),
+                           dim3(512), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigGateUp, 8>), dim3((unsigned)(a.I / 128), ty),
+                           dim3(512), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -792,9 +879,14 @@ hipError_t launch_moe_big(const MoeArgs &a, int max_tiles, hipStream_t s)
     p.y = a.ws + a.off[5];
     p.M = (int)a.H;
     p.K = (int)a.I;
-    p.expert_bytes = a.H * (a.I / kQ4kWeights) * kQ4kBytes;
-    hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDown, 8>), dim3((unsigned)(a.H / 256), ty),
-                       dim3(512), 0, s, p);
+    p.expert_bytes = a.q8_0 ? a.H * (a.I / kQ80Weights) * kQ80Bytes
+                            : a.H * (a.I / kQ4kWeights) * kQ4kBytes;
+    if (a.q8_0)
+        hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDown, 8, true>), dim3((unsigned)(a.H / 256), ty),
+                           dim3(512), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_q4k_big_kernel<kBigDown, 8>), dim3((unsigned)(a.H / 256), ty),
+                           dim3(512), 0, s, p);
     return hipGetLastError();
 }
 

@@ -374,10 +374,13 @@ gq_status gq_gemv_q4k_multi_batched_ws(const void *table, const void *table_dev,
 }
 
 static gq_status gemm_common(const char *fn, const void *w, const uint16_t *x, uint16_t *y,
-                             int64_t M, int64_t K, int64_t N, int64_t tile_rows, void *stream)
+                             int64_t M, int64_t K, int64_t N, int64_t tile_rows, bool q8,
+                             void *stream)
 {
     GQ_TRY(check_dim(fn, "M", M, true));
-    GQ_TRY(check_k(fn, "K", K, 256));
+    // Q8_0: the small-tile kernel takes two blocks per step, the large tiles
+    // whole runs of 256 weights
+    GQ_TRY(check_k(fn, "K", K, q8 && (tile_rows == 0 || tile_rows == 64) ? 64 : 256));
     GQ_TRY(check_dim(fn, "N", N, true));
     if (N > ((int64_t)1 << 21))
         return fail(GQ_ESHAPE, "%s: N = %lld exceeds the supported maximum %lld", fn,
@@ -388,43 +391,43 @@ static gq_status gemm_common(const char *fn, const void *w, const uint16_t *x, u
     GQ_TRY(check_ptr(fn, "x", x));
     GQ_TRY(check_ptr(fn, "y", y));
     if (tile_rows == 0) {
-        // too few 256 x 256 tiles for the device: K groups where they are
-        // estimated fastest
-        const int kg = gq::gemm_kgroups_choice(M, K, N);
+        // too few 256 x 256 tiles for the device: K groups (Q4_K) where they
+        // are estimated fastest
+        const int kg = q8 ? 0 : gq::gemm_kgroups_choice(M, K, N);
         if (kg)
             return launched(fn, gq::launch_gemm_kgroups(w, x, y, M, K, N, kg, (hipStream_t)stream));
-        tile_rows = gq::gemm_big_choice(M, K, N);
+        tile_rows = K % 256 == 0 ? gq::gemm_big_choice(M, K, N) : 0;
     }
     if (tile_rows == 0 || tile_rows == 64)
-        return launched(fn, gq::launch_gemm_q4k(w, x, y, M, K, N, (hipStream_t)stream));
+        return launched(fn, q8 ? gq::launch_gemm_q8_0(w, x, y, M, K, N, (hipStream_t)stream)
+                               : gq::launch_gemm_q4k(w, x, y, M, K, N, (hipStream_t)stream));
     if (!gq::gemm_big_fits(M, K, N))
         return fail(GQ_ESHAPE, "%s: N*K = %lld is too large for the %lld-row tiles", fn,
                     (long long)(N * K), (long long)tile_rows);
-    return launched(fn, gq::launch_gemm_big(w, x, y, M, K, N, (int)tile_rows, (hipStream_t)stream));
+    return launched(fn, gq::launch_gemm_big(w, x, y, M, K, N, (int)tile_rows, q8,
+                                            (hipStream_t)stream));
 }
 
 gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                       int64_t N, void *stream)
 {
-    return gemm_common("gq_gemm_q4k", w, x, y, M, K, N, 0, stream);
+    return gemm_common("gq_gemm_q4k", w, x, y, M, K, N, 0, false, stream);
 }
 
 gq_status gq_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                        int64_t N, void *stream)
 {
-    static const char fn[] = "gq_gemm_q8_0";
-    GQ_TRY(check_dim(fn, "M", M, true));
-    GQ_TRY(check_k(fn, "K", K, 64));
-    GQ_TRY(check_dim(fn, "N", N, true));
-    if (N > ((int64_t)1 << 21))
-        return fail(GQ_ESHAPE, "%s: N = %lld exceeds the supported maximum %lld", fn,
-                    (long long)N, (long long)1 << 21);
-    if (M == 0 || N == 0)
-        return GQ_OK;
-    GQ_TRY(check_ptr(fn, "w", w));
-    GQ_TRY(check_ptr(fn, "x", x));
-    GQ_TRY(check_ptr(fn, "y", y));
-    return launched(fn, gq::launch_gemm_q8_0(w, x, y, M, K, N, (hipStream_t)stream));
+    return gemm_common("gq_gemm_q8_0", w, x, y, M, K, N, 0, true, stream);
+}
+
+gq_status gq_gemm_q8_0_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                             int64_t N, int64_t tile_rows, void *stream)
+{
+    static const char fn[] = "gq_gemm_q8_0_tiles";
+    if (tile_rows != 0 && tile_rows != 64 && tile_rows != 128 && tile_rows != 256)
+        return fail(GQ_EINVAL, "%s: tile_rows = %lld must be 0, 64, 128 or 256", fn,
+                    (long long)tile_rows);
+    return gemm_common(fn, w, x, y, M, K, N, tile_rows, true, stream);
 }
 
 gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
@@ -434,7 +437,7 @@ gq_status gq_gemm_q4k_tiles(const void *w, const uint16_t *x, uint16_t *y, int64
     if (tile_rows != 0 && tile_rows != 64 && tile_rows != 128 && tile_rows != 256)
         return fail(GQ_EINVAL, "%s: tile_rows = %lld must be 0, 64, 128 or 256", fn,
                     (long long)tile_rows);
-    return gemm_common(fn, w, x, y, M, K, N, tile_rows, stream);
+    return gemm_common(fn, w, x, y, M, K, N, tile_rows, false, stream);
 }
 
 gq_status gq_gemm_q4k_kgroups(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,

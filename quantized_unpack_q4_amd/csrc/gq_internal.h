@@ -88,7 +88,7 @@ hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_
 hipError_t launch_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                             int64_t N, hipStream_t s);
 // Large-tile matrix product (prefill): tiles of bm = 256 or 128 weight rows by
-// 256 activation rows.  gemm_big_fits: the shape fits the kernel's 32-bit
+// 256 activation rows, Q4_K weights or (q8) Q8_0 weights.  gemm_big_fits: the shape fits the kernel's 32-bit
 // activation offsets.  gemm_big_choice: the tile height of the large-tile
 // kernel for a shape (256 when there are 256 such tiles or more, else 128
 // when there are 192 or more), 0 for the small-tile kernels; the automatic
@@ -96,7 +96,7 @@ hipError_t launch_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64
 bool gemm_big_fits(int64_t M, int64_t K, int64_t N);
 int gemm_big_choice(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int bm, hipStream_t s);
+                           int64_t N, int bm, bool q8, hipStream_t s);
 // Large-tile product with K split across kg (2 or 4) groups of waves inside
 // each workgroup: tiles of 256/kg weight rows x 128 activation rows, one
 // workgroup per CU, no workspace; requires (K/256) % kg == 0 and

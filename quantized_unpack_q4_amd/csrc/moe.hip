@@ -235,9 +235,9 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restric
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s)
 {
     const int64_t A = a.T * a.topk;
-    // Q8_0 stacks: weight streaming for few tokens per expert, else the
-    // 128-row tile kernel (the 256 x 256 tiles are Q4_K only)
-    const bool big = !a.q8_0 && moe_big_applies(A, a.E, a.H, a.I);
+    // the 256 x 256 tiles take whole runs of 256 weights: Q8_0 stacks whose
+    // H or I is not a multiple of 256 use the 128-row tile kernel instead
+    const bool big = moe_big_applies(A, a.E, a.H, a.I) && (!a.q8_0 || a.I % 256 == 0);
     const int bn = big ? moe_big_token_tile() : moe_token_tile(A, a.E);
     const int max_tiles = (int)((A + bn - 1) / bn + a.E);
     int32_t *offsets = reinterpret_cast<int32_t *>(a.ws + a.off[0]);

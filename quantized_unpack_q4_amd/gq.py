@@ -25,7 +25,7 @@ MAX_BATCH = 16
 EXPORTS = (
     "gq_gemv_q8_0", "gq_gemv_q4k", "gq_gemv_q4k_multi_table_bytes", "gq_gemv_q4k_multi_plan",
     "gq_gemv_q4k_multi", "gq_gemv_q4k_multi_batched", "gq_gemv_q4k_multi_batched_ws",
-    "gq_gemv_q4k_multi_batched_ws_bytes", "gq_gemv_q4k_swiglu", "gq_gemv_q4k_swiglu_batched", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q4k_kgroups", "gq_gemm_q4k_splitk",
+    "gq_gemv_q4k_multi_batched_ws_bytes", "gq_gemv_q4k_swiglu", "gq_gemv_q4k_swiglu_batched", "gq_gemm_q4k", "gq_gemm_q8_0", "gq_gemm_q4k_tiles", "gq_gemm_q8_0_tiles", "gq_gemm_q4k_kgroups", "gq_gemm_q4k_splitk",
     "gq_gemm_q4k_splitk_workspace_bytes", "gq_gemm_q4k_splitk_static",
     "gq_gemm_q4k_splitk_static_max_bytes",
     "gq_moe_gemm_q4k", "gq_moe_gemm_q4k_input_weighted", "gq_moe_gemm_q8_0",
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.gq_gemm_q8_0.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.gq_gemm_q4k_tiles.restype = st
         L.gq_gemm_q4k_tiles.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
+        L.gq_gemm_q8_0_tiles.restype = st
+        L.gq_gemm_q8_0_tiles.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.gq_gemv_q4k_multi_batched_ws.restype = st
         L.gq_gemv_q4k_multi_batched_ws.argtypes = [vp, vp, i64, vp, sz, vp]
         L.gq_gemv_q4k_multi_batched_ws_bytes.restype = sz
@@ -248,6 +250,11 @@ def gq_gemm_q8_0(w, x, y, M, K, N, stream=None):
 def gq_gemm_q4k_tiles(w, x, y, M, K, N, tile_rows, stream=None):
     _check(lib().gq_gemm_q4k_tiles(_ptr(w), _ptr(x), _ptr(y), M, K, N, tile_rows,
                                    _stream(stream)))
+
+
+def gq_gemm_q8_0_tiles(w, x, y, M, K, N, tile_rows, stream=None):
+    _check(lib().gq_gemm_q8_0_tiles(_ptr(w), _ptr(x), _ptr(y), M, K, N, tile_rows,
+                                    _stream(stream)))
 
 
 def gq_gemv_q4k_swiglu_batched(w_gate, w_up, x, h, M, K, B, stream=None):

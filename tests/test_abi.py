@@ -79,6 +79,15 @@ def test_gemm_refusals(L):
     s, m = status_and_msg(L, st)
     assert s == "GQ_ESHAPE" and "128-row" in m
     assert g(None, None, None, 64, 256, 0, 256, None) == 0
+    q = L.gq_gemm_q8_0_tiles
+    assert status_and_msg(L, q(FAKE, FAKE, FAKE, 64, 256, 8, 32, None))[0] == "GQ_EINVAL"
+    # the small tiles take K % 64 == 0, the large ones K % 256 == 0
+    assert status_and_msg(L, q(FAKE, FAKE, FAKE, 64, 96, 8, 64, None))[0] == "GQ_ESHAPE"
+    assert status_and_msg(L, q(FAKE, FAKE, FAKE, 64, 320, 8, 256, None))[0] == "GQ_ESHAPE"
+    st = q(FAKE, FAKE, FAKE, 64, 1 << 20, 1 << 10, 256, None)
+    s, m = status_and_msg(L, st)
+    assert s == "GQ_ESHAPE" and "256-row" in m
+    assert q(None, None, None, 64, 256, 0, 128, None) == 0
     k = L.gq_gemm_q4k_kgroups
     assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 1024, 8, 3, None))[0] == "GQ_EINVAL"
     assert status_and_msg(L, k(FAKE, FAKE, FAKE, 64, 1024, 8, 0, None))[0] == "GQ_EINVAL"

@@ -339,6 +339,28 @@ def test_gemm_q8_0_parity(M, K, N):
     say("  max err/S", r)
 
 
+def _gemm_q8_tiles(w_d, x16, M, K, tile_rows):
+    torch = torch_cuda()
+    N = x16.shape[0]
+    y = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    gq.gq_gemm_q8_0_tiles(w_d, dev(x16), y, M, K, N, tile_rows)
+    return half_bits(y)
+
+
+@pytest.mark.parametrize("M,K,N,tile_rows", [(300, 512, 270, 256), (520, 256, 600, 128),
+                                             (1000, 1024, 300, 256), (130, 768, 257, 128)])
+def test_gemm_q8_0_large_tiles_parity(M, K, N, tile_rows):
+    """Q8_0 on the large-tile kernel (pinned), at sizes the oracle computes in
+    full: several tiles, ragged M and N, K of one to four runs of 256."""
+    say("gemm q8_0 large tiles", M, K, N, tile_rows)
+    w = synth.q8_0_blocks(96, M, M, K)
+    x16 = synth.activations_f16(96, N, N, K)
+    y = _gemm_q8_tiles(dev(w), x16, M, K, tile_rows).view(np.float16).astype(np.float64)
+    yr, S = oracle.gemm(oracle.Q8_0, w, x16, M, K)
+    r = within(y, yr, S, TOL, "gemm q8_0 tiles %d %dx%dx%d" % (tile_rows, M, K, N))
+    say("  max err/S", r)
+
+
 def test_gemm_q8_0_one_hot_exact_and_special_blocks():
     """One-hot activation rows read out the binary16 weights binary16(d*q)
     exactly, on random blocks and on hand-set ones: q = -128, a negative
@@ -358,10 +380,12 @@ def test_gemm_q8_0_one_hot_exact_and_special_blocks():
     ks[:4] = [0, 3 * 32 + 5, 5 * 32 + 31, 7 * 32]
     x16 = np.zeros((N, K), np.float16)
     x16[np.arange(N), ks] = 1.0
-    yb = _gemm_q8(dev(w), x16, M, K)
-    for i, k in enumerate(ks):
-        assert np.array_equal(yb[i].view(np.float16), w16[:, k].view(np.float16)), (i, k)
-    assert yb[0].view(np.float16)[0] == -128.0
+    for tile_rows in (64, 128, 256):
+        yb = _gemm_q8_tiles(dev(w), x16, M, K, tile_rows)
+        for i, k in enumerate(ks):
+            assert np.array_equal(yb[i].view(np.float16), w16[:, k].view(np.float16)), \
+                (tile_rows, i, k)
+        assert yb[0].view(np.float16)[0] == -128.0
 
 
 def test_gemm_q8_0_prefill_sampled():

@@ -290,9 +290,9 @@ def test_moe_input_weighted(T):
                                             (700, False), (300, True)])
 def test_moe_q8_0(T, weight_input):
     """Q8_0 expert stacks (gq_moe_gemm_q8_0 and its input-weighted form): 100
-    tokens over 8 experts, top-2 (25 per expert), stream the weights; 300 and
-    700 take the 64- and 128-token tiles of the 128-row kernel; 5 tokens over
-    4 experts checks every token."""
+    tokens over 8 experts, top-2 (25 per expert), stream the weights; 300
+    takes the 64-token tiles of the 128-row kernel and 700 the 256 x 256
+    tiles; 5 tokens over 4 experts checks every token."""
     E, k = (4, 2) if T == 5 else (8, 2)
     H, I = 512, 256
     say("moe q8_0 T", T, "input weighted", weight_input)
@@ -308,6 +308,30 @@ def test_moe_q8_0(T, weight_input):
                        weight_input=weight_input, fmt=oracle.Q8_0)
     wsum = np.ones_like(wts[toks]) if weight_input else wts[toks]
     say("  staged", worst, "end-to-end", _e2e(o[toks], r, wsum))
+
+
+def test_moe_q8_0_many_tokens_per_expert_tiles():
+    """Q8_0 stacks on the 256 x 256 tiles: an expert with a full tile and a
+    44-token remainder (the reduced remainder tile), an expert with none,
+    every token checked in stages and end to end."""
+    T, H, I, E, k = 620, 512, 256, 8, 2
+    wg, wu, wd, x16, _, _ = _setup(68, T, H, I, E, k, fmt=oracle.Q8_0)
+    g = np.random.default_rng(69)
+    ids = np.zeros((T, k), np.int32)
+    for t in range(T):
+        first = 0 if t < 300 else int(g.integers(1, 7))
+        second = int(g.integers(1, 7))
+        while second == first:
+            second = int(g.integers(1, 7))
+        ids[t] = [first, second]  # expert 7 gets nothing, expert 0 gets 256 + 44 tokens
+    wts = g.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    o, table, sorted_, pos_of, h, d = _run(wg, wu, wd, x16, ids, wts, H, I, E, fmt=oracle.Q8_0)
+    _check_grouping(ids, E, table, sorted_, pos_of)
+    worst = _staged(wg, wu, wd, x16, ids, wts, H, I, E, o, table, sorted_, pos_of, h, d,
+                    range(T), fmt=oracle.Q8_0)
+    toks = list(range(0, T, 7))
+    r = oracle.moe_ffn(wg, wu, wd, x16[toks], ids[toks], wts[toks], H, I, E, fmt=oracle.Q8_0)
+    say("moe q8_0 tiles staged", worst, "end-to-end", _e2e(o[toks], r, wts[toks]))
 
 
 @pytest.mark.parametrize("rows", [261, 2054])
