@@ -207,8 +207,8 @@ gq_status gq_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, 
  *   Y[n][r] = binary16( sum_k X[n][k] * w16[r][k] ),  w16 = binary16(d * q)
  * accumulated in binary32 (d * q is exact; one rounding to binary16).
  * Requires K % 64 == 0 (the small-tile kernel takes two blocks per step;
- * GQ_ESHAPE otherwise), N <= 2^21.  With K % 256 == 0 and enough tiles the
- * large-tile kernel runs it, as for gq_gemm_q4k. */
+ * GQ_ESHAPE otherwise), N <= 2^21.  With K % 256 == 0 the large-tile kernel
+ * or its K-group form runs it where gq_gemm_q4k would take them. */
 gq_status gq_gemm_q8_0(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                        int64_t N, void *stream);
 

@@ -581,7 +581,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_q4k_big_kernel(BigParams
 // The dense product on tiles of 256/KG weight rows x 128 activation rows, K
 // split across KG groups of waves inside the workgroup (see big_tile); tiles
 // in the same XCD-aware order as the dense kernel.
-template <int KG>
+template <int KG, bool Q8 = false>
 __global__ __launch_bounds__(512, 1) void gemm_q4k_kgroups_kernel(BigParams p)
 {
     constexpr int FNT = 4, BM = 256 / KG, BNT = 32 * FNT, GX = BNT * KS;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_kgroups_kernel(BigParams p)
     const int n_t = tile / p.tiles_m, m_t = tile % p.tiles_m;
     const int m0 = m_t * BM, n0 = n_t * BNT;
     const int nvalid = p.N - n0 < BNT ? p.N - n0 : BNT;
-    big_tile<kBigDense, 8, FNT, KG>(p, m0, n0, nvalid, 0, 0, sX, sX + KG * GX);
+    big_tile<kBigDense, 8, FNT, KG, Q8>(p, m0, n0, nvalid, 0, 0, sX, sX + KG * GX);
 }
 
 // Y[n][m] = binary16(sum over s = 0..splits-1 of part[s][n][m]), summed in
@@ -707,7 +707,7 @@ int gemm_kgroups_choice(int64_t M, int64_t K, int64_t N)
 }
 
 hipError_t launch_gemm_kgroups(const void *w, const uint16_t *x, uint16_t *y, int64_t M,
-                               int64_t K, int64_t N, int kg, hipStream_t s)
+                               int64_t K, int64_t N, int kg, bool q8, hipStream_t s)
 {
     if ((kg != 2 && kg != 4) || (K / 256) % kg != 0 || !gemm_big_fits(M, K, N))
         return hipErrorInvalidValue;
@@ -722,7 +722,11 @@ hipError_t launch_gemm_kgroups(const void *w, const uint16_t *x, uint16_t *y, in
     p.tiles_m = (int)((M + bm - 1) / bm);
     p.tiles_total = (int)(p.tiles_m * ((N + 127) / 128));
     const int grid = (p.tiles_total + 7) / 8 * 8;
-    if (kg == 4)
+    if (kg == 4 && q8)
+        hipLaunchKernelGGL((gemm_q4k_kgroups_kernel<4, true>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    else if (q8)
+        hipLaunchKernelGGL((gemm_q4k_kgroups_kernel<2, true>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    else if (kg == 4)
         hipLaunchKernelGGL((gemm_q4k_kgroups_kernel<4>), dim3((unsigned)grid), dim3(512), 0, s, p);
     else
         hipLaunchKernelGGL((gemm_q4k_kgroups_kernel<2>), dim3((unsigned)grid), dim3(512), 0, s, p);

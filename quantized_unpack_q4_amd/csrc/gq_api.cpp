@@ -391,11 +391,12 @@ static gq_status gemm_common(const char *fn, const void *w, const uint16_t *x, u
     GQ_TRY(check_ptr(fn, "x", x));
     GQ_TRY(check_ptr(fn, "y", y));
     if (tile_rows == 0) {
-        // too few 256 x 256 tiles for the device: K groups (Q4_K) where they
-        // are estimated fastest
-        const int kg = q8 ? 0 : gq::gemm_kgroups_choice(M, K, N);
+        // too few 256 x 256 tiles for the device: K groups where they are
+        // estimated fastest
+        const int kg = K % 256 == 0 ? gq::gemm_kgroups_choice(M, K, N) : 0;
         if (kg)
-            return launched(fn, gq::launch_gemm_kgroups(w, x, y, M, K, N, kg, (hipStream_t)stream));
+            return launched(fn, gq::launch_gemm_kgroups(w, x, y, M, K, N, kg, q8,
+                                                        (hipStream_t)stream));
         tile_rows = K % 256 == 0 ? gq::gemm_big_choice(M, K, N) : 0;
     }
     if (tile_rows == 0 || tile_rows == 64)
@@ -460,7 +461,7 @@ gq_status gq_gemm_q4k_kgroups(const void *w, const uint16_t *x, uint16_t *y, int
     GQ_TRY(check_ptr(fn, "w", w));
     GQ_TRY(check_ptr(fn, "x", x));
     GQ_TRY(check_ptr(fn, "y", y));
-    return launched(fn, gq::launch_gemm_kgroups(w, x, y, M, K, N, (int)groups,
+    return launched(fn, gq::launch_gemm_kgroups(w, x, y, M, K, N, (int)groups, false,
                                                 (hipStream_t)stream));
 }
 

@@ -105,7 +105,7 @@ hipError_t launch_gemm_big(const void *w, const uint16_t *x, uint16_t *y, int64_
 // rounds of tiles on the device.
 int gemm_kgroups_choice(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_kgroups(const void *w, const uint16_t *x, uint16_t *y, int64_t M,
-                               int64_t K, int64_t N, int kg, hipStream_t s);
+                               int64_t K, int64_t N, int kg, bool q8, hipStream_t s);
 // Split-K form of the 256 x 256 large-tile product: `splits` runs of K/splits
 // (whole super-blocks) into binary32 partials ws [splits][N][M], then a fixed
 // order sum rounded to binary16.  gemm_splitk_choice: the split count that

@@ -103,6 +103,7 @@ int main()
     LAUNCHED(gq_gemm_q4k_tiles(p, x16, y16, 256, 1024, 512, 128, nullptr));
     REFUSED(gq_gemm_q4k_tiles(p, x16, y16, 256, 1024, 512, 100, nullptr), GQ_EINVAL);
     LAUNCHED(gq_gemm_q8_0_tiles(p, x16, y16, 256, 1024, 512, 256, nullptr));
+    LAUNCHED(gq_gemm_q8_0(p, x16, y16, 256, 1024, 128, nullptr)); // the K-group path
     LAUNCHED(gq_gemm_q8_0_tiles(p, x16, y16, 256, 320, 512, 64, nullptr));
     REFUSED(gq_gemm_q8_0_tiles(p, x16, y16, 256, 320, 512, 128, nullptr), GQ_ESHAPE);
     REFUSED(gq_gemm_q8_0_tiles(p, x16, y16, 256, 1024, 512, 100, nullptr), GQ_EINVAL);

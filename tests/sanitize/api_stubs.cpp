@@ -37,7 +37,7 @@ hipError_t launch_gemm_q8_0(const void *, const uint16_t *, uint16_t *, int64_t,
 bool gemm_big_fits(int64_t, int64_t K, int64_t N) { return N * K * 2 < ((int64_t)1 << 31); }
 int gemm_big_choice(int64_t, int64_t, int64_t) { return 256; }
 int gemm_kgroups_choice(int64_t, int64_t K, int64_t N) { return N < 256 && (K / 256) % 4 == 0 ? 4 : 0; }
-hipError_t launch_gemm_kgroups(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, int, hipStream_t) { return launch(); }
+hipError_t launch_gemm_kgroups(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, int, bool, hipStream_t) { return launch(); }
 hipError_t launch_gemm_big(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, int, bool, hipStream_t) { return launch(); }
 int gemm_splitk_choice(int64_t, int64_t K, int64_t) { return (K / 256) % 2 == 0 ? 2 : 1; }
 hipError_t launch_gemm_splitk(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, int, float *, hipStream_t) { return launch(); }

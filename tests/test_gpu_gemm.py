@@ -325,11 +325,13 @@ def _gemm_q8(w_d, x16, M, K):
 
 
 @pytest.mark.parametrize("M,K,N", [(128, 64, 1), (130, 192, 37), (300, 1088, 270),
-                                   (1000, 1024, 520), (1700, 64, 2048), (3000, 64, 3000)])
+                                   (1000, 1024, 520), (1700, 64, 2048), (3000, 64, 3000),
+                                   (256, 1024, 128), (300, 2048, 200)])
 def test_gemm_q8_0_parity(M, K, N):
     """Q8_0 product at sizes the oracle computes in full, across the tile
     families (N <= 64, 64 x 64, 64 x 128, 128 x 128), ragged M and N, the
-    smallest K."""
+    smallest K; the last two take K split across groups of waves (the
+    automatic choice for few tiles and K % 256 == 0)."""
     say("gemm q8_0", M, K, N)
     w = synth.q8_0_blocks(97, M, M, K)
     x16 = synth.activations_f16(97, N, N, K)
