@@ -157,9 +157,20 @@ __global__ __launch_bounds__(64 * W, 8 / W) void gemv_q4k_stream_kernel(
     const long long hi = total * (long long)(blockIdx.x + 1) / gridDim.x;
 
     auto entry = [&](int i) -> GemvEntry { return table ? table[i] : inline0; };
+    // the last entry whose work begins at or before lo (work_begin increases
+    // along the table; entry 0 begins at 0): a kThreads-way search, each
+    // thread testing one slot per level, one round trip per level (a single
+    // level up to kThreads entries).  Walking the table one dependent load at
+    // a time took the workgroups at its end ~57 us on the 224-entry decode
+    // stack, and they set the launch's end.
     int di = 0;
-    while (di + 1 < n && entry(di + 1).work_begin <= lo)
-        ++di;
+    for (int span = n; span > 1;) {
+        const int step = (span + kThreads - 1) / kThreads;
+        const bool le = tid * step < span && entry(di + tid * step).work_begin <= lo;
+        const int cnt = __syncthreads_count(le);
+        di += (cnt - 1) * step;
+        span = min(step, span - (cnt - 1) * step);
+    }
     GemvEntry e = entry(di);
 
     int nsb = e.K >> 8, r_end = 0, rpg = 2, sps = 16, rsub = 0, sbl = 0;
