@@ -760,8 +760,8 @@ long long gemv_mfma_prestaged_bytes(int64_t n, long long records, int B)
 }
 
 hipError_t launch_gemv_mfma_prestaged(const GemvEntry *table_dev, int n, long long total_bytes,
-                                      long long blocks2, long long blocks3, long long records,
-                                      int B, void *ws, hipStream_t s)
+                                      long long blocks1, long long blocks2, long long blocks3,
+                                      long long records, int B, void *ws, hipStream_t s)
 {
     int *prefix = static_cast<int *>(ws);
     uint8_t *recs = static_cast<uint8_t *>(ws) + gemv_prestaged_records_offset(n);
@@ -782,6 +782,15 @@ hipError_t launch_gemv_mfma_prestaged(const GemvEntry *table_dev, int n, long lo
     (void)blocks3;
     const int cus = device_cus();
     const GemvEntry none{};
+    if (blocks2 < cus) {
+        // too few 128-row blocks for one workgroup per CU: 64-row blocks
+        const long long grid = blocks1 < 2LL * cus ? blocks1 : 2LL * cus;
+        hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 1, true, 3>), dim3((unsigned)grid),
+                           dim3(NT), 0, s, table_dev, none, n, total_bytes, B,
+                           (const uint8_t *)nullptr, (const uint8_t *)recs, (const int *)prefix,
+                           rb);
+        return hipGetLastError();
+    }
     const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
     hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2, true, 3>), dim3((unsigned)grid), dim3(NT),
                        0, s, table_dev, none, n, total_bytes, B, (const uint8_t *)nullptr,
@@ -796,8 +805,8 @@ long long gemv_mfma_blocks(int64_t M, int tiles)
 }
 
 hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
-                            long long total_bytes, long long blocks2, long long blocks3, int B,
-                            hipStream_t s)
+                            long long total_bytes, long long blocks1, long long blocks2,
+                            long long blocks3, int B, hipStream_t s)
 {
     // three tiles per wave (192-row blocks: each block's activation staging
     // serves 1.5 times the weights; decode stack at batch 4 1273 -> 1196 us)
@@ -807,6 +816,23 @@ hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0
         hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 3>), dim3((unsigned)(2 * cus)), dim3(NT), 0,
                            s, table_dev, inline0, n, total_bytes, B, (const uint8_t *)nullptr,
                            (const uint8_t *)nullptr, (const int *)nullptr, 0);
+    } else if (blocks2 < cus) {
+        // too few 128-row blocks for one workgroup per CU (single products up
+        // to 32768 rows): 64-row blocks, one 16-row tile per wave, twice the
+        // workgroups (measured rotating over 1 GB: 14336 x 4096 at batch 4
+        // 35.8 -> 29.2 us, 4096 x 14336 108 -> 86 us, 4096 x 4096 35.5 ->
+        // 28.5 us); three weight sets up to batch 8, two above
+        const long long grid = blocks1 < 2LL * cus ? blocks1 : 2LL * cus;
+        if (B <= 8)
+            hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 1, false, 3>), dim3((unsigned)grid),
+                               dim3(NT), 0, s, table_dev, inline0, n, total_bytes, B,
+                               (const uint8_t *)nullptr, (const uint8_t *)nullptr,
+                               (const int *)nullptr, 0);
+        else
+            hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 1, false, 2>), dim3((unsigned)grid),
+                               dim3(NT), 0, s, table_dev, inline0, n, total_bytes, B,
+                               (const uint8_t *)nullptr, (const uint8_t *)nullptr,
+                               (const int *)nullptr, 0);
     } else {
         const long long grid = blocks2 < 2LL * cus ? blocks2 : 2LL * cus;
         hipLaunchKernelGGL((gemv_q4k_mfma_kernel<false, 2, false, 3>), dim3((unsigned)grid),

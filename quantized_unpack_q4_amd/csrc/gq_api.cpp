@@ -167,7 +167,8 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
     if (B >= 2 && gemv_mfma_fits(M, K, B)) {
         gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0, 0};
         const long long total = (long long)M * (K / 256) * 144;
-        return launched(fn, gq::launch_gemv_mfma(nullptr, e, 1, total, gq::gemv_mfma_blocks(M, 2),
+        return launched(fn, gq::launch_gemv_mfma(nullptr, e, 1, total, gq::gemv_mfma_blocks(M, 1),
+                                                 gq::gemv_mfma_blocks(M, 2),
                                                  gq::gemv_mfma_blocks(M, 3), (int)B,
                                                  (hipStream_t)stream));
     }
@@ -287,24 +288,27 @@ gq_status gq_gemv_q4k_multi_batched(const void *table, const void *table_dev, in
     }
     const gq::GemvEntry *ent =
         reinterpret_cast<const gq::GemvEntry *>((const uint8_t *)table + sizeof h);
-    long long blocks2 = 0, blocks3 = 0;
+    long long blocks1 = 0, blocks2 = 0, blocks3 = 0;
     for (int64_t i = 0; i < h.n; ++i) {
         gq::GemvEntry e;
         memcpy(&e, &ent[i], sizeof e);
         if (!gemv_mfma_fits(e.M, e.K, B))
             return fail(GQ_ESHAPE, "%s: entry %lld (M = %d, K = %d) is too large for batch %lld",
                         fn, (long long)i, e.M, e.K, (long long)B);
+        blocks1 += gq::gemv_mfma_blocks(e.M, 1);
         blocks2 += gq::gemv_mfma_blocks(e.M, 2);
         blocks3 += gq::gemv_mfma_blocks(e.M, 3);
     }
-    return launched(fn, gq::launch_gemv_mfma(dev, none, (int)h.n, h.total_bytes, blocks2, blocks3,
+    return launched(fn, gq::launch_gemv_mfma(dev, none, (int)h.n, h.total_bytes, blocks1, blocks2,
+                                             blocks3,
                                              (int)B, (hipStream_t)stream));
 }
 
 // Table checks shared by the batched multi-product forms: header, B, every
 // entry within the matrix-core path's limits; block and record counts.
 static gq_status batched_table(const char *fn, const void *table, int64_t B, TableHeader &h,
-                               long long &blocks2, long long &blocks3, long long &records)
+                               long long &blocks1, long long &blocks2, long long &blocks3,
+                               long long &records)
 {
     if (!table)
         return fail(GQ_EINVAL, "%s: table is NULL", fn);
@@ -316,13 +320,14 @@ static gq_status batched_table(const char *fn, const void *table, int64_t B, Tab
                     GQ_GEMV_MAX_BATCH);
     const gq::GemvEntry *ent =
         reinterpret_cast<const gq::GemvEntry *>((const uint8_t *)table + sizeof h);
-    blocks2 = blocks3 = records = 0;
+    blocks1 = blocks2 = blocks3 = records = 0;
     for (int64_t i = 0; i < h.n; ++i) {
         gq::GemvEntry e;
         memcpy(&e, &ent[i], sizeof e);
         if (B >= 2 && !gemv_mfma_fits(e.M, e.K, B))
             return fail(GQ_ESHAPE, "%s: entry %lld (M = %d, K = %d) is too large for batch %lld",
                         fn, (long long)i, e.M, e.K, (long long)B);
+        blocks1 += gq::gemv_mfma_blocks(e.M, 1);
         blocks2 += gq::gemv_mfma_blocks(e.M, 2);
         blocks3 += gq::gemv_mfma_blocks(e.M, 3);
         records += e.K / 256;
@@ -335,9 +340,9 @@ size_t gq_gemv_q4k_multi_batched_ws_bytes(const void *table, int64_t B)
     char saved[sizeof g_err];
     memcpy(saved, g_err, sizeof g_err);
     TableHeader h;
-    long long b2 = 0, b3 = 0, recs = 0;
-    const gq_status st = batched_table("gq_gemv_q4k_multi_batched_ws_bytes", table, B, h, b2, b3,
-                                       recs);
+    long long b1 = 0, b2 = 0, b3 = 0, recs = 0;
+    const gq_status st = batched_table("gq_gemv_q4k_multi_batched_ws_bytes", table, B, h, b1, b2,
+                                       b3, recs);
     memcpy(g_err, saved, sizeof g_err);
     if (st != GQ_OK)
         return 0;
@@ -351,8 +356,8 @@ gq_status gq_gemv_q4k_multi_batched_ws(const void *table, const void *table_dev,
 {
     static const char fn[] = "gq_gemv_q4k_multi_batched_ws";
     TableHeader h;
-    long long blocks2 = 0, blocks3 = 0, records = 0;
-    GQ_TRY(batched_table(fn, table, B, h, blocks2, blocks3, records));
+    long long blocks1 = 0, blocks2 = 0, blocks3 = 0, records = 0;
+    GQ_TRY(batched_table(fn, table, B, h, blocks1, blocks2, blocks3, records));
     GQ_TRY(check_ptr(fn, "table_dev", table_dev));
     if (B == 1)
         return gq_gemv_q4k_multi(table, table_dev, stream);
@@ -368,8 +373,8 @@ gq_status gq_gemv_q4k_multi_batched_ws(const void *table, const void *table_dev,
         return fail(GQ_ESHAPE, "%s: %lld super-blocks in the table exceed 2^31", fn, records);
     const gq::GemvEntry *dev = reinterpret_cast<const gq::GemvEntry *>(
         (const uint8_t *)table_dev + sizeof(TableHeader));
-    return launched(fn, gq::launch_gemv_mfma_prestaged(dev, (int)h.n, h.total_bytes, blocks2,
-                                                       blocks3, records, (int)B, ws,
+    return launched(fn, gq::launch_gemv_mfma_prestaged(dev, (int)h.n, h.total_bytes, blocks1,
+                                                       blocks2, blocks3, records, (int)B, ws,
                                                        (hipStream_t)stream));
 }
 

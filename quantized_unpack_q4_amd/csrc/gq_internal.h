@@ -62,9 +62,9 @@ hipError_t launch_gemv_swiglu(const void *w_gate, const void *w_up, const float 
                               int64_t M, int64_t K, hipStream_t s);
 
 // Small-batch (2 <= B <= 16) products on the matrix cores, over a table of
-// entries (or the single entry inline0 when table_dev is null); blocks of 128
-// rows are dealt to workgroups by byte ranges of the packed weights.
-long long gemv_mfma_blocks(int64_t M, int tiles); // blocks of 64*tiles rows (tiles 2 or 3)
+// entries (or the single entry inline0 when table_dev is null); blocks of 64,
+// 128 or 192 rows are dealt to workgroups by byte ranges of the packed weights.
+long long gemv_mfma_blocks(int64_t M, int tiles); // blocks of 64*tiles rows (tiles 1, 2 or 3)
 // The same over a table with the activations staged once per (entry,
 // super-block) into a workspace by a pre-pass: [prefix: int32 [n+1]], then at
 // gemv_prestaged_records_offset(n) one record of rec_bytes(B) per super-block
@@ -72,15 +72,15 @@ long long gemv_mfma_blocks(int64_t M, int tiles); // blocks of 64*tiles rows (ti
 inline long long gemv_prestaged_records_offset(int64_t n) { return ((n + 1) * 4 + 255) / 256 * 256; }
 long long gemv_mfma_prestaged_bytes(int64_t n, long long records, int B);
 hipError_t launch_gemv_mfma_prestaged(const GemvEntry *table_dev, int n, long long total_bytes,
-                                      long long blocks2, long long blocks3, long long records,
-                                      int B, void *ws, hipStream_t s);
+                                      long long blocks1, long long blocks2, long long blocks3,
+                                      long long records, int B, void *ws, hipStream_t s);
 // h[b][r] = silu(w_gate_r x[b]) * (w_up_r x[b]) for 2 <= B <= 16 on the same
 // kernel: blocks of 64 output rows pair 64 gate rows with the same up rows.
 hipError_t launch_gemv_swiglu_mfma(const void *w_gate, const void *w_up, const float *x, float *h,
                                    int64_t M, int64_t K, int B, hipStream_t s);
 hipError_t launch_gemv_mfma(const GemvEntry *table_dev, const GemvEntry &inline0, int n,
-                            long long total_bytes, long long blocks2, long long blocks3, int B,
-                            hipStream_t s);
+                            long long total_bytes, long long blocks1, long long blocks2,
+                            long long blocks3, int B, hipStream_t s);
 
 hipError_t launch_gemm_q4k(const void *w, const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, hipStream_t s);

@@ -28,9 +28,9 @@ int gemv_stream_grid(long long, long long tiles) { return tiles < 512 ? (int)til
 hipError_t launch_gemv_stream(const GemvEntry *, const GemvEntry &, int, long long, int, hipStream_t) { return launch(); }
 hipError_t launch_gemv_swiglu(const void *, const void *, const float *, float *, int64_t, int64_t, hipStream_t) { return launch(); }
 long long gemv_mfma_blocks(int64_t M, int tiles) { return (M + 64 * tiles - 1) / (64 * tiles); }
-hipError_t launch_gemv_mfma(const GemvEntry *, const GemvEntry &, int, long long, long long, long long, int, hipStream_t) { return launch(); }
+hipError_t launch_gemv_mfma(const GemvEntry *, const GemvEntry &, int, long long, long long, long long, long long, int, hipStream_t) { return launch(); }
 long long gemv_mfma_prestaged_bytes(int64_t n, long long records, int B) { return gemv_prestaged_records_offset(n) + records * 1024 * ((608 + 1024 * B + 1023) / 1024); }
-hipError_t launch_gemv_mfma_prestaged(const GemvEntry *, int, long long, long long, long long, long long, int, void *, hipStream_t) { return launch(); }
+hipError_t launch_gemv_mfma_prestaged(const GemvEntry *, int, long long, long long, long long, long long, long long, int, void *, hipStream_t) { return launch(); }
 hipError_t launch_gemv_swiglu_mfma(const void *, const void *, const float *, float *, int64_t, int64_t, int, hipStream_t) { return launch(); }
 hipError_t launch_gemm_q4k(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, hipStream_t) { return launch(); }
 hipError_t launch_gemm_q8_0(const void *, const uint16_t *, uint16_t *, int64_t, int64_t, int64_t, hipStream_t) { return launch(); }
