@@ -75,13 +75,14 @@ typedef enum gq_status {
  *   y[b][r] = sum_k w[r][k] * x[b][k]  for r < M, b < B, accumulated in binary32.
  * w: M rows of K/32 Q8_0 blocks (M*K/32*34 bytes).  x: [B][K] float.  y: [B][M] float.
  * Requires K % 32 == 0, 1 <= B <= GQ_GEMV_MAX_BATCH.  With B >= 2 and
- * K % 64 == 0 the block sums run on the matrix cores with x carried as a
- * binary16 hi + lo pair scaled per activation row and 32-weight block: every
- * value at least 2^-20 of its block's largest |x| keeps a relative error
- * below 2^-19; a block whose non-zero |x| span more than 2^20 is computed in
- * binary32 instead (d*q times x).  Accuracy: see GQ_GEMV_ACCURACY below.
- * Within 2 <= B <= 16 an activation row's result does not depend on B or on
- * the other rows (B = 1 runs another kernel). */
+ * K % 64 == 0 the block sums d * sum(q*x) run on the binary32 matrix-core
+ * products: the quant converted exactly, x as given, products and sums in
+ * binary32, d applied once per 32-weight block.  Accuracy: see
+ * GQ_GEMV_ACCURACY below (results in the subnormal range: up to one multiple
+ * of 2^-149 per block).  An activation row's result does not depend on the
+ * other rows; B <= 4 and B >= 5 sum in different orders (two matrix-core
+ * products), so a row's bits can differ between the two ranges, and B = 1
+ * runs another kernel. */
 gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, int64_t B,
                        void *stream);
 
@@ -91,15 +92,20 @@ gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64
  * sub-block the sum is taken in the factored form
  * (d*sc)*sum(q*x) - (dmin*m)*sum(x), with x carried as a binary16 hi + lo
  * pair (products exact, sums binary32): batch 1 on packed dot products with
- * one power-of-two scale per sub-block, batches 2..16 on the matrix cores with
- * one per activation row and super-block (see gq_gemv_q4k_multi_batched).
- * Every split value keeps a relative error below 2^-19.  A sub-block whose
- * non-zero |x| span more than 2^20 (batch 1; batches 2..16: holding a
- * non-zero |x| below 2^-20 of its super-block's largest), or that holds more
- * than 1/16 of the sum of |x| over its super-block, is computed exactly
- * instead: each weight as its binary32 value times x in binary32.  K above
- * 16384 at batch 1 (and matrices beyond the matrix-core kernel's 32-bit
- * offsets) run a kernel that dequantizes every weight to binary32 first.
+ * one power-of-two scale per sub-block, batches 3..16 on matrices of more
+ * than 32 rows per CU on the matrix cores with one per activation row and
+ * super-block (see gq_gemv_q4k_multi_batched).  Every split value keeps a
+ * relative error below 2^-19.  A sub-block whose non-zero |x| span more than
+ * 2^20 (batch 1; batches 3..16: holding a non-zero |x| below 2^-20 of its
+ * super-block's largest), or that holds more than 1/16 of the sum of |x|
+ * over its super-block, is computed exactly instead: each weight as its
+ * binary32 value times x in binary32.  The other batch 2..16 products
+ * (batch 2, up to 32 rows per CU, or matrices beyond the 32-bit offsets of
+ * that kernel) dequantize each weight to binary32, fma(q, d*sc, -dmin*m)
+ * with one rounding, and take products and sums in binary32 on the matrix
+ * cores, K split over the waves of a workgroup (results in the subnormal
+ * range: up to K/2 multiples of 2^-149).  K above 16384 at batch 1 runs a
+ * kernel that dequantizes every weight to binary32 first.
  *
  * GQ_GEMV_ACCURACY (every binary32-activation product of this header): with
  * S = sum_k |w_k x_k| (w the binary32 weight) and finite inputs,

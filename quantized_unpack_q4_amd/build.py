@@ -24,7 +24,7 @@ PROBE_LIB = os.path.join(PKG, "libgq_probe.so")
 PROBE_SOURCES = ["probes.hip"]
 ARCH = os.environ.get("GQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["dequant.hip", "gemv.hip", "gemv_stream.hip", "gemv_mfma.hip", "gemm.hip", "gemm_big.hip", "moe.hip", "moe_skinny.hip", "moe_route.hip", "gemv_q8k.hip", "gemm_q8k.hip", "gemv_q8_0_mfma.hip", "gq_api.cpp"]
+SOURCES = ["dequant.hip", "gemv.hip", "gemv_stream.hip", "gemv_mfma.hip", "gemm.hip", "gemm_big.hip", "moe.hip", "moe_skinny.hip", "moe_route.hip", "gemv_q8k.hip", "gemm_q8k.hip", "gemv_q8_0_mfma.hip", "gemv_q4k_f32.hip", "gq_api.cpp"]
 
 FLAGS = [
     "--offload-arch=" + ARCH,

@@ -164,7 +164,16 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
         const int grid = gq::gemv_stream_grid(total, gq::gemv_stream_tiles(M, K));
         return launched(fn, gq::launch_gemv_stream(nullptr, e, 1, total, grid, (hipStream_t)stream));
     }
-    if (B >= 2 && gemv_mfma_fits(M, K, B)) {
+    // batch 2..16: whole-K blocks of 64 rows (the table kernel) once they
+    // fill half the chip, else the K-split binary32 form, which is also
+    // faster at batch 2 and takes matrices past the table kernel's 32-bit
+    // offsets (measured, kernel durations: 4096x14336 at batch 4 84 -> 36 us,
+    // 4096x4096 25 -> 13 us, 14336x4096 at batch 2 26.9 -> 24.5 us; 14336x4096
+    // at batch 4 26.4 us on the table kernel against 27.8)
+    if (B >= 2) {
+        if (B == 2 || M <= 32LL * gq::device_cus() || !gemv_mfma_fits(M, K, B))
+            return launched(fn,
+                            gq::launch_gemv_q4k_f32(w, x, y, M, K, (int)B, (hipStream_t)stream));
         gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0, 0};
         const long long total = (long long)M * (K / 256) * 144;
         return launched(fn, gq::launch_gemv_mfma(nullptr, e, 1, total, gq::gemv_mfma_blocks(M, 1),

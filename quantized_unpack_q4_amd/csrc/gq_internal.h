@@ -139,6 +139,11 @@ hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 hipError_t launch_gemv_q8_0_mfma(const void *w, const float *x, float *y, int64_t M, int64_t K,
                                  int B, hipStream_t s);
 
+// A single Q4_K product, 2 <= B <= 16, on the binary32 matrix cores with K
+// split over the waves of a workgroup (gemv_q4k_f32.hip).
+hipError_t launch_gemv_q4k_f32(const void *w, const float *x, float *y, int64_t M, int64_t K,
+                               int B, hipStream_t s);
+
 // Activations as 8-bit blocks of 256 (x [B][K] -> codes [B][K], scales
 // [B][K/256], sub-block sums [B][K/32]) and the Q4_K integer-dot product over
 // them, 1 <= B <= 16.

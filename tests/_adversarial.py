@@ -76,10 +76,13 @@ def floor_for(pattern, K, kernel):
     rounded to multiples of 2^-149 at each conversion to the output scale:
     once per output (batch-1 streaming kernel), up to 16 times per
     super-block (matrix-core kernel), once per block (Q8_0) or once per
-    product (general kernel)."""
+    product (general kernel).  The binary32 matrix-core form of single Q4_K
+    products at batch 2-16 ("f32mma") rounds each product w*x once, by at most
+    2^-150 (its sums of multiples of 2^-149 are exact), so K/2 units."""
     if pattern != "subnormal":
         return 0.0
-    n = {"stream": 1.0, "mfma": K / 16.0, "q8": K / 32.0, "general": float(K)}[kernel]
+    n = {"stream": 1.0, "mfma": K / 16.0, "q8": K / 32.0, "general": float(K),
+         "f32mma": K / 2.0}[kernel]
     return n * 2.0 ** -149
 
 

@@ -44,6 +44,7 @@ hipError_t launch_gemm_splitk(const void *, const uint16_t *, uint16_t *, int64_
 hipError_t splitk_scratch(float **out) { *out = g_scratch; return hipSuccess; }
 hipError_t launch_moe(const MoeArgs &, hipStream_t) { return launch(); }
 hipError_t launch_gemv_q8_0_mfma(const void *, const float *, float *, int64_t, int64_t, int, hipStream_t) { return launch(); }
+hipError_t launch_gemv_q4k_f32(const void *, const float *, float *, int64_t, int64_t, int, hipStream_t) { return launch(); }
 hipError_t launch_quantize_q8k(const float *, int8_t *, float *, int32_t *, int64_t, int64_t, hipStream_t) { return launch(); }
 hipError_t launch_gemv_q4k_q8k(const void *, const int8_t *, const float *, const int32_t *, float *, int64_t, int64_t, int, hipStream_t) { return launch(); }
 hipError_t launch_gemm_q4k_q8k(const void *, const int8_t *, const float *, float *, int64_t, int64_t, int64_t, hipStream_t) { return launch(); }

@@ -92,8 +92,9 @@ def test_q4k_batch1_table():
 
 @pytest.mark.parametrize("B", [2, 4, 16])
 def test_q4k_batched(B):
-    """Batch rows with different patterns in one call (matrix-core kernel),
-    single matrix and a table."""
+    """Batch rows with different patterns in one call: a single matrix (the
+    binary32 matrix-core form) and a table (the binary16-split matrix-core
+    kernel)."""
     torch = torch_cuda()
     M, K = 392, 4096
     w, _ = adversarial_q4k(94, B, M, K)
@@ -103,7 +104,7 @@ def test_q4k_batched(B):
     say("batched single", B, pats)
     y = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
     gq.gq_gemv_q4k(dev(w), dev(x), y, M, K, B)
-    w1 = _compare(host(y), w, xs, M, K, oracle.Q4_K, "mfma", "batched B=%d" % B)
+    w1 = _compare(host(y), w, xs, M, K, oracle.Q4_K, "f32mma", "batched B=%d" % B)
     # the same rows as one entry of a two-entry table (the second a shorter K)
     M2, K2 = 130, 1024
     w2, _ = adversarial_q4k(95, B, M2, K2)

@@ -143,6 +143,51 @@ def test_q4k_parity_full_single_matrix(M, K):
     say("  max err/S", r)
 
 
+@pytest.mark.parametrize("M,K,B", [(12300, 768, 2), (8200, 1280, 2), (4100, 256, 3),
+                                   (1000, 4352, 12)])
+def test_q4k_batched_single_ragged(M, K, B):
+    """Single products at batch 2..16 on the binary32 matrix-core form (batch
+    2, or at most 32 rows per CU): each launch form (two 16-row tiles of eight
+    waves at 12300 rows, one tile of eight waves at 8200 and 4100, one of
+    sixteen at 1000; the 4x4x1 and the 16x16x4 products) with a partial last
+    32- or 16-row group and a partial last chunk of staged super-blocks (12,
+    20, 4 and 68 units of 64 weights), activation rows scaled from 1e-30 to
+    1e30 plus an all-zero row."""
+    say("q4k batched single", M, K, B)
+    w = synth.q4k_blocks(86, M, M, K)
+    x = synth.activations_f32(86, M + B, B, K)
+    scales = np.array([1e-30, 1e-8, 1.0, 3e4, 1e12, 1e30, 0.0, 7.0] * 2, np.float32)[:B]
+    x = (x * scales[:, None]).astype(np.float32)
+    y = _gemv("q4k", dev(w), x, M, K)
+    yr, S = oracle.gemv(oracle.Q4_K, w, x, M, K)
+    say("  max err/S", within(y, yr, S, TOL, "q4k batched %dx%d B=%d" % (M, K, B)))
+    if B > 6:
+        assert np.all(y[6] == 0)
+
+
+@pytest.mark.parametrize("M,K,B", [(14336, 4096, 2), (4096, 14336, 4), (11008, 4096, 2),
+                                   (4096, 4096, 16), (14336, 4096, 16)])
+def test_q4k_batched_single_full_size_sampled(M, K, B):
+    """Decode shapes at batch 2..16 as single products (the binary32 form at
+    batch 2 and up to 32 rows per CU, the split-activation kernel for 14336
+    rows at batch 16), 64 sampled rows, and the same bits on a second call."""
+    torch = torch_cuda()
+    say("q4k batched single full", M, K, B)
+    w = synth.q4k_blocks(87, M, M, K)
+    x = synth.activations_f32(87, M, B, K)
+    wd, xd = dev(w), dev(x)
+    y = torch.empty((B, M), dtype=torch.float32, device="cuda")
+    gq.gq_gemv_q4k(wd, xd, y, M, K, B)
+    y1 = host(y).copy()
+    gq.gq_gemv_q4k(wd, xd, y, M, K, B)
+    assert np.array_equal(y1.view(np.uint32), host(y).view(np.uint32))
+    g = np.random.default_rng(87)
+    rows = np.sort(g.choice(M, 64, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    yr, S = oracle.gemv(oracle.Q4_K, w, x, M, K, rows=rows)
+    say("  max err/S", within(y1[:, rows], yr, S, TOL, "q4k batched full %dx%d" % (M, K)))
+
+
 def test_q4k_one_hot_exact():
     M, K = 45, 1024
     w = synth.q4k_blocks(83, 0, M, K)
