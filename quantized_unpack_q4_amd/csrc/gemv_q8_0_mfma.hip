@@ -13,11 +13,14 @@
 // split, rescaled or routed around (binary32 products and sums throughout,
 // subnormals kept, as a binary32 dot product in another order would give);
 // d is applied in binary32 once per block.  B <= 4 runs the 16-block
-// v_mfma_f32_4x4x1f32 (block 4g + s: rows 4g .. 4g+3 of a 16-row tile against
-// the batch rows, over weight slice s of the block), larger batches
-// v_mfma_f32_16x16x4f32 (the batch rows fill the 16 rows of the activation
-// operand, rows past B are zero); an instruction takes one weight and one
-// activation per lane, so eight of them cover a block.
+// v_mfma_f32_4x4x1f32 in one of two layouts: block 4g + s as rows 4g .. 4g+3
+// of a 16-row tile against the batch rows over 8-weight slice s of the block
+// (eight instructions per block and tile), or block s as the 4 weights
+// 4s .. 4s+3 of a pair for one 4-row group (four instructions per group and
+// pair, each activation loaded by one lane instead of four); larger batches
+// run v_mfma_f32_16x16x4f32 (the batch rows fill the 16 rows of the
+// activation operand, rows past B are zero).  An instruction takes one
+// weight and one activation per lane.
 //
 // Work split.  A workgroup of W waves owns T 16-row tiles of weight rows over
 // all of K; wave w takes the 64-weight pairs of blocks m = w, w + W, ... (a
@@ -47,13 +50,18 @@ template <int k> __device__ __forceinline__ float sbyte(uint32_t v)
     return (float)((int32_t)(v << (24 - 8 * k)) >> 24);
 }
 
-// SMALL: batch rows 0..3 on the 4x4x1 product, else 0..15 on 16x16x4.
-template <int T, int W, bool SMALL>
+// FORM: kWide (batch rows 0..15 on 16x16x4), kGroups (0..3 on 4x4x1, block
+// 4g + s = 4-row group g of a tile over 8-weight slice s of a block), kSlices
+// (0..3 on 4x4x1, block s = the 4 weights 4s .. 4s+3 of a pair for every
+// 4-row group, so each activation is loaded by one lane, not four).
+enum { kWide = 0, kGroups = 1, kSlices = 2 };
+template <int T, int W, int FORM>
 __global__ __launch_bounds__(64 * W) void gemv_q8_0_mfma_kernel(
     const uint8_t *__restrict__ w, const float *__restrict__ x, float *__restrict__ y, int M,
     int K, int B)
 {
     constexpr int kRows = 16 * T;
+    constexpr bool SMALL = FORM != kWide, SLICES = FORM == kSlices;
     constexpr int kBatch = SMALL ? 4 : 16;
     static_assert(kBatch * kRows <= 64 * W, "the reduction needs a thread per output");
     static_assert(W % 4 == 0, "a chunk of W pairs is whole 16-byte pieces");
@@ -70,6 +78,14 @@ __global__ __launch_bounds__(64 * W) void gemv_q8_0_mfma_kernel(
     const int wr = SMALL ? ((lane >> 4) << 2) | (lane & 3) : lane & 15;
     const int ks = SMALL ? (lane >> 2) & 3 : lane >> 4;
     const int xb = SMALL ? lane & 3 : lane & 15;
+    // kSlices: lane l = 4s + j takes activation row j and weight row 4g + j of
+    // every 4-row group g, for the weights 4s .. 4s+3 of a pair (block s / 8,
+    // quants from byte 34(s/8) + 2 + 4(s%8); the scale in the low or high
+    // half of dword 8(s/8))
+    const int sl = lane >> 2, jl = lane & 3;
+    const int sblk = sl >> 3;
+    const int qd = sblk ? 9 + (sl & 7) : (sl & 7), qsh = sblk ? 0 : 2;
+    const int dd = 8 * sblk, dsh = 16 * sblk;
     const int r0 = (int)blockIdx.x * kRows;
     const int npair = K >> 6;
     const int nchunk = (npair + W - 1) / W;
@@ -121,7 +137,10 @@ __global__ __launch_bounds__(64 * W) void gemv_q8_0_mfma_kernel(
         float4 x0, x1, x2, x3;
     };
     auto load_x = [&](int m, Xs &p) {
-        if (xrow_ok && m < npair) {
+        if (SLICES) {
+            p.x0 = xrow_ok && m < npair ? ldf4(xrow + 64 * m + 4 * sl)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        } else if (xrow_ok && m < npair) {
             const float *xp = xrow + 64 * m + 8 * ks;
             p.x0 = ldf4(xp);
             p.x1 = ldf4(xp + 4);
@@ -132,15 +151,39 @@ __global__ __launch_bounds__(64 * W) void gemv_q8_0_mfma_kernel(
         }
     };
 
-    float acc[T][4];
+    constexpr int G = SLICES ? 4 : 1; // 4-row groups held apart (kSlices)
+    float acc[T][G][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[t][i] = 0.f;
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][g][i] = 0.f;
     // this wave's pair of the chunk in buffer buf against activations p
     auto compute = [&](int buf, const Xs &p) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(wbuf4[buf]);
+        if constexpr (SLICES) {
+            const float xv[4] = {p.x0.x, p.x0.y, p.x0.z, p.x0.w};
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const uint32_t *pr = wb + (16 * t + 4 * g + jl) * kStride + 17 * wave;
+                    const uint32_t q = __builtin_amdgcn_alignbyte(pr[qd + 1], pr[qd], qsh);
+                    const uint32_t dw = (pr[dd] >> dsh) & 0xffffu;
+                    float4_t c = float4_t{0.f, 0.f, 0.f, 0.f};
+                    c = __builtin_amdgcn_mfma_f32_4x4x1f32(xv[0], sbyte<0>(q), c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_4x4x1f32(xv[1], sbyte<1>(q), c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_4x4x1f32(xv[2], sbyte<2>(q), c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_4x4x1f32(xv[3], sbyte<3>(q), c, 0, 0, 0);
+                    const float d = half_to_float(dw);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[t][g][i] = fmaf(d, c[i], acc[t][g][i]);
+                }
+            return;
+        }
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const float4 u = blk ? p.x2 : p.x0, v = blk ? p.x3 : p.x1;
@@ -169,22 +212,27 @@ __global__ __launch_bounds__(64 * W) void gemv_q8_0_mfma_kernel(
                 const float d = half_to_float(dw);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[t][i] = fmaf(d, c[i], acc[t][i]);
+                    acc[t][0][i] = fmaf(d, c[i], acc[t][0][i]);
             }
         }
     };
 
     // chunk c is computed from LDS buffer c % 2 while the loaded chunk c + 1
     // is stored into the other and the loads of chunk c + 2 go out
-    Xs xc, xn;
+    // (kSlices, one float4 of activations per pair, loads them two chunks
+    // ahead)
+    constexpr int XA = SLICES ? 2 : 1;
+    Xs xc, xn, xnn;
     stage_load(0);
     load_x(wave, xc);
+    if (XA == 2)
+        load_x(W + wave, xn);
     stage_store(0);
     __syncthreads();
     if (nchunk > 1)
         stage_load(1);
     for (int c = 0; c < nchunk; ++c) {
-        load_x((c + 1) * W + wave, xn);
+        load_x((c + XA) * W + wave, XA == 2 ? xnn : xn);
         if (c * W + wave < npair)
             compute(c & 1, xc);
         if (c + 1 < nchunk) {
@@ -194,28 +242,53 @@ __global__ __launch_bounds__(64 * W) void gemv_q8_0_mfma_kernel(
         }
         __syncthreads();
         xc = xn;
+        if (XA == 2)
+            xn = xnn;
     }
-    if constexpr (SMALL) {
+    if constexpr (SLICES) {
+        // sum the 16 slices of a pair (lanes 4, 8, 16 and 32 apart)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = acc[t][g][i];
+                    v += __shfl_xor(v, 4, 64);
+                    v += __shfl_xor(v, 8, 64);
+                    v += __shfl_xor(v, 16, 64);
+                    v += __shfl_xor(v, 32, 64);
+                    acc[t][g][i] = v;
+                }
+        if (sl == 0)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        red[wave][i][16 * t + 4 * g + jl] = acc[t][g][i];
+    } else if constexpr (SMALL) {
         // sum the four weight slices of a block (lanes 4 and 8 apart)
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[t][i] += __shfl_xor(acc[t][i], 4, 64);
-                acc[t][i] += __shfl_xor(acc[t][i], 8, 64);
+                acc[t][0][i] += __shfl_xor(acc[t][0][i], 4, 64);
+                acc[t][0][i] += __shfl_xor(acc[t][0][i], 8, 64);
             }
         if (ks == 0)
 #pragma unroll
             for (int t = 0; t < T; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    red[wave][i][16 * t + wr] = acc[t][i];
+                    red[wave][i][16 * t + wr] = acc[t][0][i];
     } else {
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                red[wave][4 * (lane >> 4) + i][16 * t + wr] = acc[t][i];
+                red[wave][4 * (lane >> 4) + i][16 * t + wr] = acc[t][0][i];
     }
     __syncthreads();
     if (tid < kBatch * kRows) {
@@ -233,11 +306,20 @@ template <int T, int W>
 hipError_t go(const void *w, const float *x, float *y, int64_t M, int64_t K, int B, hipStream_t s)
 {
     const unsigned grid = (unsigned)((M + 16 * T - 1) / (16 * T));
-    if (B <= 4)
-        hipLaunchKernelGGL((gemv_q8_0_mfma_kernel<T, W, true>), dim3(grid), dim3(64 * W), 0, s,
-                           static_cast<const uint8_t *>(w), x, y, (int)M, (int)K, B);
+    // batch 4 (and 3 on one-tile launches) on the slice form, whose
+    // activation loads do not repeat per 4-row group; batch 2 on the group
+    // form, which spends half the scaling FMAs (measured, kernel durations,
+    // group -> slice form: 4096x14336 batch 4 37.4 -> 28.5 us, 11008x4096
+    // 31.0 -> 23.5, 4096x4096 13.7 -> 12.0; batch 2 14336x4096 23.8 -> 28.0,
+    // 4096x4096 10.7 -> 12.1; batch 3 14336x4096 25.5 -> 28.0)
+    if (B == 4 || (B == 3 && T == 1))
+        hipLaunchKernelGGL((gemv_q8_0_mfma_kernel<T, W, kSlices>), dim3(grid), dim3(64 * W), 0,
+                           s, static_cast<const uint8_t *>(w), x, y, (int)M, (int)K, B);
+    else if (B <= 4)
+        hipLaunchKernelGGL((gemv_q8_0_mfma_kernel<T, W, kGroups>), dim3(grid), dim3(64 * W), 0,
+                           s, static_cast<const uint8_t *>(w), x, y, (int)M, (int)K, B);
     else
-        hipLaunchKernelGGL((gemv_q8_0_mfma_kernel<T, W, false>), dim3(grid), dim3(64 * W), 0, s,
+        hipLaunchKernelGGL((gemv_q8_0_mfma_kernel<T, W, kWide>), dim3(grid), dim3(64 * W), 0, s,
                            static_cast<const uint8_t *>(w), x, y, (int)M, (int)K, B);
     return hipGetLastError();
 }

@@ -57,15 +57,17 @@ def test_q8_0_one_hot_exact():
 
 @pytest.mark.parametrize("M,K,B", [(1, 64, 2), (17, 128, 5), (100, 4096, 16), (61, 14336, 3),
                                    (333, 1024, 8), (12300, 256, 7), (8200, 192, 3),
-                                   (4100, 1088, 4), (8200, 320, 12)])
+                                   (4100, 1088, 4), (8200, 320, 12), (12300, 320, 4),
+                                   (12400, 128, 3)])
 def test_q8_0_matrix_core_ragged(M, K, B):
     """Batch 2..16 with K % 64 == 0 (the matrix-core kernel): rows that leave a
     partial 16-row group (12300 rows: a partial 32-row group of the two-tile
     form; 8200 and 4100 rows: the one-tile form with eight waves), K from one
     pair of blocks to the maximum and pair counts that leave the last chunk of
-    staged weights partial (3, 5 and 17 pairs), batch sizes on both the
-    4x4x1 and the 16x16x4 products, and activation rows scaled from 1e-30 to
-    1e30 plus an all-zero row."""
+    staged weights partial (3, 5 and 17 pairs), batch sizes on the 16x16x4
+    product and on both 4x4x1 layouts (batch 2 and 3 on two-tile launches:
+    groups; batch 4, and 3 on one-tile launches: slices), and activation rows
+    scaled from 1e-30 to 1e30 plus an all-zero row."""
     say("q8_0 mfma gemv", M, K, B)
     w = synth.q8_0_blocks(83, M, M, K)
     x = synth.activations_f32(83, M + B, B, K)
@@ -79,7 +81,8 @@ def test_q8_0_matrix_core_ragged(M, K, B):
     say("  max err/S", r)
 
 
-@pytest.mark.parametrize("M,K,B", [(14336, 4096, 16), (4096, 14336, 4), (11008, 4096, 2)])
+@pytest.mark.parametrize("M,K,B", [(14336, 4096, 16), (4096, 14336, 4), (11008, 4096, 2),
+                                   (14336, 4096, 4)])
 def test_q8_0_matrix_core_full_size_sampled(M, K, B):
     """Decode shapes at batch 2, 4 and 16 (every launch form of the kernel), 64
     sampled rows, and the same bits on a second call."""
