@@ -147,15 +147,17 @@ def test_q4k_parity_full_single_matrix(M, K):
 
 
 @pytest.mark.parametrize("M,K,B", [(12300, 768, 2), (8200, 1280, 2), (4100, 256, 3),
-                                   (1000, 4352, 12)])
+                                   (1000, 4352, 12), (300, 8448, 3), (8000, 512, 4)])
 def test_q4k_batched_single_ragged(M, K, B):
     """Single products at batch 2..16 on the binary32 matrix-core form (batch
     2, or at most 32 rows per CU): each launch form (two 16-row tiles of eight
     waves at 12300 rows, one tile of eight waves at 8200 and 4100, one of
-    sixteen at 1000; the 4x4x1 and the 16x16x4 products) with a partial last
-    32- or 16-row group and a partial last chunk of staged super-blocks (12,
-    20, 4 and 68 units of 64 weights), activation rows scaled from 1e-30 to
-    1e30 plus an all-zero row."""
+    sixteen at 1000 and 300; the 16x16x4 product and both 4x4x1 layouts: by
+    4-row groups, and by 4-weight slices at batch 4 and at batch 3 with K of
+    8192 or more) with a partial last 32- or 16-row group and a partial last
+    chunk of staged super-blocks (12, 20, 4, 68, 132 and 8 units of 64
+    weights), activation rows scaled from 1e-30 to 1e30 plus an all-zero
+    row."""
     say("q4k batched single", M, K, B)
     w = synth.q4k_blocks(86, M, M, K)
     x = synth.activations_f32(86, M + B, B, K)
