@@ -623,6 +623,25 @@ def main():
                               "int_dot_GB/s": round(q4k_bytes(M, K) / si / 1e9, 1),
                               "binary32_us": round(sb * 1e6, 2), "quantize_us": round(sq * 1e6, 2)}
         extra["gemv_q4k_q8k_%dx%d" % (M, K)] = q8k
+        # single Q4_K products at batch 2, 4 and 16 (gq_gemv_q4k: the K-split
+        # binary32 form at these shapes), rotated over the 32 layers' matrices
+        # of that shape; time per call, launch included
+        single_b = {}
+        for name, M, K in (("down", 4096, 14336), ("q", 4096, 4096)):
+            ws = [m[4] for m in stack.mats if m[0] == name]
+            for B in (2, 4, 16):
+                xb = torch.from_numpy(synth.activations_f32(0, 40 + B, B, K)).cuda()
+                yb = torch.empty((B, M), dtype=torch.float32, device="cuda")
+                it = {"i": 0}
+
+                def q4call():
+                    gq.gq_gemv_q4k(ws[it["i"] % len(ws)], xb, yb, M, K, B, stream)
+                    it["i"] += 1
+                s = event_time(torch, stream, q4call, reps=2 * len(ws), warmup=len(ws))
+                single_b["%s_%dx%d_b%d" % (name, M, K, B)] = {
+                    "us_per_call": round(s * 1e6, 2),
+                    "GB/s": round(q4k_bytes(M, K) / s / 1e9, 1)}
+        extra["gemv_q4k_single_batched"] = single_b
         del stack
         torch.cuda.empty_cache()
         # prefill matrix products
