@@ -9,7 +9,7 @@ Activation patterns (standard-normal vectors with):
                among its standard-normal neighbours;
   spike_alone  one element at -4e11 whose sub-block is otherwise zero;
   lograng      every element scaled by 10^U(-12, 12);
-  advice       x[c] = 1 and every other element 1.37 * 2^-26;
+  unit_on_tiny x[c] = 1 and every other element 1.37 * 2^-26;
   onehot_big   a one-hot vector scaled by 1e12;
   tiny, subnormal, huge   the whole vector scaled by 1e-36, 1e-40, 1e30.
 
@@ -27,7 +27,7 @@ import oracle
 from quantized_unpack_q4_amd import synth
 from tests import _q4k_edit as qe
 
-PATTERNS = ["spike", "spike_alone", "lograng", "advice", "onehot_big", "tiny", "subnormal",
+PATTERNS = ["spike", "spike_alone", "lograng", "unit_on_tiny", "onehot_big", "tiny", "subnormal",
             "huge"]
 
 
@@ -54,7 +54,7 @@ def activations(pattern, K, seed):
         x[c] = -4e11
     elif pattern == "lograng":
         x *= 10.0 ** g.uniform(-12, 12, K)
-    elif pattern == "advice":
+    elif pattern == "unit_on_tiny":
         x[:] = 1.37 * 2.0 ** -26
         x[c] = 1.0
     elif pattern == "onehot_big":

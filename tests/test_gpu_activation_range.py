@@ -134,7 +134,7 @@ def test_q4k_swiglu_spikes():
     M, K = 264, 4096
     wg, _ = adversarial_q4k(96, 0, M, K)
     wu, _ = adversarial_q4k(96, 1, M, K)
-    for i, pat in enumerate(["spike", "spike_alone", "lograng", "advice"]):
+    for i, pat in enumerate(["spike", "spike_alone", "lograng", "unit_on_tiny"]):
         x = activations(pat, K, 500 + i)
         # keep silu(g) * u finite in binary32: bring the vector to ~1e3 at most
         x = (x * np.float32(1e3 / np.abs(x).max())).astype(np.float32)
@@ -158,7 +158,7 @@ def test_q4k_swiglu_batched_spikes():
     M, K = 264, 4096
     wg, _ = adversarial_q4k(97, 0, M, K)
     wu, _ = adversarial_q4k(97, 1, M, K)
-    pats = ["spike", "spike_alone", "lograng", "advice"]
+    pats = ["spike", "spike_alone", "lograng", "unit_on_tiny"]
     x = np.stack([activations(p, K, 600 + i) for i, p in enumerate(pats)])
     x = (x * (np.float32(1e3) / np.abs(x).max(axis=1, keepdims=True))).astype(np.float32)
     B = x.shape[0]
