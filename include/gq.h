@@ -93,15 +93,16 @@ gq_status gq_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64
  * (d*sc)*sum(q*x) - (dmin*m)*sum(x), with x carried as a binary16 hi + lo
  * pair (products exact, sums binary32): batch 1 on packed dot products with
  * one power-of-two scale per sub-block, batches 3..16 on matrices of more
- * than 32 rows per CU on the matrix cores with one per activation row and
+ * than 32 rows per CU (and, at batch 3..4, of at least 12288 rows) on the
+ * matrix cores with one per activation row and
  * super-block (see gq_gemv_q4k_multi_batched).  Every split value keeps a
  * relative error below 2^-19.  A sub-block whose non-zero |x| span more than
  * 2^20 (batch 1; batches 3..16: holding a non-zero |x| below 2^-20 of its
  * super-block's largest), or that holds more than 1/16 of the sum of |x|
  * over its super-block, is computed exactly instead: each weight as its
  * binary32 value times x in binary32.  The other batch 2..16 products
- * (batch 2, up to 32 rows per CU, or matrices beyond the 32-bit offsets of
- * that kernel) dequantize each weight to binary32, fma(q, d*sc, -dmin*m)
+ * (batch 2, batch 3..4 below 12288 rows, up to 32 rows per CU, or matrices
+ * beyond the 32-bit offsets of that kernel) dequantize each weight to binary32, fma(q, d*sc, -dmin*m)
  * with one rounding, and take products and sums in binary32 on the matrix
  * cores, K split over the waves of a workgroup (results in the subnormal
  * range: up to K/2 multiples of 2^-149).  K above 16384 at batch 1 runs a

@@ -166,12 +166,15 @@ gq_status gq_gemv_q4k(const void *w, const float *x, float *y, int64_t M, int64_
     }
     // batch 2..16: whole-K blocks of 64 rows (the table kernel) once they
     // fill half the chip, else the K-split binary32 form, which is also
-    // faster at batch 2 and takes matrices past the table kernel's 32-bit
-    // offsets (measured, kernel durations: 4096x14336 at batch 4 84 -> 36 us,
-    // 4096x4096 25 -> 13 us, 14336x4096 at batch 2 26.9 -> 24.5 us; 14336x4096
-    // at batch 4 26.4 us on the table kernel against 27.8)
+    // faster at batch 2, at batch 3-4 below 12288 rows (its one-tile
+    // launches), and takes matrices past the table kernel's 32-bit offsets
+    // (measured, kernel durations: 4096x14336 at batch 4 84 -> 29 us,
+    // 4096x4096 25 -> 13 us, 14336x4096 at batch 2 26.9 -> 24.5 us,
+    // 11008x4096 at batch 4 25.8 -> 23.2 us, 9216x4096 25.6 -> 22.5 us;
+    // 14336x4096 at batch 4 26.5 us on the table kernel against 31.7)
     if (B >= 2) {
-        if (B == 2 || M <= 32LL * gq::device_cus() || !gemv_mfma_fits(M, K, B))
+        if (B == 2 || M <= 32LL * gq::device_cus() || (B <= 4 && M < 12288) ||
+            !gemv_mfma_fits(M, K, B))
             return launched(fn,
                             gq::launch_gemv_q4k_f32(w, x, y, M, K, (int)B, (hipStream_t)stream));
         gq::GemvEntry e{(const uint8_t *)w, x, y, (int)M, (int)K, 0, 0};

@@ -147,10 +147,12 @@ def test_q4k_parity_full_single_matrix(M, K):
 
 
 @pytest.mark.parametrize("M,K,B", [(12300, 768, 2), (8200, 1280, 2), (4100, 256, 3),
-                                   (1000, 4352, 12), (300, 8448, 3), (8000, 512, 4)])
+                                   (1000, 4352, 12), (300, 8448, 3), (8000, 512, 4),
+                                   (9000, 512, 4), (12200, 768, 3)])
 def test_q4k_batched_single_ragged(M, K, B):
     """Single products at batch 2..16 on the binary32 matrix-core form (batch
-    2, or at most 32 rows per CU): each launch form (two 16-row tiles of eight
+    2, batch 3-4 below 12288 rows, or at most 32 rows per CU): each launch
+    form (two 16-row tiles of eight
     waves at 12300 rows, one tile of eight waves at 8200 and 4100, one of
     sixteen at 1000 and 300; the 16x16x4 product and both 4x4x1 layouts: by
     4-row groups, and by 4-weight slices at batch 4 and at batch 3 with K of
@@ -171,7 +173,7 @@ def test_q4k_batched_single_ragged(M, K, B):
 
 
 @pytest.mark.parametrize("M,K,B", [(14336, 4096, 2), (4096, 14336, 4), (11008, 4096, 2),
-                                   (4096, 4096, 16), (14336, 4096, 16)])
+                                   (4096, 4096, 16), (14336, 4096, 16), (11008, 4096, 4)])
 def test_q4k_batched_single_full_size_sampled(M, K, B):
     """Decode shapes at batch 2..16 as single products (the binary32 form at
     batch 2 and up to 32 rows per CU, the split-activation kernel for 14336
